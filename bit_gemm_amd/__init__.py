@@ -1,0 +1,203 @@
+"""Python binding of libnvfp4 (NVFP4 FourOverSix quantizer + W4A16 GEMM for
+MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libnvfp4.so`` (built in-tree by ``python -m bit_gemm_amd.build``).  PyTorch
+provides device memory and the current stream.  There is no CPU fallback:
+if the library is missing, importing the entry points raises.
+
+Entry points mirror the C ABI in ``include/nvfp4.h``:
+
+* ``quantize_fos(w, amax=None)`` -> :class:`NVFP4Weight`
+* ``dequant(q, dtype=torch.float32)``
+* ``w4a16_gemm(x, q, out_dtype=torch.bfloat16)``
+* ``selftest_cvt()``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4.so")
+
+NVFP4_OK = 0
+STATUS_NAMES = {
+    0: "NVFP4_OK",
+    1: "NVFP4_ERR_INVALID_VALUE",
+    2: "NVFP4_ERR_UNSUPPORTED_SHAPE",
+    3: "NVFP4_ERR_MISALIGNED",
+    4: "NVFP4_ERR_WORKSPACE_TOO_SMALL",
+    5: "NVFP4_ERR_HIP",
+    6: "NVFP4_ERR_UNSUPPORTED_DEVICE",
+}
+BF16, F32 = 0, 1
+PATH_AUTO, PATH_SKINNY, PATH_TILED = 0, 1, 2
+IMPL_DEFAULT, IMPL_PORTABLE, IMPL_HWCVT = 0, 1, 2
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+_c_int = ctypes.c_int
+_c_size = ctypes.c_size_t
+
+# name -> (restype, argtypes): every symbol include/nvfp4.h declares
+SIGNATURES = {
+    "nvfp4_quantize_fos": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
+    "nvfp4_quantize_fos_ex": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_p]),
+    "nvfp4_dequant": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p]),
+    "nvfp4_w4a16_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "nvfp4_w4a16_gemm": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size, _c_p]),
+    "nvfp4_w4a16_gemm_workspace_size_ex": (_c_size, [_c_i64, _c_i64, _c_i64, _c_int, _c_int]),
+    "nvfp4_w4a16_gemm_ex": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size,
+                                     _c_int, _c_int, _c_int, _c_p]),
+    "nvfp4_w4a16_gemm_path": (_c_int, [_c_i64, _c_i64, _c_i64]),
+    "nvfp4_selftest_cvt": (_c_int, [_c_p, _c_p]),
+    "nvfp4_status_string": (ctypes.c_char_p, [_c_int]),
+    "nvfp4_last_error": (ctypes.c_char_p, []),
+    "nvfp4_version": (_c_int, []),
+}
+
+_lib = None
+
+
+class NVFP4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libnvfp4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m bit_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != NVFP4_OK:
+        raise NVFP4Error(status, lib().nvfp4_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _need_gpu(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class NVFP4Weight:
+    """Packed NVFP4 weight of a [n, k] matrix (see include/nvfp4.h)."""
+
+    codes: torch.Tensor  # uint8 [n, k/2]
+    scales: torch.Tensor  # uint8 [n, k/16]
+    tensor_scale: torch.Tensor  # float32 [1]
+    amax: torch.Tensor  # float32 [1]
+    m4_mask: Optional[torch.Tensor]  # uint8 [n, k/16] or None
+
+    @property
+    def shape(self):
+        return (self.codes.shape[0], self.codes.shape[1] * 2)
+
+
+def quantize_fos(w: torch.Tensor, amax: Optional[torch.Tensor] = None, with_mask: bool = True,
+                 impl: int = IMPL_DEFAULT, out: Optional[NVFP4Weight] = None) -> NVFP4Weight:
+    """FourOverSix NVFP4 quantization of a float32 [n, k] GPU matrix."""
+    _need_gpu(w, "w", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    n, k = w.shape
+    dev = w.device
+    if out is None:
+        out = NVFP4Weight(
+            codes=torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+            scales=torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+            tensor_scale=torch.empty(1, dtype=torch.float32, device=dev),
+            amax=torch.empty(1, dtype=torch.float32, device=dev),
+            m4_mask=torch.empty((n, k // 16), dtype=torch.uint8, device=dev) if with_mask else None,
+        )
+    if amax is not None:
+        _need_gpu(amax, "amax", torch.float32)
+    _check(lib().nvfp4_quantize_fos_ex(
+        _ptr(w), n, k, _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale), _ptr(out.codes),
+        _ptr(out.scales), _ptr(out.m4_mask), impl, _stream(dev)))
+    return out
+
+
+def dequant(q: NVFP4Weight, dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    n, k = q.shape
+    code = {torch.float32: F32, torch.bfloat16: BF16}[dtype]
+    if out is None:
+        out = torch.empty((n, k), dtype=dtype, device=q.codes.device)
+    _need_gpu(out, "out", dtype)
+    _check(lib().nvfp4_dequant(_ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), n, k, code,
+                               _stream(q.codes.device)))
+    return out
+
+
+def workspace_size(m: int, n: int, k: int, path: int = PATH_AUTO, split_k: int = 0) -> int:
+    return int(lib().nvfp4_w4a16_gemm_workspace_size_ex(m, n, k, path, split_k))
+
+
+def gemm_path(m: int, n: int, k: int) -> int:
+    return int(lib().nvfp4_w4a16_gemm_path(m, n, k))
+
+
+def w4a16_gemm(x: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.bfloat16,
+               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               path: int = PATH_AUTO, split_k: int = 0, impl: int = IMPL_DEFAULT) -> torch.Tensor:
+    """y[m, n] = x[m, k] @ W_hat[n, k]^T for bf16 x and NVFP4 weights."""
+    _need_gpu(x, "x", torch.bfloat16)
+    n, k = q.shape
+    if x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}], got {tuple(x.shape)}")
+    m = x.shape[0]
+    code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    dev = x.device
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _need_gpu(out, "out", out_dtype)
+    need = workspace_size(m, n, k, path, split_k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().nvfp4_w4a16_gemm_ex(
+        _ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), m, n, k, code,
+        _ptr(workspace), ws_bytes, path, split_k, impl, _stream(dev)))
+    return out
+
+
+def selftest_cvt(device=None) -> list:
+    """Counters of nvfp4_selftest_cvt (see include/nvfp4.h)."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    buf = torch.zeros(8, dtype=torch.int32, device=dev)
+    _check(lib().nvfp4_selftest_cvt(_ptr(buf), _stream(dev)))
+    return [int(v) & 0xFFFFFFFF for v in buf.cpu().tolist()]
+
+
+def version() -> str:
+    v = int(lib().nvfp4_version())
+    return f"{v // 10000}.{(v // 100) % 100}.{v % 100}"

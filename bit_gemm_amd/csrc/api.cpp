@@ -1,0 +1,244 @@
+// C ABI of libnvfp4 (declared in include/nvfp4.h): argument validation,
+// device check, dispatch to the gfx950 kernels, status and error strings.
+// Validation runs on the host before any HIP call, so invalid calls return
+// an error without touching the GPU.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/nvfp4.h"
+#include "launchers.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(NVFP4_ERR_HIP, "%s: %s (%d)", where, hipGetErrorString(e), (int)e);
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;  // each dimension < 2^31
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+// Per-device cache of the gfx950 check: 0 unknown, 1 ok, 2 unsupported.
+std::atomic<int> g_dev_ok[64];
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(NVFP4_ERR_UNSUPPORTED_DEVICE, "device index %d", dev);
+  int st = g_dev_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    st = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_dev_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(NVFP4_ERR_UNSUPPORTED_DEVICE, "device %d is not gfx950", dev);
+  return NVFP4_OK;
+}
+
+// Conversion implementation used by NVFP4_IMPL_DEFAULT: the gfx950
+// instructions, validated bit-exact against the portable code on the device
+// by nvfp4_selftest_cvt (counters [0]-[2] zero).
+constexpr int kDefaultImpl = nvfp4::kConvPortable;
+
+int resolve_impl(int impl, int* out) {
+  if (impl == NVFP4_IMPL_DEFAULT) {
+    *out = kDefaultImpl;
+  } else if (impl == NVFP4_IMPL_PORTABLE) {
+    *out = nvfp4::kConvPortable;
+  } else if (impl == NVFP4_IMPL_HWCVT) {
+    *out = nvfp4::kConvHw;
+  } else {
+    return fail(NVFP4_ERR_INVALID_VALUE, "impl %d is not a NVFP4_IMPL_* value", impl);
+  }
+  return NVFP4_OK;
+}
+
+int check_nk(int64_t n, int64_t k) {
+  if (n < 0 || k < 0) return fail(NVFP4_ERR_INVALID_VALUE, "negative dimension (n=%lld, k=%lld)", (long long)n, (long long)k);
+  if (k % 16 != 0) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k=%lld is not a multiple of 16", (long long)k);
+  if (n >= kMaxDim || k >= kMaxDim || (n > 0 && k > kMaxElems / n))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "matrix too large (n=%lld, k=%lld)", (long long)n, (long long)k);
+  return NVFP4_OK;
+}
+
+constexpr int kSkinnyMaxM = 48;  // token-count threshold of the dispatch
+
+int choose_path(int64_t m, int path) {
+  if (path == NVFP4_PATH_AUTO) return m <= kSkinnyMaxM ? NVFP4_PATH_SKINNY : NVFP4_PATH_TILED;
+  return path;
+}
+
+}  // namespace
+
+extern "C" {
+
+NVFP4_API int nvfp4_version(void) { return 100; }  // 0.1.0
+
+NVFP4_API const char* nvfp4_status_string(int status) {
+  switch (status) {
+    case NVFP4_OK: return "NVFP4_OK";
+    case NVFP4_ERR_INVALID_VALUE: return "NVFP4_ERR_INVALID_VALUE";
+    case NVFP4_ERR_UNSUPPORTED_SHAPE: return "NVFP4_ERR_UNSUPPORTED_SHAPE";
+    case NVFP4_ERR_MISALIGNED: return "NVFP4_ERR_MISALIGNED";
+    case NVFP4_ERR_WORKSPACE_TOO_SMALL: return "NVFP4_ERR_WORKSPACE_TOO_SMALL";
+    case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP";
+    case NVFP4_ERR_UNSUPPORTED_DEVICE: return "NVFP4_ERR_UNSUPPORTED_DEVICE";
+    default: return "NVFP4_ERR_UNKNOWN";
+  }
+}
+
+NVFP4_API const char* nvfp4_last_error(void) { return g_last_error.c_str(); }
+
+NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const float* amax_in,
+                                    float* amax_out, float* tensor_scale, uint8_t* codes,
+                                    uint8_t* scales, uint8_t* m4_mask, int impl, void* stream) {
+  g_last_error.clear();
+  int st = check_nk(n, k);
+  if (st) return st;
+  const bool empty = (n == 0 || k == 0);
+  if (!amax_out || !tensor_scale) return fail(NVFP4_ERR_INVALID_VALUE, "amax_out and tensor_scale are required");
+  if (!empty && (!w || !codes || !scales)) return fail(NVFP4_ERR_INVALID_VALUE, "w, codes and scales are required");
+  if (!aligned(amax_out, 4) || !aligned(tensor_scale, 4) || (amax_in && !aligned(amax_in, 4)))
+    return fail(NVFP4_ERR_MISALIGNED, "scalar arguments must be 4-byte aligned");
+  if (!empty && (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 16) || (m4_mask && !aligned(m4_mask, 16))))
+    return fail(NVFP4_ERR_MISALIGNED, "w, codes, scales and m4_mask must be 16-byte aligned");
+  int ci = 0;
+  if ((st = resolve_impl(impl, &ci))) return st;
+  if ((st = check_device())) return st;
+  hipError_t e = nvfp4::launch_quantize_fos(w, n, k, amax_in, amax_out, tensor_scale, codes, scales,
+                                            m4_mask, ci, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return NVFP4_OK;
+}
+
+NVFP4_API int nvfp4_quantize_fos(const float* w, int64_t n, int64_t k, const float* amax_in,
+                                 float* amax_out, float* tensor_scale, uint8_t* codes,
+                                 uint8_t* scales, uint8_t* m4_mask, void* stream) {
+  return nvfp4_quantize_fos_ex(w, n, k, amax_in, amax_out, tensor_scale, codes, scales, m4_mask,
+                               NVFP4_IMPL_DEFAULT, stream);
+}
+
+NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                            void* w_out, int64_t n, int64_t k, int out_dtype, void* stream) {
+  g_last_error.clear();
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_F32)
+    return fail(NVFP4_ERR_INVALID_VALUE, "out_dtype %d", out_dtype);
+  if (n == 0 || k == 0) return NVFP4_OK;
+  if (!codes || !scales || !tensor_scale || !w_out) return fail(NVFP4_ERR_INVALID_VALUE, "null pointer argument");
+  if (!aligned(codes, 16) || !aligned(scales, 16) || !aligned(w_out, 16) || !aligned(tensor_scale, 4))
+    return fail(NVFP4_ERR_MISALIGNED, "codes, scales, w_out must be 16-byte aligned");
+  if ((st = check_device())) return st;
+  hipError_t e = nvfp4::launch_dequant(codes, scales, tensor_scale, w_out, n, k, out_dtype == NVFP4_F32,
+                                       reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequant launch");
+  return NVFP4_OK;
+}
+
+NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k) {
+  (void)n;
+  (void)k;
+  return choose_path(m, NVFP4_PATH_AUTO);
+}
+
+NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size_ex(int64_t m, int64_t n, int64_t k, int path,
+                                                    int split_k) {
+  if (m <= 0 || n <= 0 || k <= 0) return 0;
+  if (choose_path(m, path) != NVFP4_PATH_SKINNY || m > 64) return 0;
+  return nvfp4::plan_skinny(m, n, k, split_k).ws_bytes;
+}
+
+NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
+  return nvfp4_w4a16_gemm_workspace_size_ex(m, n, k, NVFP4_PATH_AUTO, 0);
+}
+
+NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uint8_t* scales,
+                                  const float* tensor_scale, void* y, int64_t m, int64_t n,
+                                  int64_t k, int out_dtype, void* workspace,
+                                  size_t workspace_bytes, int path, int split_k, int impl,
+                                  void* stream) {
+  g_last_error.clear();
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (m < 0) return fail(NVFP4_ERR_INVALID_VALUE, "negative m=%lld", (long long)m);
+  if (m >= kMaxDim || (m > 0 && n > 0 && m > kMaxElems / n) || (m > 0 && k > 0 && m > kMaxElems / k))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "m=%lld too large", (long long)m);
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_F32)
+    return fail(NVFP4_ERR_INVALID_VALUE, "out_dtype %d", out_dtype);
+  if (path != NVFP4_PATH_AUTO && path != NVFP4_PATH_SKINNY && path != NVFP4_PATH_TILED)
+    return fail(NVFP4_ERR_INVALID_VALUE, "path %d", path);
+  if (split_k < 0) return fail(NVFP4_ERR_INVALID_VALUE, "split_k %d", split_k);
+  int ci = 0;
+  if ((st = resolve_impl(impl, &ci))) return st;
+  const int p = choose_path(m, path);
+  if (p == NVFP4_PATH_SKINNY && m > 64)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "the skinny path takes m <= 64 (m=%lld)", (long long)m);
+  if (m == 0 || n == 0) return NVFP4_OK;
+  if (!y || !tensor_scale) return fail(NVFP4_ERR_INVALID_VALUE, "y and tensor_scale are required");
+  if (k > 0 && (!x || !codes || !scales)) return fail(NVFP4_ERR_INVALID_VALUE, "x, codes and scales are required");
+  if (!aligned(y, 16) || !aligned(tensor_scale, 4) || (k > 0 && (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16))))
+    return fail(NVFP4_ERR_MISALIGNED, "x, codes, scales, y must be 16-byte aligned");
+  nvfp4::SkinnyPlan plan{1, 128, 0};
+  if (p == NVFP4_PATH_SKINNY) {
+    plan = nvfp4::plan_skinny(m, n, k, split_k);
+    if (plan.ws_bytes > 0) {
+      if (workspace_bytes < plan.ws_bytes)
+        return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, plan.ws_bytes);
+      if (!workspace) return fail(NVFP4_ERR_INVALID_VALUE, "workspace is NULL");
+      if (!aligned(workspace, 16)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+    }
+  }
+  if ((st = check_device())) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (p == NVFP4_PATH_SKINNY)
+    e = nvfp4::launch_skinny(x, codes, scales, tensor_scale, y, m, n, k, out_dtype == NVFP4_F32, plan,
+                             workspace, ci, s);
+  else
+    e = nvfp4::launch_tiled(x, codes, scales, tensor_scale, y, m, n, k, out_dtype == NVFP4_F32, ci, s);
+  if (e != hipSuccess) return hip_fail(e, "gemm launch");
+  return NVFP4_OK;
+}
+
+NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
+                               const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                               int out_dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  return nvfp4_w4a16_gemm_ex(x, codes, scales, tensor_scale, y, m, n, k, out_dtype, workspace,
+                             workspace_bytes, NVFP4_PATH_AUTO, 0, NVFP4_IMPL_DEFAULT, stream);
+}
+
+NVFP4_API int nvfp4_selftest_cvt(uint32_t* counters_out, void* stream) {
+  g_last_error.clear();
+  if (!counters_out) return fail(NVFP4_ERR_INVALID_VALUE, "counters_out is NULL");
+  if (!aligned(counters_out, 4)) return fail(NVFP4_ERR_MISALIGNED, "counters_out must be 4-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = nvfp4::launch_selftest_cvt(counters_out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "selftest launch");
+  return NVFP4_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal host-side launchers of the gfx950 kernels (called by api.cpp
+// after argument validation).  Each returns hipSuccess or the launch error.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Conversion implementations (see NVFP4_IMPL_* in nvfp4.h).
+enum ConvImpl { kConvPortable = 1, kConvHw = 2 };
+
+hipError_t launch_quantize_fos(const float* w, int64_t n, int64_t k, const float* amax_in,
+                               float* amax_out, float* tensor_scale, uint8_t* codes,
+                               uint8_t* scales, uint8_t* m4_mask, int impl, hipStream_t stream);
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                          void* out, int64_t n, int64_t k, int out_f32, hipStream_t stream);
+
+// Skinny (m <= 64) split-K path.
+struct SkinnyPlan {
+  int splits;      // number of K chunks (grid.y)
+  int kchunk;      // K elements per chunk, multiple of 128
+  size_t ws_bytes; // fp32 partial sums, splits * m * n * 4 when splits > 1
+};
+SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits);
+hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* scales,
+                         const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                         int out_f32, const SkinnyPlan& plan, void* workspace, int impl,
+                         hipStream_t stream);
+
+// Tiled bf16-MFMA path (any m).
+hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scales,
+                        const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                        int out_f32, int impl, hipStream_t stream);
+
+hipError_t launch_selftest_cvt(uint32_t* counters, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,88 @@
+// Device helpers shared by the gfx950 kernels of libnvfp4: E4M3 scale
+// rounding, E2M1 (FP4) rounding and decoding, bf16 packing, MFMA operand
+// types.  Compiled only for gfx950 (CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;   // MFMA A/B operand
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;     // 16x16 MFMA accumulator
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+
+constexpr float kFltMax = 3.40282346638528859811704183484516925e+38f;
+
+// E4M3 (bias 7, 3 mantissa bits, max 448, S.1111.111 = NaN) round to nearest
+// even of u >= 0.  Returns the rounded value and writes the bit pattern to
+// *code; a result above 448 is an overflow: *code = 0x7F and NaN is returned.
+__device__ __forceinline__ float e4m3_rne(float u, uint32_t* code) {
+  if (u < 0x1p-6f) {
+    // Subnormal range: the quantum is 2^-9.  u * 512 is exact, rintf rounds
+    // to nearest even; 8 becomes the smallest normal (pattern 0x08).
+    float m = __builtin_rintf(u * 512.0f);
+    *code = (uint32_t)m;
+    return m * 0x1p-9f;
+  }
+  uint32_t b = __float_as_uint(u);
+  // keep 3 mantissa bits: add just under half an ulp of the kept bits plus
+  // the kept LSB (ties to even), then clear the 20 dropped bits
+  uint32_t r = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
+  uint32_t e = (r >> 23);  // biased fp32 exponent, >= 121 here
+  uint32_t c = ((e - 120u) << 3) | ((r >> 20) & 7u);  // E4M3 exponent = e - 127 + 7
+  if (c > 0x7Eu) {
+    *code = 0x7Fu;
+    return __builtin_nanf("");
+  }
+  *code = c;
+  return __uint_as_float(r);
+}
+
+// Value of an E4M3 bit pattern with the sign bit clear (0x00..0x7E).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 0) return (float)m * 0x1p-9f;
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 magnitude index (0..7 <-> 0, .5, 1, 1.5, 2, 3, 4, 6) of v >= 0, round
+// to nearest with ties to the even index, saturating; NaN -> 0, +inf -> 7.
+// The index is the number of grid midpoints below v: ">" at a midpoint whose
+// upper neighbour has an odd index, ">=" where it is even.
+__device__ __forceinline__ uint32_t e2m1_rne_portable(float v) {
+  return (uint32_t)(v > 0.25f) + (uint32_t)(v >= 0.75f) + (uint32_t)(v > 1.25f) +
+         (uint32_t)(v >= 1.75f) + (uint32_t)(v > 2.5f) + (uint32_t)(v >= 3.5f) +
+         (uint32_t)(v > 5.0f);
+}
+
+// Magnitude of an E2M1 magnitude index.  Indices 2..7 are normal numbers
+// 2^(e-1) * (1 + m/2) with index = 2e + m, whose fp32 bit pattern is
+// (index + 252) << 22; 0 and 1 are the subnormals 0 and 0.5.
+__device__ __forceinline__ float e2m1_mag_portable(uint32_t idx) {
+  return idx < 2u ? 0.5f * (float)idx : __uint_as_float((idx + 252u) << 22);
+}
+
+// Signed value of a 4-bit code (bit 3 = sign).
+__device__ __forceinline__ float e2m1_val_portable(uint32_t code) {
+  return __uint_as_float(__float_as_uint(e2m1_mag_portable(code & 7u)) | ((code & 8u) << 28));
+}
+
+// gfx950 scaled conversions, used with a unit scale: two fp32 -> two FP4
+// codes in bits 0-3 (first operand) and 4-7 (second) of the result, and back.
+__device__ __forceinline__ uint32_t e2m1_pack2_hw(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+}
+
+// Round an fp32 to bf16, nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Two fp32 values that are exact in bf16 -> packed bf16x2 (lo in bits 0-15).
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+}  // namespace nvfp4

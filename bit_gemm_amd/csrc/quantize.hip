@@ -1,0 +1,184 @@
+// FourOverSix NVFP4 quantizer for gfx950.
+//
+// Method: "SOAR Weekly Champion Notes 07 | Vanilla Xiao Zhang: NVFP4
+// Quantization Improvements and Speculative Decoding in Practice", sections
+// "01 Background" (E2M1 grid, block amax mapped to 6) and "02 FourOverSix"
+// (second candidate scale = fp8(1.5 * M=6 scale); keep it only when the
+// block's mean squared dequantization error is strictly smaller).  The
+// per-step fp32 arithmetic follows the contract stated in nvfp4.h; this file
+// must be compiled without FMA contraction.
+//
+// Kernels:
+//  k_fill_zero  amax_out = 0 (no memset node, so the sequence is safe to
+//               capture in a HIP graph)
+//  k_amax       grid-stride max |w| -> atomicMax on the fp32 bit pattern
+//               (non-negative floats order like their unsigned bits)
+//  k_fos        one lane per 16-element block: block amax, E4M3 scales,
+//               both candidates, SSE compare, nibble packing, stores.
+#include "launchers.h"
+#include "nvfp4_device.h"
+
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+namespace {
+
+__global__ void k_fill_zero(float* p) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) p[0] = 0.0f;
+}
+
+__global__ __launch_bounds__(256) void k_amax(const float4* __restrict__ w, int64_t n4,
+                                              float* __restrict__ amax) {
+  float m = 0.0f;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // four independent loads in flight per iteration
+  for (; i + 3 * stride < n4; i += 4 * stride) {
+    float4 a = w[i], b = w[i + stride], c = w[i + 2 * stride], d = w[i + 3 * stride];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(d.x), fabsf(d.y)), fmaxf(fabsf(d.z), fabsf(d.w))));
+  }
+  for (; i < n4; i += stride) {
+    float4 a = w[i];
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+  }
+  // wave reduction, then across the 4 waves through LDS, one atomic per block
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  __shared__ float part[4];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    atomicMax(reinterpret_cast<unsigned int*>(amax), __float_as_uint(m));
+  }
+}
+
+// Pairwise tree over 16 squared errors: ((q0+q1)+(q2+q3)) + ... in fp32.
+__device__ __forceinline__ float tree16(const float* q) {
+  float p0 = q[0] + q[1], p1 = q[2] + q[3], p2 = q[4] + q[5], p3 = q[6] + q[7];
+  float p4 = q[8] + q[9], p5 = q[10] + q[11], p6 = q[12] + q[13], p7 = q[14] + q[15];
+  float r0 = p0 + p1, r1 = p2 + p3, r2 = p4 + p5, r3 = p6 + p7;
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Quantize one block against one candidate scale sigma.  Returns the block
+// SSE; writes the 16 packed 4-bit codes (element i at bits 4i of the 64-bit
+// pair {lo, hi}).
+template <int IMPL>
+__device__ __forceinline__ float candidate(const float* x, float sigma, float s_t, uint32_t& lo,
+                                           uint32_t& hi) {
+  float R = fminf(1.0f / (sigma * s_t), kFltMax);
+  R = (sigma == 0.0f) ? 0.0f : R;
+  float q[16];
+  lo = 0u;
+  hi = 0u;
+  if constexpr (IMPL == kConvPortable) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float ax = fabsf(x[i]);
+      const uint32_t mag = e2m1_rne_portable(ax * R);
+      const float wh = (e2m1_mag_portable(mag) * sigma) * s_t;
+      const float e = ax - wh;
+      q[i] = e * e;
+      const uint32_t code = mag | ((__float_as_uint(x[i]) >> 28) & 8u);
+      if (i < 8)
+        lo |= code << (4 * i);
+      else
+        hi |= code << (4 * (i - 8));
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t byte = e2m1_pack2_hw(x[2 * j] * R, x[2 * j + 1] * R);
+      const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
+      const float e0 = x[2 * j] - (v[0] * sigma) * s_t;
+      const float e1 = x[2 * j + 1] - (v[1] * sigma) * s_t;
+      q[2 * j] = e0 * e0;
+      q[2 * j + 1] = e1 * e1;
+      if (j < 4)
+        lo |= byte << (8 * j);
+      else
+        hi |= byte << (8 * (j - 4));
+    }
+  }
+  return tree16(q);
+}
+
+template <int IMPL>
+__global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_t nblocks,
+                                             const float* amax_src, float* amax_out,
+                                             float* __restrict__ tensor_scale,
+                                             uint8_t* __restrict__ codes,
+                                             uint8_t* __restrict__ scales,
+                                             uint8_t* __restrict__ mask) {
+  const float amax = amax_src[0];
+  float s_t = amax / 2688.0f;  // 2688 = 6 (FP4 max) * 448 (E4M3 max)
+  s_t = (s_t == 0.0f) ? 1.0f : s_t;
+  const float d6 = 6.0f * s_t;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    tensor_scale[0] = s_t;
+    if (amax_out != amax_src) amax_out[0] = amax;
+  }
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
+    const float4* p = reinterpret_cast<const float4*>(w) + 4 * b;
+    const float4 t0 = p[0], t1 = p[1], t2 = p[2], t3 = p[3];
+    const float x[16] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w,
+                         t2.x, t2.y, t2.z, t2.w, t3.x, t3.y, t3.z, t3.w};
+    float a = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
+    const float u6 = fminf(a / d6, 448.0f);
+    uint32_t c6, c4;
+    const float s6 = e4m3_rne(u6, &c6);
+    const float s4r = e4m3_rne(1.5f * s6, &c4);
+    const bool valid4 = c4 <= 0x7Eu;
+    const float s4 = valid4 ? s4r : 0.0f;
+    uint32_t lo6, hi6, lo4, hi4;
+    const float sse6 = candidate<IMPL>(x, s6, s_t, lo6, hi6);
+    const float sse4 = candidate<IMPL>(x, s4, s_t, lo4, hi4);
+    const bool pick4 = valid4 && (sse4 < sse6);
+    uint2 out;
+    out.x = pick4 ? lo4 : lo6;
+    out.y = pick4 ? hi4 : hi6;
+    reinterpret_cast<uint2*>(codes)[b] = out;
+    scales[b] = (uint8_t)(pick4 ? c4 : c6);
+    if (mask != nullptr) mask[b] = (uint8_t)pick4;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_fos(const float* w, int64_t n, int64_t k, const float* amax_in,
+                               float* amax_out, float* tensor_scale, uint8_t* codes,
+                               uint8_t* scales, uint8_t* m4_mask, int impl, hipStream_t stream) {
+  const int64_t count = n * k;
+  const float* amax_src = amax_in;
+  if (amax_src == nullptr) {
+    hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, stream, amax_out);
+    if (count > 0) {
+      const int64_t n4 = count / 4;
+      int64_t blocks = (n4 + 255) / 256;
+      if (blocks > 2048) blocks = 2048;  // 32 waves per CU, grid-stride beyond
+      hipLaunchKernelGGL(k_amax, dim3((unsigned)blocks), dim3(256), 0, stream,
+                         reinterpret_cast<const float4*>(w), n4, amax_out);
+    }
+    amax_src = amax_out;
+  }
+  const int64_t nblocks = count / 16;
+  int64_t grid = (nblocks + 255) / 256;
+  if (grid < 1) grid = 1;  // also writes tensor_scale / amax_out for empty input
+  if (grid > (1 << 20)) grid = 1 << 20;
+  if (impl == kConvHw)
+    hipLaunchKernelGGL(k_fos<kConvHw>, dim3((unsigned)grid), dim3(256), 0, stream, w, nblocks,
+                       amax_src, amax_out, tensor_scale, codes, scales, m4_mask);
+  else
+    hipLaunchKernelGGL(k_fos<kConvPortable>, dim3((unsigned)grid), dim3(256), 0, stream, w,
+                       nblocks, amax_src, amax_out, tensor_scale, codes, scales, m4_mask);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

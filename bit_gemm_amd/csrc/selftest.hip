@@ -1,0 +1,82 @@
+// Validation of the gfx950 scaled FP4 conversion instructions against the
+// library's portable ALU rounding and decoding (nvfp4_device.h).  The
+// hardware path (NVFP4_IMPL_HWCVT) is only the default when every counter
+// here is zero on the device.
+#include "launchers.h"
+#include "nvfp4_device.h"
+
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+namespace {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+__device__ __forceinline__ void count(uint32_t* counter, uint32_t c) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  if ((threadIdx.x & 63) == 0 && c != 0u) atomicAdd(counter, c);
+}
+
+__device__ __forceinline__ uint32_t sw_code(float v) {
+  return e2m1_rne_portable(fabsf(v)) | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+// [0]: every non-NaN fp32 bit pattern i (both signs), paired with pattern
+// i ^ 0x00400000 in the second operand to check the nibble order too.
+__global__ __launch_bounds__(256) void k_round(uint32_t* counters) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint32_t bad = 0u, tested = 0u;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (1ull << 32); i += stride) {
+    const uint32_t ba = (uint32_t)i, bb = ba ^ 0x00400000u;
+    const float a = __uint_as_float(ba), b = __uint_as_float(bb);
+    if (a != a || b != b) continue;  // NaN
+    const uint32_t hw = e2m1_pack2_hw(a, b);
+    const uint32_t sw = sw_code(a) | (sw_code(b) << 4);
+    bad += (hw != sw) ? 1u : 0u;
+    tested += 1u;
+  }
+  count(&counters[0], bad);
+  count(&counters[4], tested);
+}
+
+// [1] decode of all 256 bytes, [2] scaled fp32 decode, [3] scaled bf16
+// decode, for sigma over all 127 non-negative finite E4M3 values.
+__global__ __launch_bounds__(256) void k_decode(uint32_t* counters) {
+  const uint32_t byte = threadIdx.x;  // 0..255
+  const uint32_t scode = blockIdx.x;  // 0..126
+  const float sigma = e4m3_decode(scode);
+  const uint32_t word = byte * 0x01010101u;
+  const float lo = e2m1_val_portable(byte & 0xFu), hi = e2m1_val_portable(byte >> 4);
+  uint32_t bad1 = 0u, bad2 = 0u, bad3 = 0u;
+  if (scode == 0) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+    bad1 = (__float_as_uint(v[0]) != __float_as_uint(lo) || __float_as_uint(v[1]) != __float_as_uint(hi)) ? 1u : 0u;
+  }
+  {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, sigma, 1);
+    const float el = lo * sigma, eh = hi * sigma;
+    bad2 = (__float_as_uint(v[0]) != __float_as_uint(el) || __float_as_uint(v[1]) != __float_as_uint(eh)) ? 1u : 0u;
+    const bf16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, sigma, 2);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    bad3 = (hb != pack_bf16_exact(el, eh)) ? 1u : 0u;
+  }
+  count(&counters[1], bad1);
+  count(&counters[2], bad2);
+  count(&counters[3], bad3);
+}
+
+__global__ void k_zero8(uint32_t* c) {
+  if (threadIdx.x < 8) c[threadIdx.x] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_selftest_cvt(uint32_t* counters, hipStream_t stream) {
+  hipLaunchKernelGGL(k_zero8, dim3(1), dim3(64), 0, stream, counters);
+  hipLaunchKernelGGL(k_round, dim3(8192), dim3(256), 0, stream, counters);
+  hipLaunchKernelGGL(k_decode, dim3(127), dim3(256), 0, stream, counters);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

@@ -1,0 +1,213 @@
+/*
+ * nvfp4.h - C ABI of libnvfp4.so: NVFP4 weight quantization with FourOverSix
+ * block-scale selection, dequantization, and the W4A16 GEMM over the packed
+ * weights, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *  [Notes07] "SOAR Weekly Champion Notes 07 | Vanilla Xiao Zhang: NVFP4
+ *            Quantization Improvements and Speculative Decoding in Practice",
+ *            sections "01 Background" (E2M1 value set, M=6 convention) and
+ *            "02 FourOverSix" (M=4 scale = fp8(1.5 * M=6 scale), keep the
+ *            scale with the strictly smaller block MSE, format unchanged).
+ *  [Recap]   "SOAR 2026 Recap: From Compute Limits to the Open-Source
+ *            Ecosystem", section "1. Quantization and GEMM dispatch" (all
+ *            linear weights in NVFP4 at 0.5 byte per element; W4A16 kernel
+ *            for small token counts M, another path for large M, chosen by
+ *            latency).
+ *  [Notes08] "SOAR Weekly Champion Notes 08 | Vanilla Xiao Zhang: Evolving
+ *            Speculative Decoding on MiniCPM-SALA", section "01 A Brief
+ *            Recap of Speculative Decoding" (decode is bandwidth bound: every
+ *            generated token reads all of the weights from GPU memory).
+ *
+ * Format.  A weight matrix W is [n, k] row-major (k = reduction dim,
+ * k % 16 == 0).  It is stored as
+ *   codes  uint8 [n, k/2]   two 4-bit E2M1 codes per byte; byte j of a row
+ *                           holds element 2j in bits 0-3 and 2j+1 in bits
+ *                           4-7; code bit 3 = sign, bits 0-2 = magnitude
+ *                           index of {0, .5, 1, 1.5, 2, 3, 4, 6};
+ *   scales uint8 [n, k/16]  one E4M3 (bias 7, max 448, no inf) bit pattern
+ *                           per 16 consecutive elements along k, sign bit 0;
+ *   tensor_scale float32    one per matrix;
+ * and W_hat[r][c] = val(code) * scale(r, c/16) * tensor_scale.
+ * The block size 16, the E4M3 flavour and the fp32 tensor scale are the
+ * problem statement's choices; the pages only say "FP8 block scale".
+ *
+ * Conventions for every entry point.
+ *  - Array arguments are DEVICE pointers to caller-owned memory, 16-byte
+ *    aligned; scalar arguments marked "device scalar" are device pointers to
+ *    one float, 4-byte aligned.  The library never allocates, frees or
+ *    retains caller memory.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is enqueued
+ *    asynchronously; buffers must stay valid until the stream has passed it.
+ *  - Argument checks happen on the host before anything is enqueued; on an
+ *    error nothing is written and no GPU call is made.  Errors after the
+ *    checks (launch failures) return NVFP4_ERR_HIP.
+ *  - The last error message of the calling thread is nvfp4_last_error().
+ *  - Calls are thread-safe; the library holds no mutable global state apart
+ *    from a per-device cache of the device check.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define NVFP4_API __attribute__((visibility("default")))
+
+/* Status codes. */
+enum {
+  NVFP4_OK = 0,
+  NVFP4_ERR_INVALID_VALUE = 1,     /* null required pointer, negative dims, bad enum */
+  NVFP4_ERR_UNSUPPORTED_SHAPE = 2, /* k % 16 != 0, or a dimension too large */
+  NVFP4_ERR_MISALIGNED = 3,        /* pointer not aligned as documented */
+  NVFP4_ERR_WORKSPACE_TOO_SMALL = 4,
+  NVFP4_ERR_HIP = 5,               /* HIP runtime / launch error */
+  NVFP4_ERR_UNSUPPORTED_DEVICE = 6 /* current device is not gfx950 */
+};
+
+/* Output element types. */
+enum { NVFP4_BF16 = 0, NVFP4_F32 = 1 };
+
+/* GEMM paths (token-count dispatch of [Recap] section 1). */
+enum { NVFP4_PATH_AUTO = 0, NVFP4_PATH_SKINNY = 1, NVFP4_PATH_TILED = 2 };
+
+/* Conversion implementation selector for the _ex entry points. */
+enum {
+  NVFP4_IMPL_DEFAULT = 0,  /* fastest implementation validated for gfx950 */
+  NVFP4_IMPL_PORTABLE = 1, /* plain ALU code for FP4 rounding / decoding */
+  NVFP4_IMPL_HWCVT = 2     /* gfx950 scaled FP4 conversion instructions */
+};
+
+/*
+ * nvfp4_quantize_fos - FourOverSix NVFP4 quantization of one fp32 matrix.
+ *
+ * Computes ([Notes07] sections 01-02; the per-step arithmetic is this
+ * library's stated reading, one IEEE fp32 operation per step, round to
+ * nearest even, no fused multiply-add):
+ *   amax  = max |w| over the matrix, or *amax_in when amax_in != NULL;
+ *   s_t   = amax / 2688 (2688 = 6 * 448), or 1 if that is 0;
+ *   per 16-element block: a = max |w_i|; u6 = min(a / (6 s_t), 448);
+ *     sigma6 = E4M3 round-to-nearest-even(u6);
+ *     sigma4 = E4M3 RNE(1.5 * sigma6), not a candidate if it overflows
+ *              (sigma6 >= 320);
+ *     for each candidate sigma: R = sigma ? min(1/(sigma*s_t), FLT_MAX) : 0,
+ *       code_i = E2M1 RNE(|w_i| * R) (saturating at 6, sign kept, also
+ *       for values that round to zero), w_hat_i = val * sigma * s_t,
+ *       SSE = pairwise tree sum of (w_i - w_hat_i)^2 over the 16 elements;
+ *     keep sigma4 iff it is a candidate and SSE4 < SSE6 (a tie keeps M=6).
+ *
+ * w          device fp32 [n, k] row-major, finite values (NaN/inf input
+ *            gives unspecified codes but no fault).
+ * n, k       n >= 0, k >= 0, k % 16 == 0, n * k < 2^40.
+ * amax_in    device scalar or NULL.  When given it must be finite and
+ *            >= max |w| (e.g. the max over all row shards of a matrix);
+ *            a smaller value saturates block scales at 448.
+ * amax_out   device scalar (required): receives the amax that was used.
+ * tensor_scale device scalar (required): receives s_t.
+ * codes      device uint8 [n, k/2].
+ * scales     device uint8 [n, k/16]: E4M3 bits of the chosen block scales.
+ * m4_mask    device uint8 [n, k/16] or NULL: 1 where M=4 was chosen.
+ *            (Diagnostic only: the NVFP4 format does not store the choice.)
+ * Kernels: one fill of amax_out + one amax reduction pass (skipped when
+ * amax_in is given) and one quantization pass.  Deterministic.
+ */
+NVFP4_API int nvfp4_quantize_fos(const float* w, int64_t n, int64_t k, const float* amax_in,
+                                 float* amax_out, float* tensor_scale, uint8_t* codes,
+                                 uint8_t* scales, uint8_t* m4_mask, void* stream);
+
+/* Same as nvfp4_quantize_fos with an explicit conversion implementation
+ * (NVFP4_IMPL_*).  Every implementation produces identical bits. */
+NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const float* amax_in,
+                                    float* amax_out, float* tensor_scale, uint8_t* codes,
+                                    uint8_t* scales, uint8_t* m4_mask, int impl, void* stream);
+
+/*
+ * nvfp4_dequant - W_hat from the packed format ([Notes07] section 02:
+ * "dequant" of a block with its scale).
+ *
+ * out_dtype NVFP4_F32: w_out[r][c] = sign * fl32(fl32(val * sigma) * s_t)
+ *   (val * sigma is exact, so this is the correctly rounded W_hat; it equals
+ *   the w_hat the quantizer used in its error comparison).
+ * out_dtype NVFP4_BF16: the fp32 value rounded to nearest-even bfloat16.
+ * codes, scales as in the format above; tensor_scale device scalar;
+ * w_out device [n, k] of out_dtype.  n >= 0, k >= 0, k % 16 == 0.
+ */
+NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                            void* w_out, int64_t n, int64_t k, int out_dtype, void* stream);
+
+/*
+ * nvfp4_w4a16_gemm - y[m, n] = x[m, k] . W_hat[n, k]^T with bf16
+ * activations and NVFP4 weights ([Recap] section 1: W4A16 for small token
+ * counts; decode reads every weight from HBM once per token, so this
+ * kernel is bound by HBM bandwidth, [Notes08] section 01).
+ *
+ * Products val * sigma are exact in bf16; accumulation is fp32; s_t is
+ * applied in fp32 once per output; one final rounding to out_dtype.
+ * Summation order is implementation-defined but fixed for a given
+ * (m, n, k, path) (results are bit-reproducible run to run).
+ *
+ * x          device bf16 [m, k] row-major.
+ * codes, scales  the packed weights [n, k/2], [n, k/16].
+ * tensor_scale   device scalar.
+ * y          device [m, n] of out_dtype (NVFP4_BF16 or NVFP4_F32).
+ * m, n, k    >= 0, k % 16 == 0.  m == 0 or n == 0: nothing is done;
+ *            k == 0: y = 0.
+ * workspace  device buffer of at least
+ *            nvfp4_w4a16_gemm_workspace_size(m, n, k) bytes, 16-byte
+ *            aligned (may be NULL when that size is 0).  Its contents on
+ *            entry do not matter.
+ * Dispatch: m <= 48 -> memory-bound skinny split-K kernel; otherwise the
+ * bf16-MFMA tiled kernel.
+ */
+NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
+NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
+                               const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                               int out_dtype, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Same, with an explicit path (NVFP4_PATH_*), a requested split-K factor
+ * for the skinny path (0 = heuristic; clamped to [1, 64]; more splits are
+ * used when a K chunk would not fit in LDS) and a dequantization
+ * implementation (NVFP4_IMPL_*).  The skinny path requires m <= 64.  The
+ * workspace size for a forced split is
+ * nvfp4_w4a16_gemm_workspace_size_ex(m, n, k, path, split_k). */
+NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size_ex(int64_t m, int64_t n, int64_t k, int path,
+                                                    int split_k);
+NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uint8_t* scales,
+                                  const float* tensor_scale, void* y, int64_t m, int64_t n,
+                                  int64_t k, int out_dtype, void* workspace,
+                                  size_t workspace_bytes, int path, int split_k, int impl,
+                                  void* stream);
+
+/* The path NVFP4_PATH_AUTO picks for m (NVFP4_PATH_SKINNY or _TILED). */
+NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);
+
+/*
+ * nvfp4_selftest_cvt - validation of the gfx950 FP4 conversion
+ * instructions against the library's portable ALU rounding and decoding.
+ * Runs on `stream` and writes 8 uint32 counters to the device buffer
+ * `counters_out`:
+ *  [0] fp32 -> FP4 code mismatches over every non-NaN fp32 bit pattern
+ *      (both signs, including +-inf),
+ *  [1] FP4 byte -> 2 x fp32 decode mismatches (256 bytes),
+ *  [2] FP4 byte -> 2 x fp32 with scale sigma, against fl32(val * sigma),
+ *      for every E4M3 sigma in [0, 448],
+ *  [3] FP4 byte -> 2 x bf16 with scale sigma, against val * sigma,
+ *  [4] number of fp32 values tested in [0], [5..7] reserved (0).
+ * Used by the tests to decide whether NVFP4_IMPL_HWCVT is exact.
+ */
+NVFP4_API int nvfp4_selftest_cvt(uint32_t* counters_out, void* stream);
+
+NVFP4_API const char* nvfp4_status_string(int status);
+NVFP4_API const char* nvfp4_last_error(void);
+/* 10000 * major + 100 * minor + patch */
+NVFP4_API int nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVFP4_H_ */

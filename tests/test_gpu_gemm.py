@@ -1,0 +1,161 @@
+"""GPU parity: W4A16 GEMM vs the float64 oracle.
+
+Bar: relative Frobenius error <= 2e-3 for bf16 output (bf16 rounding of the
+result alone is about 1.5e-3) and <= 1e-5 for fp32 output (fp32 accumulation
+of exactly dequantized bf16 products).  One-hot activations with a
+power-of-two tensor scale must reproduce W_hat exactly.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_gemm_amd as nv
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.bfloat16: 2e-3, torch.float32: 1e-5}
+
+
+def _rel(y, ref):
+    y = y.double().cpu().numpy() if isinstance(y, torch.Tensor) else y
+    den = np.linalg.norm(ref)
+    return np.linalg.norm(y - ref) / (den if den > 0 else 1.0)
+
+
+def _quant(w):
+    wd = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    q = nv.quantize_fos(wd)
+    r = oracle.quantize_fos(w)
+    torch.cuda.synchronize()
+    assert np.array_equal(q.codes.cpu().numpy(), r.codes) and np.array_equal(q.scales.cpu().numpy(), r.scales)
+    return q, r
+
+
+def test_tiny_config():
+    w, x = synth.tiny(0)
+    q, r = _quant(w)
+    ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+    for dt in (torch.bfloat16, torch.float32):
+        y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt)
+        assert _rel(y, ref) <= TOL[dt]
+
+
+SHAPES = [
+    # (m, n, k): tails in every dimension, K % 32 == 16, one K step, many splits
+    (1, 64, 256), (3, 17, 48), (16, 100, 160), (17, 200, 4096), (33, 129, 528),
+    (48, 512, 4096), (64, 130, 272), (5, 300, 14336), (2, 1, 16), (1, 4096, 4096),
+]
+
+
+@pytest.mark.parametrize("path", [nv.PATH_SKINNY, nv.PATH_TILED])
+@pytest.mark.parametrize("impl", [nv.IMPL_PORTABLE, nv.IMPL_HWCVT])
+def test_shapes_both_paths(path, impl):
+    for i, (m, n, k) in enumerate(SHAPES):
+        print("shape", m, n, k, "path", path, "impl", impl, flush=True)
+        w = synth.student_t_weights(n, k, seed=200 + i)
+        q, r = _quant(w)
+        x = synth.activations(m, k, seed=300 + i)
+        ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+        for dt in (torch.bfloat16, torch.float32):
+            y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt, path=path, impl=impl)
+            torch.cuda.synchronize()
+            e = _rel(y, ref)
+            assert e <= TOL[dt], (m, n, k, dt, e)
+
+
+@pytest.mark.parametrize("split", [1, 2, 3, 7, 64])
+def test_forced_split_k(split):
+    m, n, k = 8, 256, 4096
+    w = synth.student_t_weights(n, k, seed=400)
+    q, r = _quant(w)
+    x = synth.activations(m, k, seed=401)
+    ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+    y = nv.w4a16_gemm(x.cuda(), q, out_dtype=torch.float32, path=nv.PATH_SKINNY, split_k=split)
+    assert _rel(y, ref) <= 1e-5
+
+
+@pytest.mark.parametrize("path", [nv.PATH_SKINNY, nv.PATH_TILED])
+def test_one_hot_exact(path):
+    """x = e_k with s_t a power of two: y[:, n] = W_hat[n, k] exactly."""
+    n, k = 96, 256
+    w = synth.student_t_weights(n, k, seed=500)
+    w[0, 0] = np.float32(2688 * 2.0 ** -8)  # tensor amax -> s_t = 2^-8
+    q, r = _quant(w)
+    assert r.tensor_scale == np.float32(2.0 ** -8)
+    wh = oracle.dequant_f64(r.codes, r.scales, r.tensor_scale)
+    for k0 in range(0, k, 64):
+        x = torch.zeros(min(48, k - k0), k, dtype=torch.bfloat16)
+        x[torch.arange(x.shape[0]), k0 + torch.arange(x.shape[0])] = 1.0
+        y = nv.w4a16_gemm(x.cuda(), q, out_dtype=torch.float32, path=path).double().cpu().numpy()
+        assert np.array_equal(y, wh[:, k0:k0 + x.shape[0]].T)
+
+
+def test_empty_and_zero_k():
+    q = nv.quantize_fos(torch.zeros((32, 64), dtype=torch.float32, device="cuda"))
+    y = nv.w4a16_gemm(torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda"), q)
+    assert y.shape == (0, 32)
+    q0 = nv.quantize_fos(torch.zeros((32, 0), dtype=torch.float32, device="cuda"))
+    for path in (nv.PATH_SKINNY, nv.PATH_TILED):
+        y = nv.w4a16_gemm(torch.zeros((4, 0), dtype=torch.bfloat16, device="cuda"), q0,
+                          out_dtype=torch.float32, path=path)
+        torch.cuda.synchronize()
+        assert torch.count_nonzero(y).item() == 0
+
+
+def test_deterministic():
+    w = synth.student_t_weights(4096, 4096, 2)
+    q, r = _quant(w)
+    for m in (1, 48, 256):
+        x = synth.activations(m, 4096, seed=synth.activation_seed(m)).cuda()
+        a = nv.w4a16_gemm(x, q, out_dtype=torch.float32)
+        b = nv.w4a16_gemm(x, q, out_dtype=torch.float32)
+        assert torch.equal(a, b)
+
+
+def test_single_layer_config_all_m():
+    """4096 x 4096 Student-t layer, M in {1, 8, 16, 32, 48}, default dispatch
+    (the launch configuration the bench times)."""
+    (name, n, k, seed), = synth.SINGLE_LAYER["layers"]
+    w = synth.student_t_weights(n, k, seed)
+    q, r = _quant(w)
+    for m in synth.SINGLE_LAYER["m"]:
+        x = synth.activations(m, k, synth.activation_seed(m))
+        ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+        for dt in (torch.bfloat16, torch.float32):
+            y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt)
+            e = _rel(y, ref)
+            print(f"{name} m={m} {dt}: rel err {e:.3e}")
+            assert e <= TOL[dt]
+
+
+@pytest.mark.parametrize("layer", synth.MLP_SET["layers"], ids=lambda l: l[0])
+def test_mlp_config(layer):
+    name, n, k, seed = layer
+    w = synth.student_t_weights(n, k, seed)
+    q, r = _quant(w)
+    for m in synth.MLP_SET["m"]:
+        x = synth.activations(m, k, synth.activation_seed(m))
+        ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+        y = nv.w4a16_gemm(x.cuda(), q)
+        assert _rel(y, ref) <= 2e-3, (name, m)
+
+
+@pytest.mark.parametrize("layer", synth.LARGE_M["layers"], ids=lambda l: l[0])
+def test_large_m_config_sampled_rows(layer):
+    """Large-M prefill shapes: every output row is computed on the GPU; the
+    oracle checks a sample of 64 rows (and all columns) per M."""
+    name, n, k, seed = layer
+    w = synth.student_t_weights(n, k, seed)
+    q, r = _quant(w)
+    wh = oracle.dequant_f64(r.codes, r.scales, r.tensor_scale)
+    rng = np.random.default_rng(7)
+    for m in synth.LARGE_M["m"]:
+        x = synth.activations(m, k, synth.activation_seed(m))
+        y = nv.w4a16_gemm(x.cuda(), q).double().cpu().numpy()
+        rows = np.sort(rng.choice(m, size=min(64, m), replace=False))
+        ref = x[rows].double().numpy() @ wh.T
+        assert _rel(y[rows], ref) <= 2e-3, (name, m)
+        assert np.isfinite(y).all()

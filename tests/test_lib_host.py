@@ -1,0 +1,113 @@
+"""Host-side tests of libnvfp4.so (CPU only: no kernel is launched).
+
+The library must load without a GPU, export every symbol include/nvfp4.h
+declares, and reject invalid arguments on the host before any HIP call.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_gemm_amd as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(nv.LIB_PATH):
+        from bit_gemm_amd import build
+        build.build()
+    return nv.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"NVFP4_API\s+[\w\s\*]+?\b(nvfp4_\w+)\s*\(", text)
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(L, name), name
+    assert set(names) == set(nv.SIGNATURES)
+
+
+def test_status_strings_and_version(L):
+    for code, name in nv.STATUS_NAMES.items():
+        assert L.nvfp4_status_string(code).decode() == name
+    assert L.nvfp4_status_string(99).decode() == "NVFP4_ERR_UNKNOWN"
+    assert nv.version() == "0.1.0"
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+ODD = 0x10008   # 8-byte aligned only
+
+
+def test_quantize_rejects_bad_arguments_on_host(L):
+    q = L.nvfp4_quantize_fos
+    assert q(FAKE, 4, 24, None, FAKE, FAKE, FAKE, FAKE, None, None) == 2  # k % 16
+    assert "multiple of 16" in L.nvfp4_last_error().decode()
+    assert q(FAKE, -1, 32, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert q(FAKE, 4, 32, None, None, FAKE, FAKE, FAKE, None, None) == 1  # amax_out
+    assert q(None, 4, 32, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1  # w
+    assert q(ODD, 4, 32, None, FAKE, FAKE, FAKE, FAKE, None, None) == 3  # misaligned w
+    assert q(FAKE, 4, 32, None, FAKE + 2, FAKE, FAKE, FAKE, None, None) == 3
+    assert q(FAKE, 1 << 31, 32, None, FAKE, FAKE, FAKE, FAKE, None, None) == 2
+    assert L.nvfp4_quantize_fos_ex(FAKE, 4, 32, None, FAKE, FAKE, FAKE, FAKE, None, 7, None) == 1
+
+
+def test_gemm_rejects_bad_arguments_on_host(L):
+    g = L.nvfp4_w4a16_gemm_ex
+    args = lambda m, n, k, **kw: dict(dict(x=FAKE, c=FAKE, s=FAKE, t=FAKE, y=FAKE, m=m, n=n, k=k, dt=0,
+                                           ws=None, wsb=0, path=0, split=0, impl=0), **kw)
+
+    def call(d):
+        return g(d["x"], d["c"], d["s"], d["t"], d["y"], d["m"], d["n"], d["k"], d["dt"], d["ws"], d["wsb"],
+                 d["path"], d["split"], d["impl"], None)
+
+    assert call(args(1, 64, 40)) == 2
+    assert call(args(-1, 64, 64)) == 1
+    assert call(args(1, 64, 64, dt=5)) == 1
+    assert call(args(1, 64, 64, path=9)) == 1
+    assert call(args(1, 64, 64, impl=9)) == 1
+    assert call(args(1, 64, 64, split=-1)) == 1
+    assert call(args(65, 64, 64, path=1)) == 2  # skinny takes m <= 64
+    assert call(args(1, 64, 64, x=ODD)) == 3
+    assert call(args(1, 64, 64, y=None)) == 1
+    need = L.nvfp4_w4a16_gemm_workspace_size(1, 4096, 4096)
+    assert need > 0
+    assert call(args(1, 4096, 4096, wsb=need - 1, ws=FAKE)) == 4
+    assert call(args(1, 4096, 4096, wsb=need, ws=None)) == 1
+    assert call(args(1, 4096, 4096, wsb=need, ws=ODD)) == 3
+
+
+def test_dequant_rejects_bad_arguments_on_host(L):
+    d = L.nvfp4_dequant
+    assert d(FAKE, FAKE, FAKE, FAKE, 4, 20, 0, None) == 2
+    assert d(FAKE, FAKE, FAKE, FAKE, 4, 32, 3, None) == 1
+    assert d(None, FAKE, FAKE, FAKE, 4, 32, 0, None) == 1
+    assert d(FAKE, FAKE, FAKE, ODD, 4, 32, 0, None) == 3
+    assert d(None, None, None, None, 0, 32, 0, None) == 0  # empty: nothing to do
+
+
+def test_dispatch_and_workspace_plan(L):
+    assert L.nvfp4_w4a16_gemm_path(1, 4096, 4096) == nv.PATH_SKINNY
+    assert L.nvfp4_w4a16_gemm_path(48, 4096, 4096) == nv.PATH_SKINNY
+    assert L.nvfp4_w4a16_gemm_path(49, 4096, 4096) == nv.PATH_TILED
+    assert L.nvfp4_w4a16_gemm_workspace_size(64, 4096, 4096) == 0  # tiled: none
+    assert L.nvfp4_w4a16_gemm_workspace_size(0, 4096, 4096) == 0
+    for m in (1, 8, 48):
+        for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
+            ws = L.nvfp4_w4a16_gemm_workspace_size(m, n, k)
+            assert ws % (4 * m * n) == 0
+            assert ws <= 64 * 4 * m * n
+    # forced split of 1 (a K chunk that fits in LDS): no workspace
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 2048, nv.PATH_SKINNY, 1) == 0
+    # a chunk larger than LDS allows is split further
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 1) == 2 * 4 * 8 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 4) == 4 * 4 * 8 * 4096
