@@ -1,0 +1,352 @@
+#!/usr/bin/env python
+"""Throughput of the NVFP4 FourOverSix quantizer + W4A16 GEMM hot path on one
+MI355X (gfx950).
+
+Workload (single decode-shaped layer): W fp32 4096 x 4096 drawn from a
+Student-t (nu=5) scaled to std 0.02 with 0.1% outliers x20 (seed 2); bf16
+activations N(0, 1) of shape M x 4096 for M in {1, 8, 16, 32, 48}
+(seed 9000 + M).  Synthetic data stands in for the pages' real model weights.
+
+One step = one pass of the whole hot path:
+  tensor amax -> FourOverSix quantization (codes, E4M3 scales, M=4 mask)
+  -> W4A16 GEMM at each M -> bf16 dequantization.
+Every step runs from a HIP graph (one graph per rotation slot) so the GPU is
+not starved by Python launch overhead.  Inputs rotate over enough copies that
+every kernel reads cold data from HBM (not the 256 MB last-level cache): 8
+fp32 sources (512 MiB) and 7 packed weight copies per rotation slot x 16
+slots; all copies hold the same quantized weights.
+
+Output: one JSON line (rank 0) with the whole-step throughput in GB/s of
+algorithmic HBM bytes, per-kernel rooflines measured with HIP events over
+graph-batched launches, and the CPU oracle timed on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 NVFP4 GEMM HBM GB/s (% peak) at M=1..48; quantizer GB/s; bit-exact"
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+N, K = 4096, 4096
+M_LIST = [1, 8, 16, 32, 48]
+W_SEED = 2
+ROT_SRC = 8  # fp32 source copies (8 x 64 MiB)
+ROT_SLOTS = 16  # graph variants; each owns 7 packed copies
+CAL_FLOATS = 64 * 1024 * 1024  # 256 MiB
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_fos_w4096x4096.txt")
+
+
+def parse_args(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--kernel-reps", type=int, default=20, help="launches per graph when timing one kernel")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    return ap.parse_args(argv)
+
+
+# ----------------------------------------------------------------------------
+# algorithmic bytes (what the method itself must move per launch)
+# ----------------------------------------------------------------------------
+def bytes_amax(n, k):
+    return 4 * n * k
+
+
+def bytes_fos(n, k):  # read fp32 W, write codes (1/2), scales (1/16), mask (1/16)
+    return n * k * (4 + 0.5 + 1 / 16 + 1 / 16)
+
+
+def bytes_gemm(m, n, k):  # packed weights + bf16 x + bf16 y
+    return n * k * (0.5 + 1 / 16) + 2 * m * k + 2 * m * n
+
+
+def bytes_gemm_weights(n, k):
+    return n * k * (0.5 + 1 / 16)
+
+
+def bytes_dequant_bf16(n, k):
+    return n * k * (0.5 + 1 / 16 + 2)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "bit_gemm_amd", "csrc"))):
+        with open(os.path.join(ROOT, "bit_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic_summary():
+    """HBM traffic of the FoS kernel from the committed rocprofv3 --pmc
+    summary, or None when absent or taken on other kernel sources."""
+    try:
+        kv = {}
+        with open(PROFILE_SUMMARY) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    a, b = line.split("=", 1)
+                    kv[a.strip()] = b.strip()
+        if kv.get("kernel_source_sha") != kernel_source_hash():
+            return None
+        return float(kv["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main(argv=None):
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1",
+                          "n_gpus_requested": args.gpus}))
+        return 2
+    import numpy as np
+    import torch
+
+    import bit_gemm_amd as nv
+    import synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nv.lib()
+
+    # ------- counter calibration: a plain elementwise kernel of known size ----
+    # (reads 256 MiB, writes 256 MiB; rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE
+    # of this kernel give the scale of those counters on this GPU)
+    cal_a = torch.ones(CAL_FLOATS, dtype=torch.float32, device=dev)
+    cal_b = torch.empty_like(cal_a)
+    for _ in range(3):
+        torch.neg(cal_a, out=cal_b)
+    torch.cuda.synchronize()
+    del cal_a, cal_b
+
+    # ---------------- inputs -------------------------------------------------
+    w_host = synth.student_t_weights(N, K, W_SEED)
+    src = [torch.from_numpy(w_host).to(dev) for _ in range(ROT_SRC)]
+    xs = {m: synth.activations(m, K, synth.activation_seed(m)).to(dev) for m in M_LIST}
+    ys = {m: torch.empty((m, N), dtype=torch.bfloat16, device=dev) for m in M_LIST}
+    ws_bytes = max(nv.workspace_size(m, N, K) for m in M_LIST)
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    deq_out = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    amax_bufs = torch.empty((ROT_SLOTS, 1), dtype=torch.float32, device=dev)
+    n_packed = 7 * ROT_SLOTS
+
+    def packed(i):
+        return nv.NVFP4Weight(codes=codes_all[i], scales=scales_all[i], tensor_scale=ts_all[i], amax=am_all[i],
+                              m4_mask=mask_all[i])
+
+    codes_all = torch.empty((n_packed, N, K // 2), dtype=torch.uint8, device=dev)
+    scales_all = torch.empty((n_packed, N, K // 16), dtype=torch.uint8, device=dev)
+    mask_all = torch.empty((n_packed, N, K // 16), dtype=torch.uint8, device=dev)
+    ts_all = torch.empty((n_packed, 1), dtype=torch.float32, device=dev)
+    am_all = torch.empty((n_packed, 1), dtype=torch.float32, device=dev)
+    for i in range(n_packed):
+        nv.quantize_fos(src[0], out=packed(i))
+    torch.cuda.synchronize()
+
+    # ---------------- one step, per rotation slot ----------------------------
+    def op_amax(v):
+        nv.tensor_amax(src[v % ROT_SRC], out=amax_bufs[v])
+
+    def op_fos(v):
+        nv.quantize_fos(src[v % ROT_SRC], amax=amax_bufs[v], out=packed(7 * v))
+
+    def op_gemm(v, j):
+        m = M_LIST[j]
+        nv.w4a16_gemm(xs[m], packed(7 * v + 1 + j), out=ys[m], workspace=workspace)
+
+    def op_dequant(v):
+        nv.dequant(packed(7 * v + 6), torch.bfloat16, out=deq_out)
+
+    def step(v):
+        op_amax(v)
+        op_fos(v)
+        for j in range(len(M_LIST)):
+            op_gemm(v, j)
+        op_dequant(v)
+
+    stream = torch.cuda.Stream()
+    graphs = []
+    with torch.cuda.stream(stream):
+        for v in range(ROT_SLOTS):  # eager warm-up of every path before capture
+            step(v)
+    torch.cuda.synchronize()
+    for v in range(ROT_SLOTS):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            step(v)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    # ---------------- timed region: K whole steps ----------------------------
+    for s in range(args.warmup):
+        graphs[s % ROT_SLOTS].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        graphs[(args.warmup + s) % ROT_SLOTS].replay()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    step_bytes = (bytes_amax(N, K) + bytes_fos(N, K) + sum(bytes_gemm(m, N, K) for m in M_LIST)
+                  + bytes_dequant_bf16(N, K))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # ---------------- per-kernel durations: HIP events over graph batches ----
+    def time_op(fn, L):
+        """Average launch duration of fn(r) over a graph of L launches whose
+        r-th launch touches rotation copy r (so reads stay cold)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for r in range(L):
+                fn(r)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        reps = 5
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            ev1.record(stream)
+        ev1.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / (reps * L)  # microseconds per launch
+
+    def gemm_any(r, j):  # r-th launch reads packed copy r (all copies: ~1 GiB)
+        m = M_LIST[j]
+        nv.w4a16_gemm(xs[m], packed(r % n_packed), out=ys[m], workspace=workspace)
+
+    def dequant_any(r):
+        nv.dequant(packed(r % n_packed), torch.bfloat16, out=deq_out)
+
+    L = args.kernel_reps
+    kernels = {}
+    kernels["amax"] = dict(us=time_op(lambda r: op_amax(r % ROT_SLOTS), L), bytes=bytes_amax(N, K), launches=2,
+                           note="fill + amax reduction kernels")
+    kernels["fos_quantize"] = dict(us=time_op(lambda r: op_fos(r % ROT_SLOTS), L), bytes=bytes_fos(N, K),
+                                   launches=1)
+    for j, m in enumerate(M_LIST):
+        kernels[f"gemm_m{m}"] = dict(us=time_op(lambda r, j=j: gemm_any(r, j), n_packed), bytes=bytes_gemm(m, N, K),
+                                     weight_bytes=bytes_gemm_weights(N, K),
+                                     path=nv.gemm_path(m, N, K),
+                                     flops=2 * m * N * K)
+    kernels["dequant_bf16"] = dict(us=time_op(dequant_any, n_packed), bytes=bytes_dequant_bf16(N, K), launches=1)
+    for name, kd in kernels.items():
+        kd["gbs"] = kd["bytes"] / (kd["us"] * 1e-6) / 1e9
+        kd["frac_hbm"] = kd["gbs"] / HBM_PEAK_GBS
+        if "weight_bytes" in kd:
+            kd["weight_gbs"] = kd["weight_bytes"] / (kd["us"] * 1e-6) / 1e9
+            kd["weight_frac_hbm"] = kd["weight_gbs"] / HBM_PEAK_GBS
+            kd["tflops"] = kd["flops"] / (kd["us"] * 1e-6) / 1e12
+    dominant = max(kernels, key=lambda k: kernels[k]["us"])
+    dk = kernels[dominant]
+    traffic = read_traffic_summary() if dominant == "fos_quantize" else None
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(dk["gbs"], 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(dk["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": round(dk["us"], 3)}
+
+    gemm_w_bytes = sum(bytes_gemm_weights(N, K) for _ in M_LIST)
+    gemm_us = sum(kernels[f"gemm_m{m}"]["us"] for m in M_LIST)
+    gemm_summary = {
+        "weight_gbs_all_m": round(gemm_w_bytes / (gemm_us * 1e-6) / 1e9, 1),
+        "weight_frac_hbm_all_m": round(gemm_w_bytes / (gemm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "per_m": {m: {"us": round(kernels[f"gemm_m{m}"]["us"], 3),
+                      "weight_gbs": round(kernels[f"gemm_m{m}"]["weight_gbs"], 1),
+                      "frac_hbm": round(kernels[f"gemm_m{m}"]["weight_frac_hbm"], 4),
+                      "tflops": round(kernels[f"gemm_m{m}"]["tflops"], 2)} for m in M_LIST},
+    }
+    fos = kernels["fos_quantize"]
+    quant_us = fos["us"] + kernels["amax"]["us"]
+    quant_summary = {
+        "fos_kernel_gbs": round(fos["gbs"], 1), "fos_frac_hbm": round(fos["frac_hbm"], 4),
+        "with_amax_pass_gbs": round((bytes_fos(N, K) + bytes_amax(N, K)) / (quant_us * 1e-6) / 1e9, 1),
+        "weights_per_s": round(N * K / (quant_us * 1e-6), 1),
+        "m4_share": round(float(mask_all[0].to(torch.int64).sum().item()) / mask_all[0].numel(), 4),
+    }
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "dtype_detail": "FP4 E2M1 weights x bf16 activations on bf16 MFMA, fp32 accumulate; fp32 quantizer",
+        "data": "synthetic",
+        "config": {"workload": "single decode-shaped layer 4096x4096, Student-t(5) std 0.02 + 0.1% outliers x20, "
+                               "bf16 activations M in {1,8,16,32,48}; step = amax + FourOverSix quantize + "
+                               "5 W4A16 GEMMs + bf16 dequant",
+                   "n": N, "k": K, "m": M_LIST, "step_algorithmic_bytes": step_bytes},
+        "roofline": roofline,
+        "gemm": gemm_summary,
+        "quantizer": quant_summary,
+        "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in kd.items()}
+                    for k, kd in kernels.items()},
+        "kernel_source_sha": kernel_source_hash(),
+    }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"], result["parity"] = cpu_baseline(args, w_host, xs, packed(1), step_bytes)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def cpu_baseline(args, w_host, xs_dev, q_dev, step_bytes):
+    """The CPU oracle on the same workload (whole steps, one thread), timed
+    on this host; its outputs are also compared with the GPU's."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    xs = {m: x.cpu() for m, x in xs_dev.items()}
+    reps = 0
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            r = oracle.quantize_fos(w_host)  # includes the amax pass
+            ys = {m: oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale) for m, x in xs.items()}
+            oracle.dequant(r.codes, r.scales, r.tensor_scale, "bf16")
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+    dt = time.perf_counter() - t0
+    torch.set_num_threads(torch_threads)
+    cpu = {"value": round(step_bytes * reps / dt / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": f"{reps} whole steps of the same workload (4096x4096 quantize + 5 GEMMs + dequant), "
+                     f"{dt:.1f} s, numpy/BLAS limited to 1 thread",
+           "ms_per_step": round(dt * 1e3 / reps, 1)}
+    # parity of what the GPU holds for this workload
+    codes_ok = bool(np.array_equal(q_dev.codes.cpu().numpy(), r.codes))
+    scales_ok = bool(np.array_equal(q_dev.scales.cpu().numpy(), r.scales))
+    mask_ok = bool(np.array_equal(q_dev.m4_mask.cpu().numpy(), r.m4_mask))
+    import bit_gemm_amd as nv
+
+    errs = {}
+    for m, x in xs_dev.items():
+        y = nv.w4a16_gemm(x, q_dev).double().cpu().numpy()
+        errs[m] = float(np.linalg.norm(y - ys[m]) / np.linalg.norm(ys[m]))
+    parity = {"quantize_bit_exact": codes_ok and scales_ok and mask_ok, "gemm_rel_err_max": max(errs.values()),
+              "gemm_rel_err_bound": 2e-3}
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -49,6 +49,7 @@ _c_size = ctypes.c_size_t
 SIGNATURES = {
     "nvfp4_quantize_fos": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "nvfp4_quantize_fos_ex": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_p]),
+    "nvfp4_tensor_amax": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
     "nvfp4_dequant": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p]),
     "nvfp4_w4a16_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "nvfp4_w4a16_gemm": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size, _c_p]),
@@ -144,6 +145,16 @@ def quantize_fos(w: torch.Tensor, amax: Optional[torch.Tensor] = None, with_mask
     _check(lib().nvfp4_quantize_fos_ex(
         _ptr(w), n, k, _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale), _ptr(out.codes),
         _ptr(out.scales), _ptr(out.m4_mask), impl, _stream(dev)))
+    return out
+
+
+def tensor_amax(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """max |w| of a float32 GPU tensor, as a float32 [1] GPU tensor."""
+    _need_gpu(w, "w", torch.float32)
+    n, k = (w.shape[0], w.numel() // max(1, w.shape[0])) if w.dim() else (1, 1)
+    if out is None:
+        out = torch.empty(1, dtype=torch.float32, device=w.device)
+    _check(lib().nvfp4_tensor_amax(_ptr(w), n, k, _ptr(out), _stream(w.device)))
     return out
 
 

@@ -57,9 +57,12 @@ int check_device() {
 }
 
 // Conversion implementation used by NVFP4_IMPL_DEFAULT: the gfx950
-// instructions, validated bit-exact against the portable code on the device
-// by nvfp4_selftest_cvt (counters [0]-[2] zero).
-constexpr int kDefaultImpl = nvfp4::kConvPortable;
+// instructions with a unit scale, validated bit-exact against the portable
+// code on the device by nvfp4_selftest_cvt (counters [0] and [1] zero: every
+// fp32 -> FP4 rounding and every FP4 decode).  The scaled decode forms
+// (counters [2], [3]) are not exact for non-power-of-two scales and are not
+// used.
+constexpr int kDefaultImpl = nvfp4::kConvHw;
 
 int resolve_impl(int impl, int* out) {
   if (impl == NVFP4_IMPL_DEFAULT) {
@@ -132,6 +135,23 @@ NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const 
   return NVFP4_OK;
 }
 
+NVFP4_API int nvfp4_tensor_amax(const float* w, int64_t n, int64_t k, float* amax_out, void* stream) {
+  g_last_error.clear();
+  if (n < 0 || k < 0) return fail(NVFP4_ERR_INVALID_VALUE, "negative dimension");
+  if (n >= kMaxDim || k >= kMaxDim || (n > 0 && k > kMaxElems / n))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "matrix too large");
+  if ((n * k) % 4 != 0) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "n * k must be a multiple of 4");
+  if (!amax_out) return fail(NVFP4_ERR_INVALID_VALUE, "amax_out is required");
+  if (n * k > 0 && !w) return fail(NVFP4_ERR_INVALID_VALUE, "w is required");
+  if (!aligned(amax_out, 4) || (n * k > 0 && !aligned(w, 16)))
+    return fail(NVFP4_ERR_MISALIGNED, "w must be 16-byte and amax_out 4-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = nvfp4::launch_tensor_amax(w, n * k, amax_out, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "amax launch");
+  return NVFP4_OK;
+}
+
 NVFP4_API int nvfp4_quantize_fos(const float* w, int64_t n, int64_t k, const float* amax_in,
                                  float* amax_out, float* tensor_scale, uint8_t* codes,
                                  uint8_t* scales, uint8_t* m4_mask, void* stream) {
@@ -200,7 +220,7 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
   if (k > 0 && (!x || !codes || !scales)) return fail(NVFP4_ERR_INVALID_VALUE, "x, codes and scales are required");
   if (!aligned(y, 16) || !aligned(tensor_scale, 4) || (k > 0 && (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16))))
     return fail(NVFP4_ERR_MISALIGNED, "x, codes, scales, y must be 16-byte aligned");
-  nvfp4::SkinnyPlan plan{1, 128, 0};
+  nvfp4::SkinnyPlan plan{};
   if (p == NVFP4_PATH_SKINNY) {
     plan = nvfp4::plan_skinny(m, n, k, split_k);
     if (plan.ws_bytes > 0) {

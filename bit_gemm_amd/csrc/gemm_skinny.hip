@@ -5,28 +5,33 @@
 // section "1. Quantization and GEMM dispatch"); decode is bound by reading
 // the weights from HBM ("SOAR Weekly Champion Notes 08 ...", section "01").
 //
-// Design (memory-bound): the packed weights are read exactly once, with
-// 16-byte loads; activations are small and reused, so each workgroup stages
-// its K chunk of x in LDS, already in MFMA B-operand order.  Weights are the
-// MFMA A operand: each wave owns 16 weight rows; lane l holds row l%16 and 32
-// consecutive codes (two 16-element blocks) per K step of 128.  val * sigma
-// has at most 6 significant bits, so it is exact in bf16; the products are
-// accumulated in fp32 by v_mfma_f32_16x16x32_bf16 and s_t is applied once in
-// fp32 at the end.  The K dimension is split over grid.y; with more than one
-// split the fp32 partial sums go to a workspace and k_reduce adds them in
-// split order (deterministic).
+// Two kernels:
+//  * k_skinny_fk (default for m <= 16): a workgroup owns 16 weight rows over
+//    the whole K and its waves split K; no workspace, one launch.  Loads of a
+//    group of K steps are in flight together and the next group is
+//    prefetched while the current one is consumed.
+//  * k_skinny + k_reduce (default for 16 < m <= 64, or any explicit
+//    split_k >= 1): 64 rows x one K chunk per workgroup with x staged in LDS
+//    in MFMA B-operand order (shared by the 4 waves), fp32 partials in the
+//    workspace, then a second kernel adds them in chunk order.
+// In both, val * sigma (<= 6 significant bits) is exact in bf16, products are
+// accumulated in fp32 by v_mfma_f32_16x16x32_bf16 (weights = A operand, 16
+// rows; tokens = B operand), and s_t is applied once to the fp32 sum.
+// Partial sums are always added in a fixed order: results are reproducible.
+#include <atomic>
+
 #include "launchers.h"
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kWaves = 4;          // waves per workgroup
+constexpr int kWaves = 4;
 constexpr int kRowsPerWg = 16 * kWaves;
-constexpr int kStepK = 128;        // K per main-loop step (4 MFMAs of K=32)
+constexpr int kStepK = 128;     // K per step (4 MFMAs of K=32)
+constexpr int kMaxSteps = 16;   // K steps per chunk held in registers
+constexpr int kLdsBudget = 131072;
 
-// Decode 8 codes (one dword, element i at bits 4i) scaled by sigma into an
-// MFMA bf16x8 operand, element order = code order.
 template <int IMPL>
 __device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sigma) {
   u32x4_t o;
@@ -55,119 +60,318 @@ __device__ __forceinline__ float scale_value(uint32_t s) {
   return (s & 0x80u) ? -v : v;
 }
 
-// out_mode: 0 = bf16 y, 1 = fp32 y, 2 = fp32 partial sums into ws[split].
+__device__ __forceinline__ void store_out(void* y, int64_t idx, float v, int out_f32) {
+  if (out_f32)
+    reinterpret_cast<float*>(y)[idx] = v;
+  else
+    reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)bf16_rne_bits(v);
+}
+
+// Full-K kernel (default for m <= 16).  A workgroup of W <= 8 waves owns 16
+// weight rows over the whole K.  K is cut into rounds of W * 512: in a round
+// wave w covers [round + 512 w, +512), and inside that slice lane group g
+// streams its own contiguous quarter (128 codes = 64 bytes of one row, plus
+// the 8 scale bytes of those 8 blocks, one load).  The MFMA k order inside a
+// wave is therefore (quarter, step, 8-code piece); the activations are
+// staged in the same order: each wave copies x[0:m, slice] to its own LDS
+// region with one 16-byte load per lane per token row and reads the B
+// fragments from there.  Loads of round r+1 are issued before round r is
+// consumed (two register buffers), and inside a round the issue order is
+// scales, activations, codes (the asm barriers keep the compiler from
+// merging or reordering them), so step s only waits for its own code load.
+// The W partial sums are added in wave order through LDS: results do not
+// depend on timing.
+constexpr int kSpw = 4;                 // K steps per wave per round
+constexpr int kWaveK = kSpw * kStepK;   // 512
+constexpr int kQuarter = kWaveK / 4;    // 128 codes per lane group
+
+template <int MR>
+struct Round {
+  u32x4_t cw[kSpw];   // codes: 4 x 16 bytes (32 codes each), raw loads
+  uint32_t sw[2];     // 8 scale bytes: step s uses bytes 2s, 2s+1
+  u32x4_t xv[MR];     // activation pieces of this lane (row m, 8 bf16), raw
+  uint32_t ok;        // validity bits: codes 0-3 (+4-7 upper halves), x 8, scales 9
+};
+
+__device__ __forceinline__ void mem_barrier() {
+  asm volatile("" ::: "memory");      // no merging of loads across this point
+  __builtin_amdgcn_sched_barrier(0);  // no scheduling across it either
+}
+
+__device__ __forceinline__ u32x4_t zero_unless(bool keep, u32x4_t v) {
+  return keep ? v : u32x4_t{0u, 0u, 0u, 0u};
+}
+
+// Loads of one round, branch free: every address is clamped into the
+// buffers and validity is recorded in R.ok; data outside the buffers is
+// replaced by zeros where it is used, not here, so that no load has to be
+// waited for before the next one is issued.
+template <int MR, bool K32, bool K128>
+__device__ __forceinline__ void load_round(Round<MR>& R, const uint8_t* crow, const uint8_t* srow,
+                                           bool row_ok, const uint16_t* x, int M, int K, int kw0,
+                                           int kq0, int lane) {
+  uint32_t ok = 0u;
+  // 1. scales of this lane's quarter (needed by the first step)
+  if constexpr (K128) {
+    const uint2 t = *reinterpret_cast<const uint2*>(srow + min(kq0, K - 128) / 16);
+    R.sw[0] = t.x;
+    R.sw[1] = t.y;
+    ok |= (row_ok && kq0 < K) ? (1u << 9) : 0u;
+  } else {
+    R.sw[0] = 0u;
+    R.sw[1] = 0u;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int kb = kq0 + 16 * b;
+      const uint32_t v = srow[min(kb, K - 16) / 16];
+      R.sw[b >> 2] |= ((row_ok && kb < K) ? v : 0u) << (8 * (b & 3));
+    }
+    ok |= 1u << 9;
+  }
+  mem_barrier();
+  // 2. activations: lane holds x[m][kw0 + 8 lane .. +8]
+  {
+    const int k = kw0 + 8 * lane;
+    const int kc = min(k, K - 8);
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const int mc = min(m, M - 1);
+      R.xv[m] = *reinterpret_cast<const u32x4_t*>(x + (int64_t)mc * K + kc);
+    }
+    ok |= (k < K) ? (1u << 8) : 0u;
+  }
+  mem_barrier();
+  // 3. codes, one 16-byte load per step, in step order
+#pragma unroll
+  for (int s = 0; s < kSpw; ++s) {
+    const int kk = kq0 + 32 * s;
+    if constexpr (K32) {
+      R.cw[s] = *reinterpret_cast<const u32x4_t*>(crow + min(kk, K - 32) / 2);
+      ok |= (row_ok && kk < K) ? (0x11u << s) : 0u;
+    } else {
+      const uint2 a = *reinterpret_cast<const uint2*>(crow + min(kk, K - 16) / 2);
+      const uint2 b = *reinterpret_cast<const uint2*>(crow + min(kk + 16, K - 16) / 2);
+      R.cw[s] = u32x4_t{a.x, a.y, b.x, b.y};
+      ok |= (row_ok && kk < K) ? (1u << s) : 0u;
+      ok |= (row_ok && kk + 16 < K) ? (0x10u << s) : 0u;
+    }
+    mem_barrier();
+  }
+  R.ok = ok;
+}
+
+template <int MR, int IMPL>
+__device__ __forceinline__ void compute_round(const Round<MR>& R, uint16_t* xs, int M, int g,
+                                              int r16, int lane, f32x4_t& acc) {
+  // stage this round's activations (row stride kWaveK + 8 bf16: 16-byte pad)
+  const bool xok = (R.ok >> 8) & 1u;
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+    *reinterpret_cast<u32x4_t*>(xs + m * (kWaveK + 8) + 8 * lane) = zero_unless(xok && m < M, R.xv[m]);
+  const bool sok = (R.ok >> 9) & 1u;
+  const int rb = min(r16, MR - 1);
+#pragma unroll
+  for (int s = 0; s < kSpw; ++s) {
+    const uint32_t s2 = sok ? (R.sw[s >> 1] >> (16 * (s & 1))) & 0xFFFFu : 0u;
+    const float sg0 = scale_value(s2 & 0xFFu), sg1 = scale_value(s2 >> 8);
+    const bool lo = (R.ok >> s) & 1u, hi = (R.ok >> (4 + s)) & 1u;
+    bf16x8_t a[4];
+    a[0] = dequant8<IMPL>(lo ? R.cw[s][0] : 0u, sg0);
+    a[1] = dequant8<IMPL>(lo ? R.cw[s][1] : 0u, sg0);
+    a[2] = dequant8<IMPL>(hi ? R.cw[s][2] : 0u, sg1);
+    a[3] = dequant8<IMPL>(hi ? R.cw[s][3] : 0u, sg1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4_t b = zero_unless(
+          r16 < M, *reinterpret_cast<const u32x4_t*>(xs + rb * (kWaveK + 8) + g * kQuarter + 32 * s + 8 * j));
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+    }
+  }
+}
+
+// MR = token rows staged per wave (M <= MR <= 16).
+template <int MR, int IMPL, bool K32, bool K128>
+__global__ __launch_bounds__(512) void k_skinny_fk(const uint16_t* __restrict__ x,
+                                                   const uint8_t* __restrict__ codes,
+                                                   const uint8_t* __restrict__ scales,
+                                                   const float* __restrict__ tensor_scale,
+                                                   void* __restrict__ y, int M, int N, int K,
+                                                   int rounds, int out_f32) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  // LDS: [W][64] f32x4 partial sums, then [W][MR][kWaveK + 8] bf16 activations
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + nwaves * 64 * sizeof(f32x4_t)) +
+                 wave * MR * (kWaveK + 8);
+
+  const int row = blockIdx.x * 16 + r16;
+  const bool row_ok = row < N;
+  const int rowc = min(row, N - 1);
+  const uint8_t* crow = codes + (int64_t)rowc * (K / 2);
+  const uint8_t* srow = scales + (int64_t)rowc * (K / 16);
+  const int round_k = nwaves * kWaveK;
+  const int kw = wave * kWaveK;
+
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Round<MR> RA, RB;
+  load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, kw, kw + g * kQuarter, lane);
+  for (int r = 0; r < rounds; r += 2) {
+    const int k1 = (r + 1) * round_k + kw;
+    if (r + 1 < rounds) load_round<MR, K32, K128>(RB, crow, srow, row_ok, x, M, K, k1, k1 + g * kQuarter, lane);
+    compute_round<MR, IMPL>(RA, xs, M, g, r16, lane, acc);
+    if (r + 1 >= rounds) break;
+    const int k2 = (r + 2) * round_k + kw;
+    if (r + 2 < rounds) load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, k2, k2 + g * kQuarter, lane);
+    compute_round<MR, IMPL>(RB, xs, M, g, r16, lane, acc);
+  }
+
+  // cross-wave sum in wave order; lane holds D[n = 4g + i][m = r16]
+  red[wave * 64 + lane] = acc;
+  __syncthreads();
+  if (wave != 0) return;
+  const float s_t = tensor_scale[0];
+  f32x4_t t = red[lane];
+  for (int w = 1; w < nwaves; ++w) {
+    const f32x4_t u = red[w * 64 + lane];
+    t[0] += u[0];
+    t[1] += u[1];
+    t[2] += u[2];
+    t[3] += u[3];
+  }
+  if (r16 >= M) return;
+  const int nbase = blockIdx.x * 16 + 4 * g;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (nbase + i < N) store_out(y, (int64_t)r16 * N + nbase + i, t[i] * s_t, out_f32);
+}
+
+// Split-K kernel (explicit split_k >= 2 only): 64 rows x one K chunk per
+// workgroup, fp32 partials to the workspace, then k_reduce adds them in
+// chunk order.
 template <int MT, int IMPL, bool K32>
 __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
                                                 const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales,
                                                 const float* __restrict__ tensor_scale,
                                                 void* __restrict__ y, float* __restrict__ ws,
-                                                int M, int N, int K, int kchunk, int out_mode) {
+                                                int M, int N, int K, int kchunk, int splits,
+                                                int out_f32) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int g = lane >> 4;  // lane group: which 32 codes of the K step
+  const int g = lane >> 4;
   const int r16 = lane & 15;
 
   const int k0 = blockIdx.y * kchunk;
   const int kend = min(k0 + kchunk, K);
-  const int nks = (kend - k0 + kStepK - 1) / kStepK;  // K steps in this chunk
-
-  // ---- stage x[0:16*MT, k0:kend) into LDS in B-operand order -------------
-  // piece (ks, j, mt, g, mm) = 8 bf16 of x[16 mt + mm][k0 + 128 ks + 32 g + 8 j ..]
-  {
-    const int pieces_per_row = nks * 16;  // 16-byte pieces per x row in the chunk
-    const int total = 16 * MT * pieces_per_row;
-    for (int p = threadIdx.x; p < total; p += blockDim.x) {
-      const int m = p / pieces_per_row;
-      const int k8 = p - m * pieces_per_row;
-      const int k = k0 + 8 * k8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (m < M && k < kend) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + k);
-      const int ks = k8 >> 4, rem = k8 & 15;
-      const int pg = rem >> 2, pj = rem & 3;
-      const int mt = m >> 4, mm = m & 15;
-      const int off = ((((ks * 4 + pj) * MT + mt) * 4 + pg) * 16 + mm) * 16;
-      *reinterpret_cast<uint4*>(lds + off) = v;
-    }
-  }
-  __syncthreads();
+  const int nks = (kend - k0 + kStepK - 1) / kStepK;  // <= kMaxSteps
 
   const int row = blockIdx.x * kRowsPerWg + wave * 16 + r16;
   const bool row_ok = row < N;
   const uint8_t* crow = codes + (int64_t)row * (K / 2);
   const uint8_t* srow = scales + (int64_t)row * (K / 16);
 
-  f32x4_t acc[MT];
+  u32x4_t cw[kMaxSteps];
+  uint32_t sb[kMaxSteps];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  for (int ks = 0; ks < nks; ++ks) {
-    const int kk = k0 + ks * kStepK + 32 * g;  // first of this lane's 32 codes
-    u32x4_t cw = {0u, 0u, 0u, 0u};
-    uint32_t sb0 = 0u, sb1 = 0u;
-    if constexpr (K32) {
-      if (row_ok && kk < kend) {
-        cw = *reinterpret_cast<const u32x4_t*>(crow + kk / 2);
-        const uint32_t s2 = *reinterpret_cast<const uint16_t*>(srow + kk / 16);
-        sb0 = s2 & 0xFFu;
-        sb1 = s2 >> 8;
-      }
-    } else {
-      if (row_ok && kk < kend) {
-        const uint2 a = *reinterpret_cast<const uint2*>(crow + kk / 2);
-        cw[0] = a.x;
-        cw[1] = a.y;
-        sb0 = srow[kk / 16];
-      }
-      if (row_ok && kk + 16 < kend) {
-        const uint2 b = *reinterpret_cast<const uint2*>(crow + kk / 2 + 8);
-        cw[2] = b.x;
-        cw[3] = b.y;
-        sb1 = srow[kk / 16 + 1];
-      }
-    }
-    const float sg0 = scale_value(sb0), sg1 = scale_value(sb1);
-    bf16x8_t a[4];
-    a[0] = dequant8<IMPL>(cw[0], sg0);
-    a[1] = dequant8<IMPL>(cw[1], sg0);
-    a[2] = dequant8<IMPL>(cw[2], sg1);
-    a[3] = dequant8<IMPL>(cw[3], sg1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int off = ((((ks * 4 + j) * MT + mt) * 4 + g) * 16 + r16) * 16;
-        const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(lds + off);
-        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], b, acc[mt], 0, 0, 0);
+  for (int ks = 0; ks < kMaxSteps; ++ks) {
+    cw[ks] = u32x4_t{0u, 0u, 0u, 0u};
+    sb[ks] = 0u;
+    if (ks < nks) {
+      const int kk = k0 + ks * kStepK + 32 * g;
+      if constexpr (K32) {
+        if (row_ok && kk < kend) {
+          cw[ks] = *reinterpret_cast<const u32x4_t*>(crow + kk / 2);
+          sb[ks] = *reinterpret_cast<const uint16_t*>(srow + kk / 16);
+        }
+      } else {
+        if (row_ok && kk < kend) {
+          const uint2 a = *reinterpret_cast<const uint2*>(crow + kk / 2);
+          cw[ks][0] = a.x;
+          cw[ks][1] = a.y;
+          sb[ks] = srow[kk / 16];
+        }
+        if (row_ok && kk + 16 < kend) {
+          const uint2 b = *reinterpret_cast<const uint2*>(crow + kk / 2 + 8);
+          cw[ks][2] = b.x;
+          cw[ks][3] = b.y;
+          sb[ks] |= (uint32_t)srow[kk / 16 + 1] << 8;
+        }
       }
     }
   }
 
-  // ---- epilogue: lane holds D[n = 4g + i][m = r16] of each m tile --------
+  // stage x[0:M, k0:kend) in LDS; piece (ks, j, mt, g, mm) = 8 bf16 of
+  // x[16 mt + mm][k0 + 128 ks + 32 g + 8 j ..]
+  {
+    const int pieces_per_row = nks * 16;
+    const int total = M * pieces_per_row;
+    for (int p = threadIdx.x; p < total; p += blockDim.x) {
+      const int m = p / pieces_per_row;
+      const int k8 = p - m * pieces_per_row;
+      const int k = k0 + 8 * k8;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (k < kend) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + k);
+      const int ks = k8 >> 4, rem = k8 & 15;
+      const int off = ((((ks * 4 + (rem & 3)) * MT + (m >> 4)) * 4 + (rem >> 2)) * 16 + (m & 15)) * 16;
+      *reinterpret_cast<uint4*>(lds + off) = v;
+    }
+  }
+  __syncthreads();
+
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool mrow_ok[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) mrow_ok[mt] = (mt * 16 + r16) < M;
+#pragma unroll
+  for (int ks = 0; ks < kMaxSteps; ++ks) {
+    if (ks < nks) {
+      const float sg0 = scale_value(sb[ks] & 0xFFu), sg1 = scale_value((sb[ks] >> 8) & 0xFFu);
+      bf16x8_t a[4];
+      a[0] = dequant8<IMPL>(cw[ks][0], sg0);
+      a[1] = dequant8<IMPL>(cw[ks][1], sg0);
+      a[2] = dequant8<IMPL>(cw[ks][2], sg1);
+      a[3] = dequant8<IMPL>(cw[ks][3], sg1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int off = ((((ks * 4 + j) * MT + mt) * 4 + g) * 16 + r16) * 16;
+          u32x4_t bv = *reinterpret_cast<const u32x4_t*>(lds + off);
+          if (!mrow_ok[mt]) bv = u32x4_t{0u, 0u, 0u, 0u};
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, bv),
+                                                            acc[mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+
   const float s_t = tensor_scale[0];
   const int nbase = blockIdx.x * kRowsPerWg + wave * 16 + 4 * g;
+  const int64_t mn = (int64_t)M * N;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + r16;
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int n = nbase + i;
-      if (n >= N) continue;
-      const int64_t idx = (int64_t)m * N + n;
-      if (out_mode == 2) {
-        ws[(int64_t)blockIdx.y * M * N + idx] = acc[mt][i];
-      } else if (out_mode == 1) {
-        reinterpret_cast<float*>(y)[idx] = acc[mt][i] * s_t;
-      } else {
-        reinterpret_cast<uint16_t*>(y)[idx] = (uint16_t)bf16_rne_bits(acc[mt][i] * s_t);
-      }
+      if (nbase + i >= N) continue;
+      const int64_t idx = (int64_t)m * N + nbase + i;
+      if (splits == 1)
+        store_out(y, idx, acc[mt][i] * s_t, out_f32);
+      else
+        ws[blockIdx.y * mn + idx] = acc[mt][i];
     }
   }
 }
 
-// y = s_t * sum over splits (in split order) of the fp32 partial sums.
+// y = s_t * sum over K chunks (in chunk order) of the fp32 partial sums.
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
                                                 const float* __restrict__ tensor_scale,
                                                 void* __restrict__ y, int64_t mn, int splits,
@@ -177,60 +381,128 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
     float s = ws[i];
     for (int sp = 1; sp < splits; ++sp) s += ws[(int64_t)sp * mn + i];
-    if (out_f32)
-      reinterpret_cast<float*>(y)[i] = s * s_t;
-    else
-      reinterpret_cast<uint16_t*>(y)[i] = (uint16_t)bf16_rne_bits(s * s_t);
+    store_out(y, i, s * s_t, out_f32);
   }
+}
+
+
+template <typename F>
+hipError_t set_lds_limit(F fn, size_t lds) {
+  // above 64 KiB a kernel must opt in to more dynamic LDS (gfx950 has 160
+  // KiB per CU); done once per kernel instantiation
+  static std::atomic<bool> done{false};
+  if (lds <= 65536 || done.load(std::memory_order_relaxed)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  if (e == hipSuccess) done.store(true, std::memory_order_relaxed);
+  return e;
+}
+
+template <int MR, int IMPL, bool K32>
+hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
+                     const uint8_t* codes, const uint8_t* scales, const float* ts, void* y, int M,
+                     int N, int K, int out_f32) {
+  const dim3 grid((unsigned)((N + 15) / 16));
+  const size_t lds = (size_t)p.waves * (64 * sizeof(f32x4_t) + (size_t)MR * (kWaveK + 8) * 2);
+  const int rounds = (K + p.waves * kWaveK - 1) / (p.waves * kWaveK);
+  if (K % 128 == 0) {
+    auto fn = k_skinny_fk<MR, IMPL, K32, true>;
+    hipError_t e = set_lds_limit(fn, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, grid, dim3(64 * p.waves), lds, stream, x, codes, scales, ts, y, M, N, K,
+                       rounds, out_f32);
+  } else {
+    auto fn = k_skinny_fk<MR, IMPL, K32, false>;
+    hipError_t e = set_lds_limit(fn, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fn, grid, dim3(64 * p.waves), lds, stream, x, codes, scales, ts, y, M, N, K,
+                       rounds, out_f32);
+  }
+  return hipGetLastError();
 }
 
 template <int MT, int IMPL, bool K32>
-void launch_mt(dim3 grid, size_t lds, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
-               const uint8_t* scales, const float* ts, void* y, float* ws, int M, int N, int K,
-               int kchunk, int out_mode) {
-  hipLaunchKernelGGL((k_skinny<MT, IMPL, K32>), grid, dim3(256), lds, stream, x, codes, scales, ts,
-                     y, ws, M, N, K, kchunk, out_mode);
+hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
+                     const uint8_t* codes, const uint8_t* scales, const float* ts, void* y,
+                     float* ws, int M, int N, int K, int out_f32) {
+  if constexpr (MT == 1) {
+    if (p.splits == 0) {  // full-K kernel (one token tile only)
+      const int mr = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16)));
+      switch (mr) {
+        case 1: return launch_fk<1, IMPL, K32>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+        case 2: return launch_fk<2, IMPL, K32>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+        case 4: return launch_fk<4, IMPL, K32>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+        case 8: return launch_fk<8, IMPL, K32>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+        default: return launch_fk<16, IMPL, K32>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+      }
+    }
+  }
+  auto fn = k_skinny<MT, IMPL, K32>;
+  const size_t lds = (size_t)(p.kchunk / kStepK) * 4 * MT * 4 * 16 * 16;
+  hipError_t ea = set_lds_limit(fn, lds);
+  if (ea != hipSuccess) return ea;
+  const dim3 grid((unsigned)((N + kRowsPerWg - 1) / kRowsPerWg), (unsigned)p.splits);
+  hipLaunchKernelGGL(fn, grid, dim3(256), lds, stream, x, codes, scales, ts, y, ws, M, N, K,
+                     p.kchunk, p.splits, out_f32);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  const int64_t mn = (int64_t)M * N;
+  int64_t blocks = (mn + 255) / 256;
+  if (blocks > 65535) blocks = 65535;
+  hipLaunchKernelGGL(k_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, ws, ts, y, mn,
+                     p.splits, out_f32);
+  return hipGetLastError();
 }
 
 template <int IMPL, bool K32>
-void launch_impl(int mt, dim3 grid, size_t lds, hipStream_t stream, const uint16_t* x,
-                 const uint8_t* codes, const uint8_t* scales, const float* ts, void* y, float* ws,
-                 int M, int N, int K, int kchunk, int out_mode) {
+hipError_t launch_impl(int mt, const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
+                       const uint8_t* codes, const uint8_t* scales, const float* ts, void* y,
+                       float* ws, int M, int N, int K, int out_f32) {
   switch (mt) {
-    case 1: launch_mt<1, IMPL, K32>(grid, lds, stream, x, codes, scales, ts, y, ws, M, N, K, kchunk, out_mode); break;
-    case 2: launch_mt<2, IMPL, K32>(grid, lds, stream, x, codes, scales, ts, y, ws, M, N, K, kchunk, out_mode); break;
-    case 3: launch_mt<3, IMPL, K32>(grid, lds, stream, x, codes, scales, ts, y, ws, M, N, K, kchunk, out_mode); break;
-    default: launch_mt<4, IMPL, K32>(grid, lds, stream, x, codes, scales, ts, y, ws, M, N, K, kchunk, out_mode); break;
+    case 1: return launch_mt<1, IMPL, K32>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
+    case 2: return launch_mt<2, IMPL, K32>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
+    case 3: return launch_mt<3, IMPL, K32>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
+    default: return launch_mt<4, IMPL, K32>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
   }
 }
 
-int max_chunk(int mt) {
-  // LDS per workgroup = kchunk * 32 * MT bytes; keep it <= 64 KiB
-  return mt == 1 ? 2048 : (mt == 2 ? 1024 : 512);
+// Largest split-K chunk (in K steps) for MT token tiles: registers hold 16
+// steps and the x chunk (16*MT rows, B-operand order) must fit the LDS budget.
+int max_steps(int mt) {
+  const int lds_steps = kLdsBudget / (16 * mt * kStepK * 2);
+  return lds_steps < kMaxSteps ? lds_steps : kMaxSteps;
 }
 
 }  // namespace
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
-  SkinnyPlan p{1, kStepK, 0};
+  SkinnyPlan p{};
   const int mt = (int)((m + 15) / 16);
   const int64_t ksteps = (k + kStepK - 1) / kStepK;
-  if (ksteps == 0) return p;
-  int64_t splits;
-  if (forced_splits > 0) {
-    splits = forced_splits;
-  } else {
-    const int64_t wgs_n = (n + kRowsPerWg - 1) / kRowsPerWg;
-    splits = (1024 + wgs_n - 1) / wgs_n;  // aim at ~4 workgroups per CU
+  if (forced_splits <= 0 && mt == 1 && k > 0) {
+    // full K per workgroup: one 512-wide slice per wave and round, up to 8
+    // waves (longer K loops over rounds)
+    int64_t waves = (k + kWaveK - 1) / kWaveK;
+    if (waves < 1) waves = 1;
+    if (waves > 8) waves = 8;
+    p.splits = 0;
+    p.waves = (int)waves;
+    p.steps_per_wave = kSpw;
+    return p;
   }
+  const int64_t tiles = (n + kRowsPerWg - 1) / kRowsPerWg;
+  int64_t splits = forced_splits;
+  if (splits <= 0) splits = (256 + tiles / 2) / tiles;  // about one workgroup per CU
   if (splits < 1) splits = 1;
   if (splits > 64) splits = 64;
-  if (splits > ksteps) splits = ksteps;
+  if (splits > ksteps) splits = ksteps < 1 ? 1 : ksteps;
   int64_t steps_per = (ksteps + splits - 1) / splits;
-  const int64_t max_steps = max_chunk(mt) / kStepK;
-  if (steps_per > max_steps) steps_per = max_steps;
+  if (steps_per < 1) steps_per = 1;
+  const int64_t cap = max_steps(mt);
+  if (steps_per > cap) steps_per = cap;
   p.kchunk = (int)(steps_per * kStepK);
   p.splits = (int)((ksteps + steps_per - 1) / steps_per);
+  if (p.splits < 1) p.splits = 1;
   p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
   return p;
 }
@@ -240,28 +512,15 @@ hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* sca
                          int out_f32, const SkinnyPlan& plan, void* workspace, int impl,
                          hipStream_t stream) {
   const int mt = (int)((m + 15) / 16);
-  const dim3 grid((unsigned)((n + kRowsPerWg - 1) / kRowsPerWg), (unsigned)plan.splits);
-  const int nks = plan.kchunk / kStepK;
-  const size_t lds = (size_t)nks * 4 * mt * 4 * 16 * 16;
-  const int out_mode = plan.splits > 1 ? 2 : (out_f32 ? 1 : 0);
   const bool k32 = (k % 32) == 0;
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
   float* ws = reinterpret_cast<float*>(workspace);
-  if (impl == kConvHw) {
-    if (k32) launch_impl<kConvHw, true>(mt, grid, lds, stream, xp, codes, scales, tensor_scale, y, ws, (int)m, (int)n, (int)k, plan.kchunk, out_mode);
-    else launch_impl<kConvHw, false>(mt, grid, lds, stream, xp, codes, scales, tensor_scale, y, ws, (int)m, (int)n, (int)k, plan.kchunk, out_mode);
-  } else {
-    if (k32) launch_impl<kConvPortable, true>(mt, grid, lds, stream, xp, codes, scales, tensor_scale, y, ws, (int)m, (int)n, (int)k, plan.kchunk, out_mode);
-    else launch_impl<kConvPortable, false>(mt, grid, lds, stream, xp, codes, scales, tensor_scale, y, ws, (int)m, (int)n, (int)k, plan.kchunk, out_mode);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || plan.splits == 1) return e;
-  const int64_t mn = m * n;
-  int64_t blocks = (mn + 255) / 256;
-  if (blocks > 65535) blocks = 65535;
-  hipLaunchKernelGGL(k_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, ws, tensor_scale, y,
-                     mn, plan.splits, out_f32);
-  return hipGetLastError();
+  const int M = (int)m, N = (int)n, K = (int)k;
+  if (impl == kConvHw)
+    return k32 ? launch_impl<kConvHw, true>(mt, plan, stream, xp, codes, scales, tensor_scale, y, ws, M, N, K, out_f32)
+               : launch_impl<kConvHw, false>(mt, plan, stream, xp, codes, scales, tensor_scale, y, ws, M, N, K, out_f32);
+  return k32 ? launch_impl<kConvPortable, true>(mt, plan, stream, xp, codes, scales, tensor_scale, y, ws, M, N, K, out_f32)
+             : launch_impl<kConvPortable, false>(mt, plan, stream, xp, codes, scales, tensor_scale, y, ws, M, N, K, out_f32);
 }
 
 }  // namespace nvfp4

@@ -15,14 +15,21 @@ hipError_t launch_quantize_fos(const float* w, int64_t n, int64_t k, const float
                                float* amax_out, float* tensor_scale, uint8_t* codes,
                                uint8_t* scales, uint8_t* m4_mask, int impl, hipStream_t stream);
 
+hipError_t launch_tensor_amax(const float* w, int64_t count, float* amax_out, hipStream_t stream);
+
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                           void* out, int64_t n, int64_t k, int out_f32, hipStream_t stream);
 
-// Skinny (m <= 64) split-K path.
+// Skinny (m <= 64) path.  splits == 0: full-K kernel with `waves` waves per
+// workgroup, each over `steps_per_wave` K steps of 128.  splits >= 1: split-K
+// kernel over `kchunk`-wide K chunks (+ a reduction kernel when splits > 1,
+// whose fp32 partials [splits, m, n] live in the workspace).
 struct SkinnyPlan {
-  int splits;      // number of K chunks (grid.y)
-  int kchunk;      // K elements per chunk, multiple of 128
-  size_t ws_bytes; // fp32 partial sums, splits * m * n * 4 when splits > 1
+  int splits;
+  int kchunk;
+  int waves;
+  int steps_per_wave;
+  size_t ws_bytes;
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits);
 hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* scales,

@@ -32,13 +32,15 @@ __global__ __launch_bounds__(256) void k_amax(const float4* __restrict__ w, int6
   float m = 0.0f;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // four independent loads in flight per iteration
-  for (; i + 3 * stride < n4; i += 4 * stride) {
-    float4 a = w[i], b = w[i + stride], c = w[i + 2 * stride], d = w[i + 3 * stride];
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(c.x), fabsf(c.y)), fmaxf(fabsf(c.z), fabsf(c.w))));
-    m = fmaxf(m, fmaxf(fmaxf(fabsf(d.x), fabsf(d.y)), fmaxf(fabsf(d.z), fabsf(d.w))));
+  // eight independent 16-byte loads in flight per iteration
+  constexpr int U = 8;
+  for (; i + (U - 1) * stride < n4; i += U * stride) {
+    float4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = w[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
   }
   for (; i < n4; i += stride) {
     float4 a = w[i];
@@ -152,20 +154,28 @@ __global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_
 
 }  // namespace
 
+hipError_t launch_tensor_amax(const float* w, int64_t count, float* amax_out, hipStream_t stream) {
+  hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, stream, amax_out);
+  if (count > 0) {
+    const int64_t n4 = count / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    // One block per CU: the per-block results meet in one device-scope
+    // atomic on a single address, which costs ~10 ns per block.
+    if (blocks > 256) blocks = 256;
+    hipLaunchKernelGGL(k_amax, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4*>(w), n4, amax_out);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_fos(const float* w, int64_t n, int64_t k, const float* amax_in,
                                float* amax_out, float* tensor_scale, uint8_t* codes,
                                uint8_t* scales, uint8_t* m4_mask, int impl, hipStream_t stream) {
   const int64_t count = n * k;
   const float* amax_src = amax_in;
   if (amax_src == nullptr) {
-    hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, stream, amax_out);
-    if (count > 0) {
-      const int64_t n4 = count / 4;
-      int64_t blocks = (n4 + 255) / 256;
-      if (blocks > 2048) blocks = 2048;  // 32 waves per CU, grid-stride beyond
-      hipLaunchKernelGGL(k_amax, dim3((unsigned)blocks), dim3(256), 0, stream,
-                         reinterpret_cast<const float4*>(w), n4, amax_out);
-    }
+    hipError_t e = launch_tensor_amax(w, count, amax_out, stream);
+    if (e != hipSuccess) return e;
     amax_src = amax_out;
   }
   const int64_t nblocks = count / 16;

@@ -119,6 +119,17 @@ NVFP4_API int nvfp4_quantize_fos(const float* w, int64_t n, int64_t k, const flo
                                  float* amax_out, float* tensor_scale, uint8_t* codes,
                                  uint8_t* scales, uint8_t* m4_mask, void* stream);
 
+/*
+ * nvfp4_tensor_amax - amax_out = max |w| over an fp32 [n, k] matrix (exact).
+ * The first step of nvfp4_quantize_fos, exposed so that callers can compute
+ * it separately (for example per row shard, followed by a max across shards,
+ * then nvfp4_quantize_fos with amax_in).  w: device fp32, 16-byte aligned;
+ * amax_out: device scalar.  n, k >= 0, n * k % 4 == 0 (true when k % 16 == 0).
+ * Two kernels: a fill of amax_out and the reduction (atomic max on the fp32
+ * bit pattern, which orders like the value for non-negative floats).
+ */
+NVFP4_API int nvfp4_tensor_amax(const float* w, int64_t n, int64_t k, float* amax_out, void* stream);
+
 /* Same as nvfp4_quantize_fos with an explicit conversion implementation
  * (NVFP4_IMPL_*).  Every implementation produces identical bits. */
 NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const float* amax_in,
@@ -158,10 +169,14 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *            k == 0: y = 0.
  * workspace  device buffer of at least
  *            nvfp4_w4a16_gemm_workspace_size(m, n, k) bytes, 16-byte
- *            aligned (may be NULL when that size is 0).  Its contents on
- *            entry do not matter.
- * Dispatch: m <= 48 -> memory-bound skinny split-K kernel; otherwise the
- * bf16-MFMA tiled kernel.
+ *            aligned (may be NULL when that size is 0).  Scratch: its
+ *            contents on entry do not matter.  Calls that may run
+ *            concurrently must use distinct workspaces.  m <= 16 needs
+ *            none (size 0).
+ * Dispatch: m <= 16 -> memory-bound skinny kernel, one launch, a workgroup
+ * per 16 weight rows over the whole K; 16 < m <= 48 -> split-K skinny
+ * kernel with activations shared through LDS by 64 weight rows, plus a
+ * reduction kernel; m > 48 -> the bf16-MFMA tiled kernel.
  */
 NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
@@ -169,9 +184,11 @@ NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_
                                int out_dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
 
-/* Same, with an explicit path (NVFP4_PATH_*), a requested split-K factor
- * for the skinny path (0 = heuristic; clamped to [1, 64]; more splits are
- * used when a K chunk would not fit in LDS) and a dequantization
+/* Same, with an explicit path (NVFP4_PATH_*), a split-K factor for the
+ * skinny path (0 = automatic; >= 1 = the split-K kernel with that many K
+ * chunks, clamped to [1, 64], more when a chunk would not fit in registers
+ * and LDS, plus a reduction kernel when there is more than one) and a
+ * dequantization
  * implementation (NVFP4_IMPL_*).  The skinny path requires m <= 64.  The
  * workspace size for a forced split is
  * nvfp4_w4a16_gemm_workspace_size_ex(m, n, k, path, split_k). */

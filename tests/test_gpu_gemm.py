@@ -159,3 +159,24 @@ def test_large_m_config_sampled_rows(layer):
         ref = x[rows].double().numpy() @ wh.T
         assert _rel(y[rows], ref) <= 2e-3, (name, m)
         assert np.isfinite(y).all()
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace, filled with garbage first, shared by a sequence of
+    split-K calls of different shapes: its contents on entry never matter."""
+    ws = torch.full((8 << 20,), 0xAB, dtype=torch.uint8, device="cuda")
+    seq = [(1, 256, 256, 2), (1, 64, 256, 2), (48, 1024, 4096, 0), (3, 64, 4096, 5), (16, 4096, 4096, 3),
+           (33, 64, 256, 0), (1, 64, 256, 2)]
+    cache = {}
+    for i, (m, n, k, split) in enumerate(seq):
+        if (n, k) not in cache:
+            w = synth.student_t_weights(n, k, seed=600 + len(cache))
+            cache[(n, k)] = _quant(w)
+        q, r = cache[(n, k)]
+        x = synth.activations(m, k, seed=700 + i)
+        assert nv.workspace_size(m, n, k, nv.PATH_SKINNY, split) <= ws.numel()
+        y = nv.w4a16_gemm(x.cuda(), q, out_dtype=torch.float32, workspace=ws, path=nv.PATH_SKINNY,
+                          split_k=split)
+        torch.cuda.synchronize()
+        ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+        assert _rel(y, ref) <= 1e-5, (m, n, k, split)

@@ -79,11 +79,11 @@ def test_gemm_rejects_bad_arguments_on_host(L):
     assert call(args(65, 64, 64, path=1)) == 2  # skinny takes m <= 64
     assert call(args(1, 64, 64, x=ODD)) == 3
     assert call(args(1, 64, 64, y=None)) == 1
-    need = L.nvfp4_w4a16_gemm_workspace_size(1, 4096, 4096)
+    need = L.nvfp4_w4a16_gemm_workspace_size_ex(1, 4096, 4096, nv.PATH_SKINNY, 4)
     assert need > 0
-    assert call(args(1, 4096, 4096, wsb=need - 1, ws=FAKE)) == 4
-    assert call(args(1, 4096, 4096, wsb=need, ws=None)) == 1
-    assert call(args(1, 4096, 4096, wsb=need, ws=ODD)) == 3
+    assert call(args(1, 4096, 4096, wsb=need - 1, ws=FAKE, path=1, split=4)) == 4
+    assert call(args(1, 4096, 4096, wsb=need, ws=None, path=1, split=4)) == 1
+    assert call(args(1, 4096, 4096, wsb=need, ws=ODD, path=1, split=4)) == 3
 
 
 def test_dequant_rejects_bad_arguments_on_host(L):
@@ -101,13 +101,16 @@ def test_dispatch_and_workspace_plan(L):
     assert L.nvfp4_w4a16_gemm_path(49, 4096, 4096) == nv.PATH_TILED
     assert L.nvfp4_w4a16_gemm_workspace_size(64, 4096, 4096) == 0  # tiled: none
     assert L.nvfp4_w4a16_gemm_workspace_size(0, 4096, 4096) == 0
-    for m in (1, 8, 48):
+    for m in (1, 8, 16):  # the full-K skinny kernel needs no workspace
+        for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
+            assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0
+    for m in (17, 48):  # split-K: fp32 partials [splits, m, n]
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
             ws = L.nvfp4_w4a16_gemm_workspace_size(m, n, k)
-            assert ws % (4 * m * n) == 0
-            assert ws <= 64 * 4 * m * n
-    # forced split of 1 (a K chunk that fits in LDS): no workspace
+            assert ws % (4 * m * n) == 0 and ws <= 64 * 4 * m * n
+    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 4096) == 4 * 4 * 48 * 4096
+    # explicit split K
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 2048, nv.PATH_SKINNY, 1) == 0
-    # a chunk larger than LDS allows is split further
-    assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 1) == 2 * 4 * 8 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 4) == 4 * 4 * 8 * 4096
+    # a chunk larger than registers / LDS allow is split further (16 steps max)
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 8192, nv.PATH_SKINNY, 2) == 4 * 4 * 8 * 4096
