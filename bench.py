@@ -44,7 +44,7 @@ W_SEED = 2
 ROT_SRC = 8  # fp32 source copies (8 x 64 MiB)
 ROT_SLOTS = 16  # graph variants; each owns 7 packed copies
 CAL_FLOATS = 64 * 1024 * 1024  # 256 MiB
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_fos_w4096x4096.txt")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "traffic_w4096x4096.txt")
 
 
 def parse_args(argv=None):
@@ -55,6 +55,9 @@ def parse_args(argv=None):
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the steps directly instead of from HIP graphs (for counter "
+                         "collection); prints the step time only")
     return ap.parse_args(argv)
 
 
@@ -89,9 +92,10 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def read_traffic_summary():
-    """HBM traffic of the FoS kernel from the committed rocprofv3 --pmc
-    summary, or None when absent or taken on other kernel sources."""
+def read_traffic_summary(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 --pmc
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated), or None when absent or
+    taken on other kernel sources."""
     try:
         kv = {}
         with open(PROFILE_SUMMARY) as f:
@@ -101,7 +105,7 @@ def read_traffic_summary():
                     kv[a.strip()] = b.strip()
         if kv.get("kernel_source_sha") != kernel_source_hash():
             return None
-        return float(kv["hbm_bytes_per_launch"])
+        return float(kv[f"{kernel}.hbm_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
@@ -181,6 +185,22 @@ def main(argv=None):
         op_dequant(v)
 
     stream = torch.cuda.Stream()
+    step_bytes = (bytes_amax(N, K) + bytes_fos(N, K) + sum(bytes_gemm(m, N, K) for m in M_LIST)
+                  + bytes_dequant_bf16(N, K))
+    if args.eager:
+        with torch.cuda.stream(stream):
+            for s in range(args.warmup):
+                step(s % ROT_SLOTS)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s in range(args.steps):
+                step((args.warmup + s) % ROT_SLOTS)
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+        ms = (t1 - t0) * 1e3 / args.steps
+        print(json.dumps({"metric": METRIC, "mode": "eager (profiling)", "value": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                          "unit": "GB/s", "ms_per_step": round(ms, 4), "steps": args.steps, "warmup": args.warmup}))
+        return 0
     graphs = []
     with torch.cuda.stream(stream):
         for v in range(ROT_SLOTS):  # eager warm-up of every path before capture
@@ -204,8 +224,6 @@ def main(argv=None):
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
-    step_bytes = (bytes_amax(N, K) + bytes_fos(N, K) + sum(bytes_gemm(m, N, K) for m in M_LIST)
-                  + bytes_dequant_bf16(N, K))
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     # ---------------- per-kernel durations: HIP events over graph batches ----
@@ -257,7 +275,7 @@ def main(argv=None):
             kd["tflops"] = kd["flops"] / (kd["us"] * 1e-6) / 1e12
     dominant = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dominant]
-    traffic = read_traffic_summary() if dominant == "fos_quantize" else None
+    traffic = read_traffic_summary(dominant)
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(dk["gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dk["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": round(dk["us"], 3)}

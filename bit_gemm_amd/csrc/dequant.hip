@@ -1,8 +1,7 @@
 // NVFP4 dequantization for gfx950: W_hat = sign * fl32(fl32(val * sigma) * s_t)
 // as fp32, or that value rounded to nearest-even bf16.  This is the
 // "dequant(W_block, scale)" of "SOAR Weekly Champion Notes 07 ...", section
-// "02 FourOverSix", with the tensor scale applied.  One lane per 16-element
-// block.
+// "02 FourOverSix", with the tensor scale applied.
 #include "launchers.h"
 #include "nvfp4_device.h"
 
@@ -16,37 +15,47 @@ __device__ __forceinline__ float scale_value(uint32_t s) {
   return (s & 0x80u) ? -v : v;
 }
 
+// One thread per 16 output bytes: 8 elements (bf16 output, half a block) or
+// 4 elements (fp32 output, a quarter block), so the stores of a wave cover
+// 1 KiB contiguously.  FP4 codes are decoded by the gfx950 conversion with
+// a unit scale (exact: every code's value, checked over all 256 bytes by
+// nvfp4_selftest_cvt); val * sigma is exact, then one rounding by s_t.
 template <bool F32>
-__global__ __launch_bounds__(256) void k_dequant(const uint2* __restrict__ codes,
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scales,
                                                  const float* __restrict__ tensor_scale,
-                                                 void* __restrict__ out, int64_t nblocks) {
+                                                 void* __restrict__ out, int64_t nthreads) {
+  constexpr int E = F32 ? 4 : 8;  // elements per thread
   const float s_t = tensor_scale[0];
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
-    const uint2 c = codes[b];
-    const float sigma = scale_value(scales[b]);
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const uint32_t code = ((i < 8 ? c.x : c.y) >> (4 * (i & 7))) & 0xFu;
-      v[i] = (e2m1_val_portable(code) * sigma) * s_t;
-    }
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nthreads; t += stride) {
+    const float sigma = scale_value(scales[t * E / 16]);
+    float v[E];
     if constexpr (F32) {
-      float4* o = reinterpret_cast<float4*>(out) + 4 * b;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      const uint32_t c = reinterpret_cast<const uint16_t*>(codes)[t];
+      const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+      const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+      v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
     } else {
-      uint4* o = reinterpret_cast<uint4*>(out) + 2 * b;
+      const uint32_t c = reinterpret_cast<const uint32_t*>(codes)[t];
+      const auto a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 0);
+      const auto b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 1);
+      const auto d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 2);
+      const auto e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(c, 1.0f, 3);
+      v[0] = a[0]; v[1] = a[1]; v[2] = b[0]; v[3] = b[1];
+      v[4] = d[0]; v[5] = d[1]; v[6] = e[0]; v[7] = e[1];
+    }
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        uint4 u;
-        u.x = bf16_rne_bits(v[8 * q + 0]) | (bf16_rne_bits(v[8 * q + 1]) << 16);
-        u.y = bf16_rne_bits(v[8 * q + 2]) | (bf16_rne_bits(v[8 * q + 3]) << 16);
-        u.z = bf16_rne_bits(v[8 * q + 4]) | (bf16_rne_bits(v[8 * q + 5]) << 16);
-        u.w = bf16_rne_bits(v[8 * q + 6]) | (bf16_rne_bits(v[8 * q + 7]) << 16);
-        o[q] = u;
-      }
+    for (int i = 0; i < E; ++i) v[i] = (v[i] * sigma) * s_t;
+    if constexpr (F32) {
+      reinterpret_cast<float4*>(out)[t] = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+      uint4 u;
+      u.x = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
+      u.y = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
+      u.z = bf16_rne_bits(v[4]) | (bf16_rne_bits(v[5]) << 16);
+      u.w = bf16_rne_bits(v[6]) | (bf16_rne_bits(v[7]) << 16);
+      reinterpret_cast<uint4*>(out)[t] = u;
     }
   }
 }
@@ -55,16 +64,17 @@ __global__ __launch_bounds__(256) void k_dequant(const uint2* __restrict__ codes
 
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
                           void* out, int64_t n, int64_t k, int out_f32, hipStream_t stream) {
-  const int64_t nblocks = n * k / 16;
-  if (nblocks == 0) return hipSuccess;
-  int64_t grid = (nblocks + 255) / 256;
-  if (grid > (1 << 20)) grid = 1 << 20;
+  const int64_t count = n * k;
+  if (count == 0) return hipSuccess;
+  const int64_t nthreads = count / (out_f32 ? 4 : 8);
+  int64_t grid = (nthreads + 255) / 256;
+  if (grid > 8192) grid = 8192;  // 32 workgroups per CU, grid-stride beyond
   if (out_f32)
-    hipLaunchKernelGGL(k_dequant<true>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       reinterpret_cast<const uint2*>(codes), scales, tensor_scale, out, nblocks);
+    hipLaunchKernelGGL(k_dequant<true>, dim3((unsigned)grid), dim3(256), 0, stream, codes, scales,
+                       tensor_scale, out, nthreads);
   else
-    hipLaunchKernelGGL(k_dequant<false>, dim3((unsigned)grid), dim3(256), 0, stream,
-                       reinterpret_cast<const uint2*>(codes), scales, tensor_scale, out, nblocks);
+    hipLaunchKernelGGL(k_dequant<false>, dim3((unsigned)grid), dim3(256), 0, stream, codes, scales,
+                       tensor_scale, out, nthreads);
   return hipGetLastError();
 }
 

@@ -13,8 +13,9 @@
 //               capture in a HIP graph)
 //  k_amax       grid-stride max |w| -> atomicMax on the fp32 bit pattern
 //               (non-negative floats order like their unsigned bits)
-//  k_fos        one lane per 16-element block: block amax, E4M3 scales,
-//               both candidates, SSE compare, nibble packing, stores.
+//  k_fos        one lane per 16-element block (loads coalesced and
+//               transposed through LDS): block amax, E4M3 scales, both
+//               candidates, SSE compare, nibble packing, stores.
 #include "launchers.h"
 #include "nvfp4_device.h"
 
@@ -70,10 +71,8 @@ __device__ __forceinline__ float tree16(const float* q) {
 // SSE; writes the 16 packed 4-bit codes (element i at bits 4i of the 64-bit
 // pair {lo, hi}).
 template <int IMPL>
-__device__ __forceinline__ float candidate(const float* x, float sigma, float s_t, uint32_t& lo,
-                                           uint32_t& hi) {
-  float R = fminf(1.0f / (sigma * s_t), kFltMax);
-  R = (sigma == 0.0f) ? 0.0f : R;
+__device__ __forceinline__ float candidate(const float* x, float sigma, float R, float s_t,
+                                           uint32_t& lo, uint32_t& hi) {
   float q[16];
   lo = 0u;
   hi = 0u;
@@ -109,6 +108,14 @@ __device__ __forceinline__ float candidate(const float* x, float sigma, float s_
   return tree16(q);
 }
 
+// One lane per 16-element block.  Loads are coalesced (each wave reads one
+// 4 KiB chunk = 64 blocks with 16-byte loads at consecutive addresses) and
+// transposed through LDS so that lane l then holds block l of the chunk.
+// The LDS slot of 16-byte piece q of block b is 64 b + 16 (q ^ ((b >> 2) & 3)),
+// which keeps both the writes and the 64-byte-per-lane reads free of bank
+// conflicts.  R(sigma) = min(1 / (sigma * s_t), FLT_MAX) takes only 127
+// values per tensor; the workgroup computes them once into an LDS table
+// (the same fp32 operations as the per-block form, so the same bits).
 template <int IMPL>
 __global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_t nblocks,
                                              const float* amax_src, float* amax_out,
@@ -116,6 +123,8 @@ __global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_
                                              uint8_t* __restrict__ codes,
                                              uint8_t* __restrict__ scales,
                                              uint8_t* __restrict__ mask) {
+  __shared__ float rtab[128];
+  __shared__ __attribute__((aligned(16))) float chunk[4][1024];
   const float amax = amax_src[0];
   float s_t = amax / 2688.0f;  // 2688 = 6 (FP4 max) * 448 (E4M3 max)
   s_t = (s_t == 0.0f) ? 1.0f : s_t;
@@ -124,12 +133,48 @@ __global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_
     tensor_scale[0] = s_t;
     if (amax_out != amax_src) amax_out[0] = amax;
   }
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblocks; b += stride) {
-    const float4* p = reinterpret_cast<const float4*>(w) + 4 * b;
-    const float4 t0 = p[0], t1 = p[1], t2 = p[2], t3 = p[3];
-    const float x[16] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w,
-                         t2.x, t2.y, t2.z, t2.w, t3.x, t3.y, t3.z, t3.w};
+  if (threadIdx.x < 128) {
+    const float sg = e4m3_decode(threadIdx.x);  // 127 = NaN pattern: never looked up
+    const float r = fminf(1.0f / (sg * s_t), kFltMax);
+    rtab[threadIdx.x] = (sg == 0.0f) ? 0.0f : r;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  float* cw = chunk[wave];
+  const int64_t nchunks = (nblocks + 63) / 64;
+  const int64_t wstride = (int64_t)gridDim.x * 4;
+  for (int64_t c = (int64_t)blockIdx.x * 4 + wave; c < nchunks; c += wstride) {
+    const int64_t b0 = c * 64;  // first block of the chunk
+    const int nb = (int)min<int64_t>(64, nblocks - b0);
+    // coalesced loads: piece p = lane + 64 j is elements [4p, 4p + 4) of the chunk
+    float4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = lane + 64 * j;
+      v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p < 4 * nb) v[j] = reinterpret_cast<const float4*>(w + 16 * b0)[p];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = lane + 64 * j, b = p >> 2, q = p & 3;
+      *reinterpret_cast<float4*>(cw + 16 * b + 4 * (q ^ ((b >> 2) & 3))) = v[j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 t = *reinterpret_cast<const float4*>(cw + 16 * lane + 4 * (q ^ ((lane >> 2) & 3)));
+      x[4 * q] = t.x;
+      x[4 * q + 1] = t.y;
+      x[4 * q + 2] = t.z;
+      x[4 * q + 3] = t.w;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    if (lane >= nb) continue;
+    const int64_t b = b0 + lane;
     float a = 0.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) a = fmaxf(a, fabsf(x[i]));
@@ -140,8 +185,8 @@ __global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_
     const bool valid4 = c4 <= 0x7Eu;
     const float s4 = valid4 ? s4r : 0.0f;
     uint32_t lo6, hi6, lo4, hi4;
-    const float sse6 = candidate<IMPL>(x, s6, s_t, lo6, hi6);
-    const float sse4 = candidate<IMPL>(x, s4, s_t, lo4, hi4);
+    const float sse6 = candidate<IMPL>(x, s6, rtab[c6], s_t, lo6, hi6);
+    const float sse4 = candidate<IMPL>(x, s4, rtab[valid4 ? c4 : 0u], s_t, lo4, hi4);
     const bool pick4 = valid4 && (sse4 < sse6);
     uint2 out;
     out.x = pick4 ? lo4 : lo6;
@@ -179,9 +224,10 @@ hipError_t launch_quantize_fos(const float* w, int64_t n, int64_t k, const float
     amax_src = amax_out;
   }
   const int64_t nblocks = count / 16;
-  int64_t grid = (nblocks + 255) / 256;
+  const int64_t nchunks = (nblocks + 63) / 64;  // one 64-block chunk per wave
+  int64_t grid = (nchunks + 3) / 4;
   if (grid < 1) grid = 1;  // also writes tensor_scale / amax_out for empty input
-  if (grid > (1 << 20)) grid = 1 << 20;
+  if (grid > 2048) grid = 2048;  // 8 workgroups per CU, grid-stride beyond
   if (impl == kConvHw)
     hipLaunchKernelGGL(k_fos<kConvHw>, dim3((unsigned)grid), dim3(256), 0, stream, w, nblocks,
                        amax_src, amax_out, tensor_scale, codes, scales, m4_mask);
