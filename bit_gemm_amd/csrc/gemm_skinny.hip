@@ -13,7 +13,10 @@
 //  * k_skinny + k_reduce (default for 16 < m <= 64, or any explicit
 //    split_k >= 1): 64 rows x one K chunk per workgroup with x staged in LDS
 //    in MFMA B-operand order (shared by the 4 waves), fp32 partials in the
-//    workspace, then a second kernel adds them in chunk order.
+//    workspace, then a second kernel adds them in chunk order.  (A single
+//    launch in which the last workgroup of a tile adds the partials was
+//    measured slower here: the device-coherent stores and loads it needs
+//    cost more than the second launch.)
 // In both, val * sigma (<= 6 significant bits) is exact in bf16, products are
 // accumulated in fp32 by v_mfma_f32_16x16x32_bf16 (weights = A operand, 16
 // rows; tokens = B operand), and s_t is applied once to the fp32 sum.
@@ -249,9 +252,8 @@ __global__ __launch_bounds__(512) void k_skinny_fk(const uint16_t* __restrict__ 
     if (nbase + i < N) store_out(y, (int64_t)r16 * N + nbase + i, t[i] * s_t, out_f32);
 }
 
-// Split-K kernel (explicit split_k >= 2 only): 64 rows x one K chunk per
-// workgroup, fp32 partials to the workspace, then k_reduce adds them in
-// chunk order.
+// Split-K kernel: 64 rows x one K chunk per workgroup, fp32 partials to the
+// workspace when there is more than one chunk (then k_reduce).
 template <int MT, int IMPL, bool K32>
 __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
                                                 const uint8_t* __restrict__ codes,
@@ -306,19 +308,49 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
   }
 
   // stage x[0:M, k0:kend) in LDS; piece (ks, j, mt, g, mm) = 8 bf16 of
-  // x[16 mt + mm][k0 + 128 ks + 32 g + 8 j ..]
-  {
+  // x[16 mt + mm][k0 + 128 ks + 32 g + 8 j ..].
+  if (kend - k0 == nks * kStepK) {
+    // whole K steps: direct global -> LDS copies (no registers): 1 KiB
+    // chunk c = (ks, j, mt) holds the pieces of all 64 lanes (g, mm) in lane
+    // order, so lane l's 16 bytes land at slot 64 c + l.  Token rows >= M
+    // repeat row M-1 (never read: those B operands are zeroed).
+    const int nchunk = nks * 4 * MT;
+    for (int c = wave; c < nchunk; c += kWaves) {
+      const int mt = c % MT, rj = c / MT, j = rj & 3, ks = rj >> 2;
+      const int m = min(mt * 16 + r16, M - 1);
+      const uint16_t* src = x + (int64_t)m * K + k0 + ks * kStepK + 32 * g + 8 * j;
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(lds + 1024 * c),
+                                       16, 0, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the copies (and everything else) have landed
+    asm volatile("" ::: "memory");
+  } else {
+    // ragged last chunk: eight 16-byte loads per thread in flight, then
+    // their LDS stores (zeros beyond kend)
+    constexpr int kBatch = 8;
     const int pieces_per_row = nks * 16;
     const int total = M * pieces_per_row;
-    for (int p = threadIdx.x; p < total; p += blockDim.x) {
-      const int m = p / pieces_per_row;
-      const int k8 = p - m * pieces_per_row;
-      const int k = k0 + 8 * k8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (k < kend) v = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + k);
-      const int ks = k8 >> 4, rem = k8 & 15;
-      const int off = ((((ks * 4 + (rem & 3)) * MT + (m >> 4)) * 4 + (rem >> 2)) * 16 + (m & 15)) * 16;
-      *reinterpret_cast<uint4*>(lds + off) = v;
+    for (int p0 = threadIdx.x; p0 < total; p0 += kBatch * blockDim.x) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int p = p0 + i * blockDim.x;
+        const int pc = min(p, total - 1);
+        const int m = pc / pieces_per_row;
+        const int k = k0 + 8 * (pc - m * pieces_per_row);
+        v[i] = *reinterpret_cast<const uint4*>(x + (int64_t)m * K + min(k, K - 8));
+        if (!(p < total && k < kend)) v[i] = make_uint4(0u, 0u, 0u, 0u);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int p = p0 + i * blockDim.x;
+        if (p >= total) break;
+        const int m = p / pieces_per_row;
+        const int k8 = p - m * pieces_per_row;
+        const int ks = k8 >> 4, rem = k8 & 15;
+        const int off = ((((ks * 4 + (rem & 3)) * MT + (m >> 4)) * 4 + (rem >> 2)) * 16 + (m & 15)) * 16;
+        *reinterpret_cast<uint4*>(lds + off) = v[i];
+      }
     }
   }
   __syncthreads();
@@ -354,30 +386,60 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
 
   const float s_t = tensor_scale[0];
   const int nbase = blockIdx.x * kRowsPerWg + wave * 16 + 4 * g;
+  if (splits == 1) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * s_t, out_f32);
+    }
+    return;
+  }
+  // Several K chunks: fp32 partial sums to the workspace; k_reduce adds them.
   const int64_t mn = (int64_t)M * N;
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + r16;
     if (m >= M) continue;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (nbase + i >= N) continue;
-      const int64_t idx = (int64_t)m * N + nbase + i;
-      if (splits == 1)
-        store_out(y, idx, acc[mt][i] * s_t, out_f32);
-      else
-        ws[blockIdx.y * mn + idx] = acc[mt][i];
+    float* dst = ws + blockIdx.y * mn + (int64_t)m * N + nbase;
+    if ((N & 3) == 0 && nbase + 3 < N) {  // 16-byte aligned: nbase and N are multiples of 4
+      *reinterpret_cast<float4*>(dst) = float4{acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]};
+      continue;
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (nbase + i < N) dst[i] = acc[mt][i];
   }
 }
 
-// y = s_t * sum over K chunks (in chunk order) of the fp32 partial sums.
+// y = s_t * sum over K chunks (in chunk order) of the fp32 partial sums;
+// four outputs per thread when m * n is a multiple of 4.
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
                                                 const float* __restrict__ tensor_scale,
                                                 void* __restrict__ y, int64_t mn, int splits,
                                                 int out_f32) {
   const float s_t = tensor_scale[0];
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  if ((mn & 3) == 0) {
+    const int64_t mn4 = mn >> 2;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn4; i += stride) {
+      float4 s = reinterpret_cast<const float4*>(ws)[i];
+      for (int sp = 1; sp < splits; ++sp) {
+        const float4 t = reinterpret_cast<const float4*>(ws + (int64_t)sp * mn)[i];
+        s.x += t.x;
+        s.y += t.y;
+        s.z += t.z;
+        s.w += t.w;
+      }
+      store_out(y, 4 * i, s.x * s_t, out_f32);
+      store_out(y, 4 * i + 1, s.y * s_t, out_f32);
+      store_out(y, 4 * i + 2, s.z * s_t, out_f32);
+      store_out(y, 4 * i + 3, s.w * s_t, out_f32);
+    }
+    return;
+  }
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
     float s = ws[i];
     for (int sp = 1; sp < splits; ++sp) s += ws[(int64_t)sp * mn + i];
@@ -385,15 +447,15 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
   }
 }
 
-
-template <typename F>
-hipError_t set_lds_limit(F fn, size_t lds) {
-  // above 64 KiB a kernel must opt in to more dynamic LDS (gfx950 has 160
-  // KiB per CU); done once per kernel instantiation
+// Above 64 KiB a kernel must opt in to more dynamic LDS (gfx950 has 160 KiB
+// per CU; 1 KiB is left for the kernels' static LDS).  Done once per kernel:
+// the flag is per template argument, i.e. per kernel instantiation.
+template <auto Kernel>
+hipError_t set_lds_limit(size_t lds) {
   static std::atomic<bool> done{false};
   if (lds <= 65536 || done.load(std::memory_order_relaxed)) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 159 * 1024);
   if (e == hipSuccess) done.store(true, std::memory_order_relaxed);
   return e;
 }
@@ -407,13 +469,13 @@ hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
   const int rounds = (K + p.waves * kWaveK - 1) / (p.waves * kWaveK);
   if (K % 128 == 0) {
     auto fn = k_skinny_fk<MR, IMPL, K32, true>;
-    hipError_t e = set_lds_limit(fn, lds);
+    hipError_t e = set_lds_limit<k_skinny_fk<MR, IMPL, K32, true>>(lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, grid, dim3(64 * p.waves), lds, stream, x, codes, scales, ts, y, M, N, K,
                        rounds, out_f32);
   } else {
     auto fn = k_skinny_fk<MR, IMPL, K32, false>;
-    hipError_t e = set_lds_limit(fn, lds);
+    hipError_t e = set_lds_limit<k_skinny_fk<MR, IMPL, K32, false>>(lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(fn, grid, dim3(64 * p.waves), lds, stream, x, codes, scales, ts, y, M, N, K,
                        rounds, out_f32);
@@ -439,7 +501,7 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
   }
   auto fn = k_skinny<MT, IMPL, K32>;
   const size_t lds = (size_t)(p.kchunk / kStepK) * 4 * MT * 4 * 16 * 16;
-  hipError_t ea = set_lds_limit(fn, lds);
+  hipError_t ea = set_lds_limit<k_skinny<MT, IMPL, K32>>(lds);
   if (ea != hipSuccess) return ea;
   const dim3 grid((unsigned)((N + kRowsPerWg - 1) / kRowsPerWg), (unsigned)p.splits);
   hipLaunchKernelGGL(fn, grid, dim3(256), lds, stream, x, codes, scales, ts, y, ws, M, N, K,
@@ -447,8 +509,9 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   const int64_t mn = (int64_t)M * N;
-  int64_t blocks = (mn + 255) / 256;
-  if (blocks > 65535) blocks = 65535;
+  const int64_t work = (mn & 3) == 0 ? mn / 4 : mn;  // outputs per thread: 4 or 1
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(k_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, ws, ts, y, mn,
                      p.splits, out_f32);
   return hipGetLastError();

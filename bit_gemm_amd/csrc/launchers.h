@@ -21,9 +21,9 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
                           void* out, int64_t n, int64_t k, int out_f32, hipStream_t stream);
 
 // Skinny (m <= 64) path.  splits == 0: full-K kernel with `waves` waves per
-// workgroup, each over `steps_per_wave` K steps of 128.  splits >= 1: split-K
-// kernel over `kchunk`-wide K chunks (+ a reduction kernel when splits > 1,
-// whose fp32 partials [splits, m, n] live in the workspace).
+// workgroup.  splits >= 1: split-K kernel over `kchunk`-wide K chunks, plus a
+// reduction kernel when splits > 1 (fp32 partials [splits, m, n] in the
+// workspace).
 struct SkinnyPlan {
   int splits;
   int kchunk;

@@ -187,8 +187,7 @@ NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_
 /* Same, with an explicit path (NVFP4_PATH_*), a split-K factor for the
  * skinny path (0 = automatic; >= 1 = the split-K kernel with that many K
  * chunks, clamped to [1, 64], more when a chunk would not fit in registers
- * and LDS, plus a reduction kernel when there is more than one) and a
- * dequantization
+ * and LDS) and a dequantization
  * implementation (NVFP4_IMPL_*).  The skinny path requires m <= 64.  The
  * workspace size for a forced split is
  * nvfp4_w4a16_gemm_workspace_size_ex(m, n, k, path, split_k). */
