@@ -85,11 +85,21 @@ int check_nk(int64_t n, int64_t k) {
   return NVFP4_OK;
 }
 
-constexpr int kSkinnyMaxM = 48;  // token-count threshold of the dispatch
-
-int choose_path(int64_t m, int path) {
-  if (path == NVFP4_PATH_AUTO) return m <= kSkinnyMaxM ? NVFP4_PATH_SKINNY : NVFP4_PATH_TILED;
-  return path;
+// Path selection: the lower-latency kernel for the shape ([Recap] section 1
+// picks between its two GEMMs the same way), from latencies measured on
+// MI355X (4096 x 4096, 14336 x 4096 and 4096 x 14336 weights, m = 1..4096):
+// the skinny kernels win up to m = 16 everywhere and up to m = 64 on
+// matrices of <= 32 Mi weights; on larger matrices the tiled kernel (K
+// split over workgroups) wins from m ~ 48, or from m ~ 32 when k > 8192.
+// With k % 64 != 0 the tiled path has only its single-stage kernel, so the
+// skinny path keeps m <= 64.
+int choose_path(int64_t m, int64_t n, int64_t k, int path) {
+  if (path != NVFP4_PATH_AUTO) return path;
+  if (m <= 16) return NVFP4_PATH_SKINNY;
+  if (m > 64) return NVFP4_PATH_TILED;
+  if (k % 64 != 0 || n * k <= (int64_t(1) << 25)) return NVFP4_PATH_SKINNY;
+  if (m <= 32 && k <= 8192) return NVFP4_PATH_SKINNY;
+  return NVFP4_PATH_TILED;
 }
 
 }  // namespace
@@ -178,16 +188,16 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
 }
 
 NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k) {
-  (void)n;
-  (void)k;
-  return choose_path(m, NVFP4_PATH_AUTO);
+  return choose_path(m, n, k, NVFP4_PATH_AUTO);
 }
 
 NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size_ex(int64_t m, int64_t n, int64_t k, int path,
                                                     int split_k) {
-  if (m <= 0 || n <= 0 || k <= 0) return 0;
-  if (choose_path(m, path) != NVFP4_PATH_SKINNY || m > 64) return 0;
-  return nvfp4::plan_skinny(m, n, k, split_k).ws_bytes;
+  if (m <= 0 || n <= 0 || k <= 0 || split_k < 0) return 0;
+  const int p = choose_path(m, n, k, path);
+  if (p == NVFP4_PATH_SKINNY) return m > 64 ? 0 : nvfp4::plan_skinny(m, n, k, split_k).ws_bytes;
+  if (p == NVFP4_PATH_TILED) return nvfp4::plan_tiled(m, n, k, split_k).ws_bytes;
+  return 0;
 }
 
 NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
@@ -212,7 +222,7 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
   if (split_k < 0) return fail(NVFP4_ERR_INVALID_VALUE, "split_k %d", split_k);
   int ci = 0;
   if ((st = resolve_impl(impl, &ci))) return st;
-  const int p = choose_path(m, path);
+  const int p = choose_path(m, n, k, path);
   if (p == NVFP4_PATH_SKINNY && m > 64)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "the skinny path takes m <= 64 (m=%lld)", (long long)m);
   if (m == 0 || n == 0) return NVFP4_OK;
@@ -221,14 +231,20 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
   if (!aligned(y, 16) || !aligned(tensor_scale, 4) || (k > 0 && (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16))))
     return fail(NVFP4_ERR_MISALIGNED, "x, codes, scales, y must be 16-byte aligned");
   nvfp4::SkinnyPlan plan{};
+  nvfp4::TiledPlan tplan{};
+  size_t need = 0;
   if (p == NVFP4_PATH_SKINNY) {
     plan = nvfp4::plan_skinny(m, n, k, split_k);
-    if (plan.ws_bytes > 0) {
-      if (workspace_bytes < plan.ws_bytes)
-        return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, plan.ws_bytes);
-      if (!workspace) return fail(NVFP4_ERR_INVALID_VALUE, "workspace is NULL");
-      if (!aligned(workspace, 16)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 16-byte aligned");
-    }
+    need = plan.ws_bytes;
+  } else {
+    tplan = nvfp4::plan_tiled(m, n, k, split_k);
+    need = tplan.ws_bytes;
+  }
+  if (need > 0) {
+    if (workspace_bytes < need)
+      return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!workspace) return fail(NVFP4_ERR_INVALID_VALUE, "workspace is NULL");
+    if (!aligned(workspace, 16)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   }
   if ((st = check_device())) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -237,7 +253,8 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
     e = nvfp4::launch_skinny(x, codes, scales, tensor_scale, y, m, n, k, out_dtype == NVFP4_F32, plan,
                              workspace, ci, s);
   else
-    e = nvfp4::launch_tiled(x, codes, scales, tensor_scale, y, m, n, k, out_dtype == NVFP4_F32, ci, s);
+    e = nvfp4::launch_tiled(x, codes, scales, tensor_scale, y, m, n, k, out_dtype == NVFP4_F32, tplan,
+                            workspace, ci, s);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return NVFP4_OK;
 }

@@ -21,8 +21,6 @@
 // accumulated in fp32 by v_mfma_f32_16x16x32_bf16 (weights = A operand, 16
 // rows; tokens = B operand), and s_t is applied once to the fp32 sum.
 // Partial sums are always added in a fixed order: results are reproducible.
-#include <atomic>
-
 #include "launchers.h"
 #include "nvfp4_device.h"
 
@@ -447,19 +445,6 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
   }
 }
 
-// Above 64 KiB a kernel must opt in to more dynamic LDS (gfx950 has 160 KiB
-// per CU; 1 KiB is left for the kernels' static LDS).  Done once per kernel:
-// the flag is per template argument, i.e. per kernel instantiation.
-template <auto Kernel>
-hipError_t set_lds_limit(size_t lds) {
-  static std::atomic<bool> done{false};
-  if (lds <= 65536 || done.load(std::memory_order_relaxed)) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, 159 * 1024);
-  if (e == hipSuccess) done.store(true, std::memory_order_relaxed);
-  return e;
-}
-
 template <int MR, int IMPL, bool K32>
 hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
                      const uint8_t* codes, const uint8_t* scales, const float* ts, void* y, int M,
@@ -508,13 +493,7 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
                      p.kchunk, p.splits, out_f32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  const int64_t mn = (int64_t)M * N;
-  const int64_t work = (mn & 3) == 0 ? mn / 4 : mn;  // outputs per thread: 4 or 1
-  int64_t blocks = (work + 255) / 256;
-  if (blocks > 2048) blocks = 2048;
-  hipLaunchKernelGGL(k_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, ws, ts, y, mn,
-                     p.splits, out_f32);
-  return hipGetLastError();
+  return launch_split_reduce(ws, ts, y, (int64_t)M * N, p.splits, out_f32, stream);
 }
 
 template <int IMPL, bool K32>
@@ -537,6 +516,16 @@ int max_steps(int mt) {
 }
 
 }  // namespace
+
+hipError_t launch_split_reduce(const float* ws, const float* tensor_scale, void* y, int64_t mn,
+                               int splits, int out_f32, hipStream_t stream) {
+  const int64_t work = (mn & 3) == 0 ? mn / 4 : mn;  // outputs per thread: 4 or 1
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(k_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, ws, tensor_scale, y,
+                     mn, splits, out_f32);
+  return hipGetLastError();
+}
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   SkinnyPlan p{};

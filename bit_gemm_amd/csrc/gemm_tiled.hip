@@ -6,15 +6,26 @@
 // (val * sigma is exact in bf16) into LDS, because the NVFP4 block scales
 // (E4M3 per 16) are not the block-scale layout of gfx950's scaled MFMA.
 //
-// Tile: 128 weight rows (n) x 128 token rows (m) x 64 k per step, 256
-// threads = 4 waves in a 2 x 2 grid, each wave 64 x 64 = 4 x 4 MFMA
-// 16x16x32 tiles.  Global loads of step s+1 are issued before the MFMAs of
-// step s (register prefetch); LDS holds one step of A and B fragments.
+// Two kernels:
+//  * k_lm (K a multiple of 64): BN weight rows x BM tokens per workgroup,
+//    v_mfma_f32_32x32x16_bf16 (the 32x32 shape keeps the matrix cores busy
+//    with few independent accumulators; the 16x16x32 shape needs more than a
+//    wave holds here), 64 k per step, two LDS stages (the next step's weights
+//    are dequantized and its activations stored while the current step's
+//    MFMAs run, one barrier per step), loads two steps ahead.
+//    Configurations: 256 x 256 with 8 waves (each 64 x 128) when there are
+//    enough such tiles to fill the GPU, else 128 x 128 with 4 waves, whose K
+//    loop is split over several workgroups when there are few tiles (fp32
+//    partials, then a reduction kernel adds them in split order).
+//  * k_tiled (any K): 128 x 128 x 64 tiles, 4 waves of 4 x 4
+//    v_mfma_f32_16x16x32_bf16, one LDS stage.
 #include "launchers.h"
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
 namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;  // 32x32 MFMA accumulator
 
 constexpr int kBN = 128, kBM = 128, kBK = 64;
 // LDS fragment layout (each entry 16 bytes = 8 bf16):
@@ -178,20 +189,258 @@ __global__ __launch_bounds__(256) void k_tiled(const uint16_t* __restrict__ x,
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// k_lm.  A fragment (ks, T) is 32 rows x 16 k in LDS, entry l (16 bytes) =
+// (h = l / 32, r = l % 32) holds row r of tile T at k = k0 + 8 (4 h + ks)
+// .. +8: the loader lane (h, r) owns the contiguous k0 + 32 h .. +32 of its
+// row (16 bytes of codes, 2 scales; 64 bytes of activations), and the MFMA
+// reads entry `lane` - the same k order on both operands, so the products
+// pair up.  Every LDS store and load is one contiguous 1 KiB per wave.
+// blockIdx.z = K split: steps [z * steps_per, min(K / 64, (z + 1) * steps_per)).
+template <int BN, int BM, int WGN, int WGM, int IMPL>
+__global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restrict__ x,
+                                                       const uint8_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales,
+                                                       const float* __restrict__ tensor_scale,
+                                                       void* __restrict__ y, float* __restrict__ ws,
+                                                       int M, int N, int K, int steps_per,
+                                                       int out_f32) {
+  constexpr int NW = WGN * WGM;
+  constexpr int NT = BN / 32, MT = BM / 32;    // 32-row tiles per workgroup
+  constexpr int WNT = NT / WGN, WMT = MT / WGM;  // per wave
+  constexpr int A_BYTES = 4 * NT * 1024, B_BYTES = 4 * MT * 1024;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int WA = (NT + NW - 1) / NW, WB = (MT + NW - 1) / NW;  // loader tiles per wave
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int wn = wave / WGM, wm = wave % WGM;
+  const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
+
+  u32x4_t cv[WA];
+  uint32_t sv[WA];
+  u32x4_t xv[WB][4];
+  auto load_step = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < WA; ++i) {
+      const int tile = WA * wave + i;
+      if (tile >= NT) break;
+      const int row = n0 + 32 * tile + r32;
+      const int rowc = min(row, N - 1);
+      cv[i] = *reinterpret_cast<const u32x4_t*>(codes + (int64_t)rowc * (K / 2) + k0 / 2 + 16 * h);
+      const uint32_t s2 = *reinterpret_cast<const uint16_t*>(scales + (int64_t)rowc * (K / 16) + k0 / 16 + 2 * h);
+      sv[i] = row < N ? s2 : 0u;  // sigma 0: rows past N contribute zeros
+    }
+#pragma unroll
+    for (int j = 0; j < WB; ++j) {
+      const int tile = WB * wave + j;
+      if (tile >= MT) break;
+      // rows past M read row M - 1 (finite values); their outputs are not stored
+      const int m = min(m0 + 32 * tile + r32, M - 1);
+      const uint16_t* xp = x + (int64_t)m * K + k0 + 32 * h;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xv[j][q] = *reinterpret_cast<const u32x4_t*>(xp + 8 * q);
+    }
+  };
+  auto store_step = [&](uint8_t* st) {
+    uint8_t* sA = st;
+    uint8_t* sB = st + A_BYTES;
+#pragma unroll
+    for (int i = 0; i < WA; ++i) {
+      const int tile = WA * wave + i;
+      if (tile >= NT) break;
+      const float sg0 = scale_value(sv[i] & 0xFFu), sg1 = scale_value((sv[i] >> 8) & 0xFFu);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const uint4 o = dequant8u<IMPL>(cv[i][ks], ks < 2 ? sg0 : sg1);
+        *reinterpret_cast<uint4*>(sA + ((ks * NT + tile) * 64 + lane) * 16) = o;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < WB; ++j) {
+      const int tile = WB * wave + j;
+      if (tile >= MT) break;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        *reinterpret_cast<u32x4_t*>(sB + ((ks * MT + tile) * 64 + lane) * 16) = xv[j][ks];
+    }
+  };
+
+  f32x16_t acc[WNT][WMT];
+#pragma unroll
+  for (int a = 0; a < WNT; ++a)
+#pragma unroll
+    for (int b = 0; b < WMT; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  const int s0 = blockIdx.z * steps_per;
+  const int nsteps = min(K / 64 - s0, steps_per);  // >= 1 (the plan has no empty split)
+  const int kbase = s0 * 64;
+  load_step(kbase);
+  store_step(lds);
+  if (nsteps > 1) load_step(kbase + 64);
+  for (int s = 0; s < nsteps; ++s) {
+    __syncthreads();  // stage s % 2 complete; nobody reads stage (s + 1) % 2 any more
+    const uint8_t* sA = lds + (s & 1) * STAGE;
+    const uint8_t* sB = sA + A_BYTES;
+    bf16x8_t af[2][WNT], bfr[2][WMT];
+#pragma unroll
+    for (int i = 0; i < WNT; ++i)
+      af[0][i] = *reinterpret_cast<const bf16x8_t*>(sA + ((WNT * wn + i) * 64 + lane) * 16);
+#pragma unroll
+    for (int j = 0; j < WMT; ++j)
+      bfr[0][j] = *reinterpret_cast<const bf16x8_t*>(sB + ((WMT * wm + j) * 64 + lane) * 16);
+    if (s + 1 < nsteps) {
+      store_step(lds + ((s + 1) & 1) * STAGE);
+      if (s + 2 < nsteps) load_step(kbase + (s + 2) * 64);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = ks & 1;
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int i = 0; i < WNT; ++i)
+          af[c ^ 1][i] = *reinterpret_cast<const bf16x8_t*>(sA + (((ks + 1) * NT + WNT * wn + i) * 64 + lane) * 16);
+#pragma unroll
+        for (int j = 0; j < WMT; ++j)
+          bfr[c ^ 1][j] = *reinterpret_cast<const bf16x8_t*>(sB + (((ks + 1) * MT + WMT * wm + j) * 64 + lane) * 16);
+      }
+#pragma unroll
+      for (int a = 0; a < WNT; ++a)
+#pragma unroll
+        for (int b = 0; b < WMT; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][a], bfr[c][b], acc[a][b], 0, 0, 0);
+    }
+  }
+
+  // D of a 32 x 32 tile: lane l, value v -> weight row 8 (v / 4) + 4 (l / 32)
+  // + v % 4, token l % 32.  With a K split: raw fp32 partials to plane z.
+  const bool partial = gridDim.z > 1;
+  float* plane = ws + (int64_t)blockIdx.z * M * N;
+  const float s_t = partial ? 1.0f : tensor_scale[0];
+#pragma unroll
+  for (int b = 0; b < WMT; ++b) {
+    const int m = m0 + 32 * (WMT * wm + b) + r32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int a = 0; a < WNT; ++a) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 32 * (WNT * wn + a) + 8 * q + 4 * h;
+        const float v0 = acc[a][b][4 * q] * s_t, v1 = acc[a][b][4 * q + 1] * s_t;
+        const float v2 = acc[a][b][4 * q + 2] * s_t, v3 = acc[a][b][4 * q + 3] * s_t;
+        const int64_t idx = (int64_t)m * N + n;
+        if (partial) {
+          if ((N & 3) == 0 && n + 3 < N) {
+            *reinterpret_cast<float4*>(plane + idx) = make_float4(v0, v1, v2, v3);
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (n + i < N) plane[idx + i] = vv[i];
+          }
+        } else if ((N & 3) == 0 && n + 3 < N) {  // 4 outputs, 16- or 8-byte aligned
+          if (out_f32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + idx) = make_float4(v0, v1, v2, v3);
+          } else {
+            uint2 v;
+            v.x = bf16_rne_bits(v0) | (bf16_rne_bits(v1) << 16);
+            v.y = bf16_rne_bits(v2) | (bf16_rne_bits(v3) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + idx) = v;
+          }
+        } else {
+          const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (n + i >= N) continue;
+            if (out_f32)
+              reinterpret_cast<float*>(y)[idx + i] = vv[i];
+            else
+              reinterpret_cast<uint16_t*>(y)[idx + i] = (uint16_t)bf16_rne_bits(vv[i]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BN, int BM, int WGN, int WGM, int IMPL>
+hipError_t launch_lm(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
+                     const float* ts, void* y, float* ws, int M, int N, int K, int splits,
+                     int steps_per, int out_f32, hipStream_t stream) {
+  constexpr size_t lds = 2 * (4 * (BN / 32) * 1024 + 4 * (BM / 32) * 1024);
+  hipError_t e = set_lds_limit<k_lm<BN, BM, WGN, WGM, IMPL>>(lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + BM - 1) / BM), (unsigned)splits);
+  hipLaunchKernelGGL((k_lm<BN, BM, WGN, WGM, IMPL>), grid, dim3(64 * WGN * WGM), lds, stream, x,
+                     codes, scales, ts, y, ws, M, N, K, steps_per, out_f32);
+  e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_split_reduce(ws, ts, y, (int64_t)M * N, splits, out_f32, stream);
+}
+
+template <int IMPL>
+hipError_t launch_lm_plan(const TiledPlan& p, const uint16_t* x, const uint8_t* codes,
+                          const uint8_t* scales, const float* ts, void* y, float* ws, int M, int N,
+                          int K, int out_f32, hipStream_t stream) {
+  if (p.kernel == 2)
+    return launch_lm<256, 256, 4, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
+                                           p.steps_per_split, out_f32, stream);
+  return launch_lm<128, 128, 2, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
+                                         p.steps_per_split, out_f32, stream);
+}
+
 }  // namespace
+
+TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k, int forced_splits) {
+  TiledPlan p{0, 1, 0, 0};
+  if (k < 64 || k % 64 != 0) return p;  // single-stage kernel, no split
+  const int64_t nsteps = k / 64;
+  const int64_t tiles256 = ((n + 255) / 256) * ((m + 255) / 256);
+  p.kernel = tiles256 >= 128 ? 2 : 1;
+  int64_t splits = 1;
+  if (forced_splits > 0) {
+    splits = forced_splits;
+  } else if (p.kernel == 1) {
+    // few 128 x 128 tiles: split K until there are about two workgroups
+    // per CU, keeping at least 4 steps per split
+    const int64_t tiles = ((n + 127) / 128) * ((m + 127) / 128);
+    if (tiles < 512) splits = (512 + tiles - 1) / tiles;
+    const int64_t cap = nsteps / 4 > 0 ? nsteps / 4 : 1;
+    if (splits > cap) splits = cap;
+    if (splits > 16) splits = 16;
+  }
+  if (splits > nsteps) splits = nsteps;
+  if (splits < 1) splits = 1;
+  const int64_t per = (nsteps + splits - 1) / splits;
+  p.steps_per_split = (int)per;
+  p.splits = (int)((nsteps + per - 1) / per);  // no empty split
+  p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+  return p;
+}
 
 hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scales,
                         const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
-                        int out_f32, int impl, hipStream_t stream) {
-  const dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
+                        int out_f32, const TiledPlan& plan, void* workspace, int impl,
+                        hipStream_t stream) {
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
+  float* ws = reinterpret_cast<float*>(workspace);
+  const int M = (int)m, N = (int)n, K = (int)k;
+  if (plan.kernel != 0) {
+    return impl == kConvHw
+               ? launch_lm_plan<kConvHw>(plan, xp, codes, scales, tensor_scale, y, ws, M, N, K, out_f32, stream)
+               : launch_lm_plan<kConvPortable>(plan, xp, codes, scales, tensor_scale, y, ws, M, N, K, out_f32, stream);
+  }
+  const dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
   const bool k32 = (k % 32) == 0;
   if (impl == kConvHw) {
-    if (k32) hipLaunchKernelGGL((k_tiled<kConvHw, true>), grid, dim3(256), 0, stream, xp, codes, scales, tensor_scale, y, (int)m, (int)n, (int)k, out_f32);
-    else hipLaunchKernelGGL((k_tiled<kConvHw, false>), grid, dim3(256), 0, stream, xp, codes, scales, tensor_scale, y, (int)m, (int)n, (int)k, out_f32);
+    if (k32) hipLaunchKernelGGL((k_tiled<kConvHw, true>), grid, dim3(256), 0, stream, xp, codes, scales, tensor_scale, y, M, N, K, out_f32);
+    else hipLaunchKernelGGL((k_tiled<kConvHw, false>), grid, dim3(256), 0, stream, xp, codes, scales, tensor_scale, y, M, N, K, out_f32);
   } else {
-    if (k32) hipLaunchKernelGGL((k_tiled<kConvPortable, true>), grid, dim3(256), 0, stream, xp, codes, scales, tensor_scale, y, (int)m, (int)n, (int)k, out_f32);
-    else hipLaunchKernelGGL((k_tiled<kConvPortable, false>), grid, dim3(256), 0, stream, xp, codes, scales, tensor_scale, y, (int)m, (int)n, (int)k, out_f32);
+    if (k32) hipLaunchKernelGGL((k_tiled<kConvPortable, true>), grid, dim3(256), 0, stream, xp, codes, scales, tensor_scale, y, M, N, K, out_f32);
+    else hipLaunchKernelGGL((k_tiled<kConvPortable, false>), grid, dim3(256), 0, stream, xp, codes, scales, tensor_scale, y, M, N, K, out_f32);
   }
   return hipGetLastError();
 }

@@ -37,10 +37,26 @@ hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* sca
                          int out_f32, const SkinnyPlan& plan, void* workspace, int impl,
                          hipStream_t stream);
 
-// Tiled bf16-MFMA path (any m).
+// y = s_t * (sum of `splits` fp32 planes [splits, mn] in plane order),
+// rounded to the output type.
+hipError_t launch_split_reduce(const float* ws, const float* tensor_scale, void* y, int64_t mn,
+                               int splits, int out_f32, hipStream_t stream);
+
+// Tiled bf16-MFMA path (any m).  kernel: 0 = 128 x 128 single-stage kernel
+// (any K), 1 = 128 x 128 and 2 = 256 x 256 two-stage kernels (K a multiple of
+// 64), which may split K over `splits` workgroups of `steps_per_split` 64-wide
+// steps (fp32 partials [splits, m, n] in the workspace, then the reduction).
+struct TiledPlan {
+  int kernel;
+  int splits;
+  int steps_per_split;
+  size_t ws_bytes;
+};
+TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k, int forced_splits);
 hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scales,
                         const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
-                        int out_f32, int impl, hipStream_t stream);
+                        int out_f32, const TiledPlan& plan, void* workspace, int impl,
+                        hipStream_t stream);
 
 hipError_t launch_selftest_cvt(uint32_t* counters, hipStream_t stream);
 

@@ -1,10 +1,13 @@
 // Device helpers shared by the gfx950 kernels of libnvfp4: E4M3 scale
 // rounding, E2M1 (FP4) rounding and decoding, bf16 packing, MFMA operand
-// types.  Compiled only for gfx950 (CDNA4, wave64).
+// types, and the host-side LDS opt-in.  Compiled only for gfx950 (CDNA4,
+// wave64).
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <atomic>
 
 namespace nvfp4 {
 
@@ -68,10 +71,16 @@ __device__ __forceinline__ float e2m1_val_portable(uint32_t code) {
   return __uint_as_float(__float_as_uint(e2m1_mag_portable(code & 7u)) | ((code & 8u) << 28));
 }
 
-// gfx950 scaled conversions, used with a unit scale: two fp32 -> two FP4
-// codes in bits 0-3 (first operand) and 4-7 (second) of the result, and back.
-__device__ __forceinline__ uint32_t e2m1_pack2_hw(float a, float b) {
-  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0) & 0xFFu;
+// gfx950 scaled conversions, used with a unit scale.  Each conversion turns
+// two fp32 into two FP4 codes (first operand in the low nibble) and writes
+// them to the byte of the destination that its selector names, keeping the
+// other bytes; so eight values become one word, element i at bits 4i..4i+3.
+__device__ __forceinline__ uint32_t e2m1_pack8_hw(float v0, float v1, float v2, float v3,
+                                                  float v4, float v5, float v6, float v7) {
+  uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v0, v1, 1.0f, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v2, v3, 1.0f, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v4, v5, 1.0f, 2);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v6, v7, 1.0f, 3);
 }
 
 // Round an fp32 to bf16, nearest even (finite inputs).
@@ -83,6 +92,19 @@ __device__ __forceinline__ uint32_t bf16_rne_bits(float f) {
 // Two fp32 values that are exact in bf16 -> packed bf16x2 (lo in bits 0-15).
 __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Host side: above 64 KiB a kernel must opt in to more dynamic LDS (gfx950
+// has 160 KiB per CU; 1 KiB is left for the kernels' static LDS).  Done once per kernel:
+// the flag is per template argument, i.e. per kernel instantiation.
+template <auto Kernel>
+hipError_t set_lds_limit(size_t lds) {
+  static std::atomic<bool> done{false};
+  if (lds <= 65536 || done.load(std::memory_order_relaxed)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(Kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, 159 * 1024);
+  if (e == hipSuccess) done.store(true, std::memory_order_relaxed);
+  return e;
 }
 
 }  // namespace nvfp4

@@ -67,6 +67,19 @@ __device__ __forceinline__ float tree16(const float* q) {
   return (r0 + r1) + (r2 + r3);
 }
 
+// Squared errors of elements 2J and 2J + 1 of an 8-element group whose codes
+// are packed in `word` (byte J): the hardware decode at unit scale gives the
+// signed E2M1 values, then w_hat = (val * sigma) * s_t as in the contract.
+template <int J>
+__device__ __forceinline__ void sq_err2(uint32_t word, const float* x, float sigma, float s_t,
+                                        float* q) {
+  const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, J);
+  const float e0 = x[2 * J] - (v[0] * sigma) * s_t;
+  const float e1 = x[2 * J + 1] - (v[1] * sigma) * s_t;
+  q[2 * J] = e0 * e0;
+  q[2 * J + 1] = e1 * e1;
+}
+
 // Quantize one block against one candidate scale sigma.  Returns the block
 // SSE; writes the 16 packed 4-bit codes (element i at bits 4i of the 64-bit
 // pair {lo, hi}).
@@ -91,19 +104,18 @@ __device__ __forceinline__ float candidate(const float* x, float sigma, float R,
         hi |= code << (4 * (i - 8));
     }
   } else {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t byte = e2m1_pack2_hw(x[2 * j] * R, x[2 * j + 1] * R);
-      const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(byte, 1.0f, 0);
-      const float e0 = x[2 * j] - (v[0] * sigma) * s_t;
-      const float e1 = x[2 * j + 1] - (v[1] * sigma) * s_t;
-      q[2 * j] = e0 * e0;
-      q[2 * j + 1] = e1 * e1;
-      if (j < 4)
-        lo |= byte << (8 * j);
-      else
-        hi |= byte << (8 * (j - 4));
-    }
+    lo = e2m1_pack8_hw(x[0] * R, x[1] * R, x[2] * R, x[3] * R, x[4] * R, x[5] * R, x[6] * R,
+                       x[7] * R);
+    hi = e2m1_pack8_hw(x[8] * R, x[9] * R, x[10] * R, x[11] * R, x[12] * R, x[13] * R,
+                       x[14] * R, x[15] * R);
+    sq_err2<0>(lo, x, sigma, s_t, q);
+    sq_err2<1>(lo, x, sigma, s_t, q);
+    sq_err2<2>(lo, x, sigma, s_t, q);
+    sq_err2<3>(lo, x, sigma, s_t, q);
+    sq_err2<0>(hi, x + 8, sigma, s_t, q + 8);
+    sq_err2<1>(hi, x + 8, sigma, s_t, q + 8);
+    sq_err2<2>(hi, x + 8, sigma, s_t, q + 8);
+    sq_err2<3>(hi, x + 8, sigma, s_t, q + 8);
   }
   return tree16(q);
 }
@@ -147,7 +159,9 @@ __global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_
   for (int64_t c = (int64_t)blockIdx.x * 4 + wave; c < nchunks; c += wstride) {
     const int64_t b0 = c * 64;  // first block of the chunk
     const int nb = (int)min<int64_t>(64, nblocks - b0);
-    // coalesced loads: piece p = lane + 64 j is elements [4p, 4p + 4) of the chunk
+    // coalesced loads: piece p = lane + 64 j is elements [4p, 4p + 4) of the
+    // chunk (conditional, which keeps the kernel within 64 VGPRs: 8 waves per
+    // SIMD)
     float4 v[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {

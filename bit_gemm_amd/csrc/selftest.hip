@@ -23,7 +23,8 @@ __device__ __forceinline__ uint32_t sw_code(float v) {
 }
 
 // [0]: every non-NaN fp32 bit pattern i (both signs), paired with pattern
-// i ^ 0x00400000 in the second operand to check the nibble order too.
+// i ^ 0x00400000, through all four byte selectors of the packing conversion
+// (operand order alternating, so the nibble order is checked too).
 __global__ __launch_bounds__(256) void k_round(uint32_t* counters) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   uint32_t bad = 0u, tested = 0u;
@@ -31,8 +32,9 @@ __global__ __launch_bounds__(256) void k_round(uint32_t* counters) {
     const uint32_t ba = (uint32_t)i, bb = ba ^ 0x00400000u;
     const float a = __uint_as_float(ba), b = __uint_as_float(bb);
     if (a != a || b != b) continue;  // NaN
-    const uint32_t hw = e2m1_pack2_hw(a, b);
-    const uint32_t sw = sw_code(a) | (sw_code(b) << 4);
+    const uint32_t hw = e2m1_pack8_hw(a, b, b, a, a, b, b, a);
+    const uint32_t ab = sw_code(a) | (sw_code(b) << 4), ba2 = sw_code(b) | (sw_code(a) << 4);
+    const uint32_t sw = ab | (ba2 << 8) | (ab << 16) | (ba2 << 24);
     bad += (hw != sw) ? 1u : 0u;
     tested += 1u;
   }
@@ -50,8 +52,17 @@ __global__ __launch_bounds__(256) void k_decode(uint32_t* counters) {
   const float lo = e2m1_val_portable(byte & 0xFu), hi = e2m1_val_portable(byte >> 4);
   uint32_t bad1 = 0u, bad2 = 0u, bad3 = 0u;
   if (scode == 0) {
-    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
-    bad1 = (__float_as_uint(v[0]) != __float_as_uint(lo) || __float_as_uint(v[1]) != __float_as_uint(hi)) ? 1u : 0u;
+    // the byte under test at each selector position, other bytes different
+    const uint32_t other = (byte ^ 0x5Au) * 0x01010101u;
+#define DEC_AT(J)                                                                        \
+  {                                                                                      \
+    const uint32_t wj = (other & ~(0xFFu << (8 * J))) | (byte << (8 * J));              \
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(wj, 1.0f, J);                \
+    bad1 += (__float_as_uint(v[0]) != __float_as_uint(lo) ||                             \
+             __float_as_uint(v[1]) != __float_as_uint(hi)) ? 1u : 0u;                    \
+  }
+    DEC_AT(0) DEC_AT(1) DEC_AT(2) DEC_AT(3)
+#undef DEC_AT
   }
   {
     const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, sigma, 1);

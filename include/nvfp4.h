@@ -172,11 +172,18 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *            aligned (may be NULL when that size is 0).  Scratch: its
  *            contents on entry do not matter.  Calls that may run
  *            concurrently must use distinct workspaces.  m <= 16 needs
- *            none (size 0).
- * Dispatch: m <= 16 -> memory-bound skinny kernel, one launch, a workgroup
- * per 16 weight rows over the whole K; 16 < m <= 48 -> split-K skinny
- * kernel with activations shared through LDS by 64 weight rows, plus a
- * reduction kernel; m > 48 -> the bf16-MFMA tiled kernel.
+ *            none (size 0); it holds fp32 partial sums [splits, m, n]
+ *            whenever a path splits K.
+ * Dispatch (the lower-latency kernel for the shape, [Recap] section 1, as
+ * measured on MI355X; nvfp4_w4a16_gemm_path tells which):
+ *   m <= 16 -> memory-bound skinny kernel, one launch, a workgroup per 16
+ *     weight rows over the whole K;
+ *   16 < m <= 64 -> split-K skinny kernel with activations shared through
+ *     LDS by 64 weight rows, plus a reduction kernel, when n * k <= 2^25
+ *     or k % 64 != 0 or (m <= 32 and k <= 8192); else the tiled kernel;
+ *   m > 64 -> the bf16-MFMA tiled kernel (256 x 256 or 128 x 128 tiles when
+ *     k % 64 == 0, the latter with K split over workgroups when there are
+ *     few tiles; 128 x 128 single-stage tiles for other k).
  */
 NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
@@ -184,12 +191,13 @@ NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_
                                int out_dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
 
-/* Same, with an explicit path (NVFP4_PATH_*), a split-K factor for the
- * skinny path (0 = automatic; >= 1 = the split-K kernel with that many K
+/* Same, with an explicit path (NVFP4_PATH_*), a split-K factor
+ * (0 = automatic; skinny path: >= 1 = the split-K kernel with that many K
  * chunks, clamped to [1, 64], more when a chunk would not fit in registers
- * and LDS) and a dequantization
- * implementation (NVFP4_IMPL_*).  The skinny path requires m <= 64.  The
- * workspace size for a forced split is
+ * and LDS; tiled path with k % 64 == 0: that many K splits of whole 64-wide
+ * steps, at most k / 64, fewer when the steps do not divide evenly; other k
+ * ignore it) and a dequantization implementation (NVFP4_IMPL_*).  The
+ * skinny path requires m <= 64.  The workspace size for these choices is
  * nvfp4_w4a16_gemm_workspace_size_ex(m, n, k, path, split_k). */
 NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size_ex(int64_t m, int64_t n, int64_t k, int path,
                                                     int split_k);
@@ -199,7 +207,8 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
                                   size_t workspace_bytes, int path, int split_k, int impl,
                                   void* stream);
 
-/* The path NVFP4_PATH_AUTO picks for m (NVFP4_PATH_SKINNY or _TILED). */
+/* The path NVFP4_PATH_AUTO picks for (m, n, k): NVFP4_PATH_SKINNY or
+ * NVFP4_PATH_TILED. */
 NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);
 
 /*
@@ -208,8 +217,10 @@ NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);
  * Runs on `stream` and writes 8 uint32 counters to the device buffer
  * `counters_out`:
  *  [0] fp32 -> FP4 code mismatches over every non-NaN fp32 bit pattern
- *      (both signs, including +-inf),
- *  [1] FP4 byte -> 2 x fp32 decode mismatches (256 bytes),
+ *      (both signs, including +-inf), through each of the four byte
+ *      positions the packing conversion can write,
+ *  [1] FP4 byte -> 2 x fp32 decode mismatches (256 bytes, read from each
+ *      of the four byte positions of a word),
  *  [2] FP4 byte -> 2 x fp32 with scale sigma, against fl32(val * sigma),
  *      for every E4M3 sigma in [0, 448],
  *  [3] FP4 byte -> 2 x bf16 with scale sigma, against val * sigma,

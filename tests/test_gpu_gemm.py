@@ -161,6 +161,42 @@ def test_large_m_config_sampled_rows(layer):
         assert np.isfinite(y).all()
 
 
+# Large-M kernel configurations (K a multiple of 64): 256 x 256 tiles when
+# there are >= 128 of them, else 128 x 128; ragged M and N, odd N (scalar
+# stores), a single K step, and tiny M through the tiled path.
+LM_SHAPES = [(1000, 8000, 192), (300, 700, 256), (257, 4100, 64), (130, 1001, 128), (5, 333, 128)]
+
+
+@pytest.mark.parametrize("impl", [nv.IMPL_PORTABLE, nv.IMPL_HWCVT])
+def test_large_m_kernel_configs(impl):
+    for i, (m, n, k) in enumerate(LM_SHAPES):
+        print("shape", m, n, k, "impl", impl, flush=True)
+        w = synth.student_t_weights(n, k, seed=800 + i)
+        q, r = _quant(w)
+        x = synth.activations(m, k, seed=900 + i)
+        ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+        for dt in (torch.bfloat16, torch.float32):
+            y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt, path=nv.PATH_TILED, impl=impl)
+            torch.cuda.synchronize()
+            e = _rel(y, ref)
+            assert e <= TOL[dt], (m, n, k, dt, e)
+
+
+@pytest.mark.parametrize("split", [0, 1, 2, 3, 7, 16])
+def test_tiled_split_k(split):
+    """K split over workgroups on the tiled path (fp32 partials + in-order
+    reduction); 0 = the automatic plan."""
+    m, n, k = 200, 520, 1024
+    w = synth.student_t_weights(n, k, seed=1000)
+    q, r = _quant(w)
+    x = synth.activations(m, k, seed=1001)
+    ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+    for dt in (torch.bfloat16, torch.float32):
+        y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt, path=nv.PATH_TILED, split_k=split)
+        torch.cuda.synchronize()
+        assert _rel(y, ref) <= TOL[dt], (split, dt)
+
+
 def test_workspace_reuse_across_shapes():
     """One workspace, filled with garbage first, shared by a sequence of
     split-K calls of different shapes: its contents on entry never matter."""

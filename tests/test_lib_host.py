@@ -96,11 +96,27 @@ def test_dequant_rejects_bad_arguments_on_host(L):
 
 
 def test_dispatch_and_workspace_plan(L):
-    assert L.nvfp4_w4a16_gemm_path(1, 4096, 4096) == nv.PATH_SKINNY
-    assert L.nvfp4_w4a16_gemm_path(48, 4096, 4096) == nv.PATH_SKINNY
-    assert L.nvfp4_w4a16_gemm_path(49, 4096, 4096) == nv.PATH_TILED
-    assert L.nvfp4_w4a16_gemm_workspace_size(64, 4096, 4096) == 0  # tiled: none
+    S, T = nv.PATH_SKINNY, nv.PATH_TILED
+    P = L.nvfp4_w4a16_gemm_path
+    assert P(1, 4096, 4096) == S and P(16, 14336, 14336) == S
+    assert P(48, 4096, 4096) == S and P(64, 4096, 4096) == S and P(65, 4096, 4096) == T
+    assert P(32, 14336, 4096) == S and P(33, 14336, 4096) == T and P(48, 14336, 4096) == T
+    assert P(17, 4096, 14336) == T and P(32, 4096, 14336) == T
+    assert P(48, 14336, 4112) == S  # k % 64 != 0: single-stage tiled kernel only
+    assert P(4096, 4096, 4096) == T
     assert L.nvfp4_w4a16_gemm_workspace_size(0, 4096, 4096) == 0
+    # tiled path: 128 x 128 tiles, K split until ~512 workgroups (>= 4 steps
+    # of 64 per split, at most 16 splits); 256 x 256 tiles are never split;
+    # K not a multiple of 64 takes the single-stage kernel, no split
+    T = nv.PATH_TILED
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(64, 4096, 4096, T, 0) == 16 * 4 * 64 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(4096, 4096, 4096) == 0
+    assert L.nvfp4_w4a16_gemm_workspace_size(1024, 14336, 4096) == 0
+    assert L.nvfp4_w4a16_gemm_workspace_size(1024, 4096, 4096) == 2 * 4 * 1024 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(64, 4096, 4112, T, 0) == 0
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(256, 4096, 4096, T, 3) == 3 * 4 * 256 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 5) == 2 * 4 * 100 * 256
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 1) == 0
     for m in (1, 8, 16):  # the full-K skinny kernel needs no workspace
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
             assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0
