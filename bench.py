@@ -54,6 +54,8 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="skip the per-shape GEMM report on the MLP and large-M decoder layers")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
     ap.add_argument("--eager", action="store_true",
                     help="launch the steps directly instead of from HIP graphs (for counter "
@@ -317,10 +319,81 @@ def main(argv=None):
         "kernel_source_sha": kernel_source_hash(),
     }
 
+    if not args.no_shapes:
+        result["decoder_shapes"] = decoder_shapes(args, stream, time_op, src[0])
+
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(args, w_host, xs, packed(1), step_bytes)
     print(json.dumps(result), flush=True)
     return 0
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix rate
+# decoder layer shapes (n, k)
+MLP_SHAPES = [("up_gate", 14336, 4096), ("down", 4096, 14336)]
+MLP_M = [1, 4, 16, 48]
+LARGE_SHAPES = [("attn", 4096, 4096), ("up_gate", 14336, 4096)]
+LARGE_M = [64, 256, 1024, 4096]
+
+
+def decoder_shapes(args, stream, time_op, w_dev):
+    """GEMM latency on the other decoder-layer shapes (reported beside the
+    step, not part of it): the MLP matrices at decode token counts (weight
+    GB/s against HBM) and the large-M prefill shapes (TFLOP/s against the
+    bf16 MFMA peak).  Each launch reads its own packed copy (>= 1 GiB of
+    copies per shape for the decode counts) so weights come from HBM.  The
+    weights are the single layer's Student-t matrix tiled to each shape
+    (latency does not depend on the values; drawing 58.7 M Student-t values
+    on the host would take longer than the whole run)."""
+    import torch
+
+    import bit_gemm_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    out = {"mlp": {}, "large_m": {}, "weights": "the 4096 x 4096 Student-t layer tiled to each shape"}
+
+    def copies(n, k, count):
+        w = w_dev.repeat((n + N - 1) // N, (k + K - 1) // K)[:n, :k].contiguous()
+        q = nv.quantize_fos(w)
+        del w
+        codes = q.codes.unsqueeze(0).repeat(count, 1, 1)
+        scales = q.scales.unsqueeze(0).repeat(count, 1, 1)
+        return [nv.NVFP4Weight(codes[i], scales[i], q.tensor_scale, q.amax, None) for i in range(count)]
+
+    for name, n, k in MLP_SHAPES:
+        wb = bytes_gemm_weights(n, k)
+        count = max(8, int((1 << 30) // wb))
+        qs = copies(n, k, count)
+        ws = torch.empty(max(16, max(nv.workspace_size(m, n, k) for m in MLP_M)), dtype=torch.uint8, device=dev)
+        res = {}
+        for m in MLP_M:
+            x = synth.activations(m, k, synth.activation_seed(m)).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            us = time_op(lambda r: nv.w4a16_gemm(x, qs[r % count], out=y, workspace=ws), count)
+            gbs = wb / (us * 1e-6) / 1e9
+            res[m] = {"us": round(us, 3), "weight_gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "path": "skinny" if nv.gemm_path(m, n, k) == nv.PATH_SKINNY else "tiled"}
+        out["mlp"][f"{name}_n{n}_k{k}"] = res
+        del qs, ws
+        torch.cuda.empty_cache()
+
+    for name, n, k in LARGE_SHAPES:
+        qs = copies(n, k, 4)
+        ws = torch.empty(max(16, max(nv.workspace_size(m, n, k) for m in LARGE_M)), dtype=torch.uint8, device=dev)
+        res = {}
+        for m in LARGE_M:
+            x = synth.activations(m, k, synth.activation_seed(m)).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            launches = 16 if m <= 1024 else 4
+            us = time_op(lambda r: nv.w4a16_gemm(x, qs[r % 4], out=y, workspace=ws), launches)
+            tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+            res[m] = {"us": round(us, 3), "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                      "path": "skinny" if nv.gemm_path(m, n, k) == nv.PATH_SKINNY else "tiled"}
+        out["large_m"][f"{name}_n{n}_k{k}"] = res
+        del qs, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(args, w_host, xs_dev, q_dev, step_bytes):

@@ -413,7 +413,11 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
 }
 
 // y = s_t * sum over K chunks (in chunk order) of the fp32 partial sums;
-// four outputs per thread when m * n is a multiple of 4.
+// four outputs per thread when m * n is a multiple of 4.  The planes are
+// loaded kRedBatch at a time (independent loads in flight together) and
+// added in plane order.
+constexpr int kRedBatch = 8;
+
 __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
                                                 const float* __restrict__ tensor_scale,
                                                 void* __restrict__ y, int64_t mn, int splits,
@@ -422,14 +426,23 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if ((mn & 3) == 0) {
     const int64_t mn4 = mn >> 2;
+    const float4* p = reinterpret_cast<const float4*>(ws);
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn4; i += stride) {
-      float4 s = reinterpret_cast<const float4*>(ws)[i];
-      for (int sp = 1; sp < splits; ++sp) {
-        const float4 t = reinterpret_cast<const float4*>(ws + (int64_t)sp * mn)[i];
-        s.x += t.x;
-        s.y += t.y;
-        s.z += t.z;
-        s.w += t.w;
+      float4 s = p[i];
+      for (int sp = 1; sp < splits; sp += kRedBatch) {
+        float4 t[kRedBatch];
+#pragma unroll
+        for (int b = 0; b < kRedBatch; ++b)
+          if (sp + b < splits) t[b] = p[(int64_t)(sp + b) * mn4 + i];
+#pragma unroll
+        for (int b = 0; b < kRedBatch; ++b) {
+          if (sp + b < splits) {
+            s.x += t[b].x;
+            s.y += t[b].y;
+            s.z += t[b].z;
+            s.w += t[b].w;
+          }
+        }
       }
       store_out(y, 4 * i, s.x * s_t, out_f32);
       store_out(y, 4 * i + 1, s.y * s_t, out_f32);
@@ -440,7 +453,15 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
   }
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < mn; i += stride) {
     float s = ws[i];
-    for (int sp = 1; sp < splits; ++sp) s += ws[(int64_t)sp * mn + i];
+    for (int sp = 1; sp < splits; sp += kRedBatch) {
+      float t[kRedBatch];
+#pragma unroll
+      for (int b = 0; b < kRedBatch; ++b)
+        if (sp + b < splits) t[b] = ws[(int64_t)(sp + b) * mn + i];
+#pragma unroll
+      for (int b = 0; b < kRedBatch; ++b)
+        if (sp + b < splits) s += t[b];
+    }
     store_out(y, i, s * s_t, out_f32);
   }
 }

@@ -13,10 +13,12 @@
 //    wave holds here), 64 k per step, two LDS stages (the next step's weights
 //    are dequantized and its activations stored while the current step's
 //    MFMAs run, one barrier per step), loads two steps ahead.
-//    Configurations: 256 x 256 with 8 waves (each 64 x 128) when there are
-//    enough such tiles to fill the GPU, else 128 x 128 with 4 waves, whose K
-//    loop is split over several workgroups when there are few tiles (fp32
-//    partials, then a reduction kernel adds them in split order).
+//    Configurations: m <= 64: one 64-token tile x 256 weight rows (4 waves),
+//    or x 128 rows for long K; larger m: 256 x 256 with 8 waves (each
+//    64 x 128) when there are enough such tiles to fill the GPU, else
+//    128 x 128 with 4 waves.  With few tiles the K loop is split over
+//    workgroups (fp32 partials, then a reduction kernel adds them in split
+//    order).
 //  * k_tiled (any K): 128 x 128 x 64 tiles, 4 waves of 4 x 4
 //    v_mfma_f32_16x16x32_bf16, one LDS stage.
 #include "launchers.h"
@@ -385,11 +387,20 @@ template <int IMPL>
 hipError_t launch_lm_plan(const TiledPlan& p, const uint16_t* x, const uint8_t* codes,
                           const uint8_t* scales, const float* ts, void* y, float* ws, int M, int N,
                           int K, int out_f32, hipStream_t stream) {
-  if (p.kernel == 2)
-    return launch_lm<256, 256, 4, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
-                                           p.steps_per_split, out_f32, stream);
-  return launch_lm<128, 128, 2, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
-                                         p.steps_per_split, out_f32, stream);
+  switch (p.kernel) {
+    case 2:
+      return launch_lm<256, 256, 4, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
+                                             p.steps_per_split, out_f32, stream);
+    case 3:
+      return launch_lm<128, 64, 2, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
+                                            p.steps_per_split, out_f32, stream);
+    case 4:
+      return launch_lm<256, 64, 4, 1, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
+                                            p.steps_per_split, out_f32, stream);
+    default:
+      return launch_lm<128, 128, 2, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
+                                             p.steps_per_split, out_f32, stream);
+  }
 }
 
 }  // namespace
@@ -398,20 +409,28 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k, int forced_splits) {
   TiledPlan p{0, 1, 0, 0};
   if (k < 64 || k % 64 != 0) return p;  // single-stage kernel, no split
   const int64_t nsteps = k / 64;
-  const int64_t tiles256 = ((n + 255) / 256) * ((m + 255) / 256);
-  p.kernel = tiles256 >= 128 ? 2 : 1;
+  const int64_t cap = nsteps / 4 > 0 ? nsteps / 4 : 1;  // >= 4 steps per split
   int64_t splits = 1;
-  if (forced_splits > 0) {
-    splits = forced_splits;
-  } else if (p.kernel == 1) {
-    // few 128 x 128 tiles: split K until there are about two workgroups
-    // per CU, keeping at least 4 steps per split
-    const int64_t tiles = ((n + 127) / 128) * ((m + 127) / 128);
-    if (tiles < 512) splits = (512 + tiles - 1) / tiles;
-    const int64_t cap = nsteps / 4 > 0 ? nsteps / 4 : 1;
-    if (splits > cap) splits = cap;
-    if (splits > 16) splits = 16;
+  if (m <= 64) {
+    // one 64-token tile: 128 weight rows per workgroup for long K, else
+    // 256; K split to about 450 workgroups
+    p.kernel = nsteps >= 128 ? 3 : 4;
+    const int64_t bn = p.kernel == 3 ? 128 : 256;
+    const int64_t tiles = (n + bn - 1) / bn;
+    splits = (448 + tiles / 2) / tiles;
+  } else {
+    const int64_t tiles256 = ((n + 255) / 256) * ((m + 255) / 256);
+    p.kernel = tiles256 >= 128 ? 2 : 1;
+    if (p.kernel == 1) {
+      // few 128 x 128 tiles: split K until there are about two workgroups per CU
+      const int64_t tiles = ((n + 127) / 128) * ((m + 127) / 128);
+      if (tiles < 512) splits = (512 + tiles - 1) / tiles;
+    }
   }
+  if (splits > cap) splits = cap;
+  if (splits > 16) splits = 16;
+  if (splits < 1) splits = 1;
+  if (forced_splits > 0) splits = forced_splits;
   if (splits > nsteps) splits = nsteps;
   if (splits < 1) splits = 1;
   const int64_t per = (nsteps + splits - 1) / splits;

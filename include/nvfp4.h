@@ -179,11 +179,14 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *   m <= 16 -> memory-bound skinny kernel, one launch, a workgroup per 16
  *     weight rows over the whole K;
  *   16 < m <= 64 -> split-K skinny kernel with activations shared through
- *     LDS by 64 weight rows, plus a reduction kernel, when n * k <= 2^25
- *     or k % 64 != 0 or (m <= 32 and k <= 8192); else the tiled kernel;
- *   m > 64 -> the bf16-MFMA tiled kernel (256 x 256 or 128 x 128 tiles when
- *     k % 64 == 0, the latter with K split over workgroups when there are
- *     few tiles; 128 x 128 single-stage tiles for other k).
+ *     LDS by 64 weight rows, plus a reduction kernel, when k % 64 != 0 or
+ *     n * k <= 2^25; else the tiled kernel;
+ *   m > 64 -> the tiled kernel.
+ * The tiled kernel (bf16 MFMA): when k % 64 == 0, one 64-token tile x 256
+ * (or, for k >= 8192, 128) weight rows for m <= 64, else 256 x 256 or
+ * 128 x 128 tiles; K is split over workgroups (fp32 partials in the
+ * workspace, one reduction kernel) when there are few tiles.  Other k:
+ * 128 x 128 single-stage tiles.
  */
 NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,

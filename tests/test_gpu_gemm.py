@@ -161,10 +161,12 @@ def test_large_m_config_sampled_rows(layer):
         assert np.isfinite(y).all()
 
 
-# Large-M kernel configurations (K a multiple of 64): 256 x 256 tiles when
-# there are >= 128 of them, else 128 x 128; ragged M and N, odd N (scalar
-# stores), a single K step, and tiny M through the tiled path.
-LM_SHAPES = [(1000, 8000, 192), (300, 700, 256), (257, 4100, 64), (130, 1001, 128), (5, 333, 128)]
+# Two-stage tiled kernel configurations (K a multiple of 64): 256 x 256 tiles
+# when there are >= 128 of them, else 128 x 128; one 64-token tile with 256
+# (or, for K >= 8192, 128) weight rows for M <= 64, K split over workgroups;
+# ragged M and N, odd N (scalar stores), a single K step.
+LM_SHAPES = [(1000, 8000, 192), (300, 700, 256), (257, 4100, 64), (130, 1001, 128), (5, 333, 128),
+             (40, 300, 8192), (33, 520, 1024), (64, 1000, 512)]
 
 
 @pytest.mark.parametrize("impl", [nv.IMPL_PORTABLE, nv.IMPL_HWCVT])

@@ -100,16 +100,20 @@ def test_dispatch_and_workspace_plan(L):
     P = L.nvfp4_w4a16_gemm_path
     assert P(1, 4096, 4096) == S and P(16, 14336, 14336) == S
     assert P(48, 4096, 4096) == S and P(64, 4096, 4096) == S and P(65, 4096, 4096) == T
-    assert P(32, 14336, 4096) == S and P(33, 14336, 4096) == T and P(48, 14336, 4096) == T
+    assert P(17, 14336, 4096) == T and P(48, 14336, 4096) == T
     assert P(17, 4096, 14336) == T and P(32, 4096, 14336) == T
-    assert P(48, 14336, 4112) == S  # k % 64 != 0: single-stage tiled kernel only
+    assert P(48, 14336, 4112) == S and P(64, 4096, 4112) == S  # k % 64 != 0
     assert P(4096, 4096, 4096) == T
     assert L.nvfp4_w4a16_gemm_workspace_size(0, 4096, 4096) == 0
-    # tiled path: 128 x 128 tiles, K split until ~512 workgroups (>= 4 steps
-    # of 64 per split, at most 16 splits); 256 x 256 tiles are never split;
-    # K not a multiple of 64 takes the single-stage kernel, no split
+    # tiled path: m <= 64 one 64-token tile, K split to ~450 workgroups;
+    # larger m 128 x 128 tiles split until ~512 workgroups; 256 x 256 tiles
+    # never split; >= 4 steps of 64 per split, at most 16 splits; K not a
+    # multiple of 64 takes the single-stage kernel, no split
     T = nv.PATH_TILED
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(64, 4096, 4096, T, 0) == 16 * 4 * 64 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(48, 14336, 4096) == 8 * 4 * 48 * 14336
+    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 14336) == 14 * 4 * 48 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(128, 4096, 4096) == 16 * 4 * 128 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(4096, 4096, 4096) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size(1024, 14336, 4096) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size(1024, 4096, 4096) == 2 * 4 * 1024 * 4096
