@@ -5,11 +5,12 @@
 // section "1. Quantization and GEMM dispatch"); decode is bound by reading
 // the weights from HBM ("SOAR Weekly Champion Notes 08 ...", section "01").
 //
-// Two kernels:
-//  * k_skinny_fk (default for m <= 16): a workgroup owns 16 weight rows over
-//    the whole K and its waves split K; no workspace, one launch.  Loads of a
-//    group of K steps are in flight together and the next group is
+// Kernels:
+//  * k_skinny_fk (default for 2 < m <= 16): a workgroup owns 16 weight rows
+//    over the whole K and its waves split K; no workspace, one launch.  Loads
+//    of a group of K steps are in flight together and the next group is
 //    prefetched while the current one is consumed.
+//  * k_skinny_dot (m <= 2): the same layout with VALU dot products.
 //  * k_skinny + k_reduce (default for 16 < m <= 64, or any explicit
 //    split_k >= 1): 64 rows x one K chunk per workgroup with x staged in LDS
 //    in MFMA B-operand order (shared by the 4 waves), fp32 partials in the
@@ -250,6 +251,141 @@ __global__ __launch_bounds__(512) void k_skinny_fk(const uint16_t* __restrict__ 
     if (nbase + i < N) store_out(y, (int64_t)r16 * N + nbase + i, t[i] * s_t, out_f32);
 }
 
+// Full-K kernel for one or two tokens: VALU dot products instead of MFMAs
+// (an MFMA would use 1/16 or 2/16 of its B columns here).  Same workgroup
+// layout, loads and rounds as k_skinny_fk.  Each byte of codes becomes a
+// bf16 pair (exact E2M1 values; unit-scale hardware decode, or the portable
+// decode), v_dot2_f32_bf16 accumulates the products of one 16-weight block
+// in fp32, and the block sum is scaled by sigma once.  The four lane groups
+// of a row are added with two xor shuffles, the waves in wave order.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+
+template <int IMPL, int B>
+__device__ __forceinline__ bf16x2_t decode_pair_at(uint32_t d) {
+  if constexpr (IMPL == kConvHw) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, 1.0f, B);
+  } else {
+    const uint32_t lo = __float_as_uint(e2m1_val_portable((d >> (8 * B)) & 0xFu));
+    const uint32_t hi = __float_as_uint(e2m1_val_portable((d >> (8 * B + 4)) & 0xFu));
+    return __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(hi, lo, 0x07060302u));
+  }
+}
+
+// sum over the 8 codes of dword d (k = 8 consecutive) times the 8 bf16 of xq.
+// (Each element is copied to a scalar before the bit cast: clang's
+// __builtin_bit_cast of a vector-element expression reads element 0.)
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2_t, v); }
+
+template <int IMPL>
+__device__ __forceinline__ float dot8(uint32_t d, u32x4_t xq, float acc) {
+  const uint32_t q0 = xq[0], q1 = xq[1], q2 = xq[2], q3 = xq[3];
+  acc = __builtin_amdgcn_fdot2_f32_bf16(decode_pair_at<IMPL, 0>(d), as_bf16x2(q0), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(decode_pair_at<IMPL, 1>(d), as_bf16x2(q1), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(decode_pair_at<IMPL, 2>(d), as_bf16x2(q2), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(decode_pair_at<IMPL, 3>(d), as_bf16x2(q3), acc, false);
+  return acc;
+}
+
+template <int MR, int IMPL>
+__device__ __forceinline__ void compute_round_dot(const Round<MR>& R, uint16_t* xs, int M, int g,
+                                                  int lane, float (&acc)[MR]) {
+  const bool xok = (R.ok >> 8) & 1u;
+#pragma unroll
+  for (int m = 0; m < MR; ++m)
+    *reinterpret_cast<u32x4_t*>(xs + m * (kWaveK + 8) + 8 * lane) = zero_unless(xok && m < M, R.xv[m]);
+  const bool sok = (R.ok >> 9) & 1u;
+#pragma unroll
+  for (int s = 0; s < kSpw; ++s) {
+    const uint32_t s2 = sok ? (R.sw[s >> 1] >> (16 * (s & 1))) & 0xFFFFu : 0u;
+    const float sg0 = scale_value(s2 & 0xFFu), sg1 = scale_value(s2 >> 8);
+    const bool lo = (R.ok >> s) & 1u, hi = (R.ok >> (4 + s)) & 1u;
+    const uint32_t d0 = lo ? R.cw[s][0] : 0u, d1 = lo ? R.cw[s][1] : 0u;
+    const uint32_t d2 = hi ? R.cw[s][2] : 0u, d3 = hi ? R.cw[s][3] : 0u;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const uint16_t* xb = xs + m * (kWaveK + 8) + g * kQuarter + 32 * s;
+      const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(xb);
+      const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(xb + 8);
+      const u32x4_t x2 = *reinterpret_cast<const u32x4_t*>(xb + 16);
+      const u32x4_t x3 = *reinterpret_cast<const u32x4_t*>(xb + 24);
+      const float b0 = dot8<IMPL>(d1, x1, dot8<IMPL>(d0, x0, 0.0f));  // block 2s of the quarter
+      const float b1 = dot8<IMPL>(d3, x3, dot8<IMPL>(d2, x2, 0.0f));  // block 2s + 1
+      acc[m] += sg0 * b0;
+      acc[m] += sg1 * b1;
+    }
+  }
+}
+
+// ONE: K fits in one round (no second register buffer: fewer VGPRs, more
+// workgroups per CU).
+template <int MR, int IMPL, bool K32, bool K128, bool ONE>
+__global__ __launch_bounds__(512) void k_skinny_dot(const uint16_t* __restrict__ x,
+                                                    const uint8_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ scales,
+                                                    const float* __restrict__ tensor_scale,
+                                                    void* __restrict__ y, int M, int N, int K,
+                                                    int rounds, int out_f32) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+  // LDS: [W][MR][16] f32 partial sums, then [W][MR][kWaveK + 8] bf16 activations
+  float* red = reinterpret_cast<float*>(lds);
+  uint16_t* xs = reinterpret_cast<uint16_t*>(lds + nwaves * 64 * sizeof(f32x4_t)) +
+                 wave * MR * (kWaveK + 8);
+
+  const int row = blockIdx.x * 16 + r16;
+  const bool row_ok = row < N;
+  const int rowc = min(row, N - 1);
+  const uint8_t* crow = codes + (int64_t)rowc * (K / 2);
+  const uint8_t* srow = scales + (int64_t)rowc * (K / 16);
+  const int round_k = nwaves * kWaveK;
+  const int kw = wave * kWaveK;
+
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+  if constexpr (ONE) {
+    Round<MR> RA;
+    load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, kw, kw + g * kQuarter, lane);
+    compute_round_dot<MR, IMPL>(RA, xs, M, g, lane, acc);
+  } else {
+    Round<MR> RA, RB;
+    load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, kw, kw + g * kQuarter, lane);
+    for (int r = 0; r < rounds; r += 2) {
+      const int k1 = (r + 1) * round_k + kw;
+      if (r + 1 < rounds) load_round<MR, K32, K128>(RB, crow, srow, row_ok, x, M, K, k1, k1 + g * kQuarter, lane);
+      compute_round_dot<MR, IMPL>(RA, xs, M, g, lane, acc);
+      if (r + 1 >= rounds) break;
+      const int k2 = (r + 2) * round_k + kw;
+      if (r + 2 < rounds) load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, k2, k2 + g * kQuarter, lane);
+      compute_round_dot<MR, IMPL>(RB, xs, M, g, lane, acc);
+    }
+  }
+  // lane groups g = 0..3 of a row: ((g0 + g1) + (g2 + g3)) in every lane
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    acc[m] += __shfl_xor(acc[m], 16, 64);
+    acc[m] += __shfl_xor(acc[m], 32, 64);
+  }
+  if (g == 0) {
+#pragma unroll
+    for (int m = 0; m < MR; ++m) red[(wave * MR + m) * 16 + r16] = acc[m];
+  }
+  __syncthreads();
+  if (wave != 0 || g != 0 || !row_ok) return;
+  const float s_t = tensor_scale[0];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    if (m >= M) continue;
+    float t = red[m * 16 + r16];
+    for (int w = 1; w < nwaves; ++w) t += red[(w * MR + m) * 16 + r16];
+    store_out(y, (int64_t)m * N + row, t * s_t, out_f32);
+  }
+}
+
 // Split-K kernel: 64 rows x one K chunk per workgroup, fp32 partials to the
 // workspace when there is more than one chunk (then k_reduce).
 template <int MT, int IMPL, bool K32>
@@ -473,6 +609,31 @@ hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
   const dim3 grid((unsigned)((N + 15) / 16));
   const size_t lds = (size_t)p.waves * (64 * sizeof(f32x4_t) + (size_t)MR * (kWaveK + 8) * 2);
   const int rounds = (K + p.waves * kWaveK - 1) / (p.waves * kWaveK);
+  if constexpr (MR <= 2) {  // one or two tokens: VALU dot products
+    const dim3 block(64 * p.waves);
+    // The one-round kernel needs fewer VGPRs, so more workgroups fit per
+    // CU; that pays when there are more workgroups than MI355X's 256 CUs
+    // (measured: 14336 x 4096 at m = 1: 10.8 us against 12.8 us); with one
+    // workgroup per CU the two-buffer build is faster (4096 x 4096: 4.8 us
+    // against 5.1 us).
+    const bool one = rounds == 1 && grid.x > 256;
+    if (K % 128 == 0) {
+      if (one)
+        hipLaunchKernelGGL((k_skinny_dot<MR, IMPL, K32, true, true>), grid, block, lds, stream, x,
+                           codes, scales, ts, y, M, N, K, rounds, out_f32);
+      else
+        hipLaunchKernelGGL((k_skinny_dot<MR, IMPL, K32, true, false>), grid, block, lds, stream, x,
+                           codes, scales, ts, y, M, N, K, rounds, out_f32);
+    } else {
+      if (one)
+        hipLaunchKernelGGL((k_skinny_dot<MR, IMPL, K32, false, true>), grid, block, lds, stream, x,
+                           codes, scales, ts, y, M, N, K, rounds, out_f32);
+      else
+        hipLaunchKernelGGL((k_skinny_dot<MR, IMPL, K32, false, false>), grid, block, lds, stream, x,
+                           codes, scales, ts, y, M, N, K, rounds, out_f32);
+    }
+    return hipGetLastError();
+  }
   if (K % 128 == 0) {
     auto fn = k_skinny_fk<MR, IMPL, K32, true>;
     hipError_t e = set_lds_limit<k_skinny_fk<MR, IMPL, K32, true>>(lds);

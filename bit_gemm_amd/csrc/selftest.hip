@@ -75,6 +75,21 @@ __global__ __launch_bounds__(256) void k_decode(uint32_t* counters) {
   count(&counters[1], bad1);
   count(&counters[2], bad2);
   count(&counters[3], bad3);
+  // [5] unit-scale decode straight to bf16 pairs from each byte position
+  uint32_t bad5 = 0u;
+  if (scode == 0) {
+    const uint32_t other = (byte ^ 0xA5u) * 0x01010101u;
+    const uint32_t want = pack_bf16_exact(lo, hi);
+#define DEC16_AT(J)                                                                       \
+  {                                                                                       \
+    const uint32_t wj = (other & ~(0xFFu << (8 * J))) | (byte << (8 * J));               \
+    const bf16x2_t h = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(wj, 1.0f, J);            \
+    bad5 += (__builtin_bit_cast(uint32_t, h) != want) ? 1u : 0u;                          \
+  }
+    DEC16_AT(0) DEC16_AT(1) DEC16_AT(2) DEC16_AT(3)
+#undef DEC16_AT
+  }
+  count(&counters[5], bad5);
 }
 
 __global__ void k_zero8(uint32_t* c) {

@@ -227,7 +227,9 @@ NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);
  *  [2] FP4 byte -> 2 x fp32 with scale sigma, against fl32(val * sigma),
  *      for every E4M3 sigma in [0, 448],
  *  [3] FP4 byte -> 2 x bf16 with scale sigma, against val * sigma,
- *  [4] number of fp32 values tested in [0], [5..7] reserved (0).
+ *  [4] number of fp32 values tested in [0],
+ *  [5] FP4 byte -> 2 x bf16 decode at unit scale (256 bytes, from each of
+ *      the four byte positions), [6..7] reserved (0).
  * Used by the tests to decide whether NVFP4_IMPL_HWCVT is exact.
  */
 NVFP4_API int nvfp4_selftest_cvt(uint32_t* counters_out, void* stream);

@@ -47,6 +47,9 @@ SHAPES = [
     # (m, n, k): tails in every dimension, K % 32 == 16, one K step, many splits
     (1, 64, 256), (3, 17, 48), (16, 100, 160), (17, 200, 4096), (33, 129, 528),
     (48, 512, 4096), (64, 130, 272), (5, 300, 14336), (2, 1, 16), (1, 4096, 4096),
+    # m <= 2 (VALU dot products): more 16-row workgroups than CUs, K in one
+    # round, with and without k % 128 == 0
+    (2, 5000, 1040), (1, 4200, 4096),
 ]
 
 
