@@ -191,8 +191,9 @@ __device__ __forceinline__ void compute_round(const Round<MR>& R, uint16_t* xs, 
   }
 }
 
-// MR = token rows staged per wave (M <= MR <= 16).
-template <int MR, int IMPL, bool K32, bool K128>
+// MR = token rows staged per wave (M <= MR <= 16).  ONE: K fits in one
+// round (no second register buffer: fewer VGPRs, more workgroups per CU).
+template <int MR, int IMPL, bool K32, bool K128, bool ONE>
 __global__ __launch_bounds__(512) void k_skinny_fk(const uint16_t* __restrict__ x,
                                                    const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ scales,
@@ -219,16 +220,22 @@ __global__ __launch_bounds__(512) void k_skinny_fk(const uint16_t* __restrict__ 
   const int kw = wave * kWaveK;
 
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  Round<MR> RA, RB;
-  load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, kw, kw + g * kQuarter, lane);
-  for (int r = 0; r < rounds; r += 2) {
-    const int k1 = (r + 1) * round_k + kw;
-    if (r + 1 < rounds) load_round<MR, K32, K128>(RB, crow, srow, row_ok, x, M, K, k1, k1 + g * kQuarter, lane);
+  if constexpr (ONE) {
+    Round<MR> RA;
+    load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, kw, kw + g * kQuarter, lane);
     compute_round<MR, IMPL>(RA, xs, M, g, r16, lane, acc);
-    if (r + 1 >= rounds) break;
-    const int k2 = (r + 2) * round_k + kw;
-    if (r + 2 < rounds) load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, k2, k2 + g * kQuarter, lane);
-    compute_round<MR, IMPL>(RB, xs, M, g, r16, lane, acc);
+  } else {
+    Round<MR> RA, RB;
+    load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, kw, kw + g * kQuarter, lane);
+    for (int r = 0; r < rounds; r += 2) {
+      const int k1 = (r + 1) * round_k + kw;
+      if (r + 1 < rounds) load_round<MR, K32, K128>(RB, crow, srow, row_ok, x, M, K, k1, k1 + g * kQuarter, lane);
+      compute_round<MR, IMPL>(RA, xs, M, g, r16, lane, acc);
+      if (r + 1 >= rounds) break;
+      const int k2 = (r + 2) * round_k + kw;
+      if (r + 2 < rounds) load_round<MR, K32, K128>(RA, crow, srow, row_ok, x, M, K, k2, k2 + g * kQuarter, lane);
+      compute_round<MR, IMPL>(RB, xs, M, g, r16, lane, acc);
+    }
   }
 
   // cross-wave sum in wave order; lane holds D[n = 4g + i][m = r16]
@@ -602,6 +609,18 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
   }
 }
 
+template <auto Kernel>
+hipError_t launch_fk_kernel(dim3 grid, int waves, size_t lds, hipStream_t stream,
+                            const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
+                            const float* ts, void* y, int M, int N, int K, int rounds,
+                            int out_f32) {
+  hipError_t e = set_lds_limit<Kernel>(lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(Kernel, grid, dim3(64 * waves), lds, stream, x, codes, scales, ts, y, M, N, K,
+                     rounds, out_f32);
+  return hipGetLastError();
+}
+
 template <int MR, int IMPL, bool K32>
 hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
                      const uint8_t* codes, const uint8_t* scales, const float* ts, void* y, int M,
@@ -609,14 +628,14 @@ hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
   const dim3 grid((unsigned)((N + 15) / 16));
   const size_t lds = (size_t)p.waves * (64 * sizeof(f32x4_t) + (size_t)MR * (kWaveK + 8) * 2);
   const int rounds = (K + p.waves * kWaveK - 1) / (p.waves * kWaveK);
+  // The one-round kernels need fewer VGPRs, so more workgroups fit per CU;
+  // that pays when there are more workgroups than MI355X's 256 CUs
+  // (measured: 14336 x 4096 at m = 1: 10.8 us against 12.8 us); with one
+  // workgroup per CU the two-buffer build is faster (4096 x 4096: 4.8 us
+  // against 5.1 us).
+  const bool one = rounds == 1 && grid.x > 256;
   if constexpr (MR <= 2) {  // one or two tokens: VALU dot products
     const dim3 block(64 * p.waves);
-    // The one-round kernel needs fewer VGPRs, so more workgroups fit per
-    // CU; that pays when there are more workgroups than MI355X's 256 CUs
-    // (measured: 14336 x 4096 at m = 1: 10.8 us against 12.8 us); with one
-    // workgroup per CU the two-buffer build is faster (4096 x 4096: 4.8 us
-    // against 5.1 us).
-    const bool one = rounds == 1 && grid.x > 256;
     if (K % 128 == 0) {
       if (one)
         hipLaunchKernelGGL((k_skinny_dot<MR, IMPL, K32, true, true>), grid, block, lds, stream, x,
@@ -635,19 +654,11 @@ hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
     return hipGetLastError();
   }
   if (K % 128 == 0) {
-    auto fn = k_skinny_fk<MR, IMPL, K32, true>;
-    hipError_t e = set_lds_limit<k_skinny_fk<MR, IMPL, K32, true>>(lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, grid, dim3(64 * p.waves), lds, stream, x, codes, scales, ts, y, M, N, K,
-                       rounds, out_f32);
-  } else {
-    auto fn = k_skinny_fk<MR, IMPL, K32, false>;
-    hipError_t e = set_lds_limit<k_skinny_fk<MR, IMPL, K32, false>>(lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fn, grid, dim3(64 * p.waves), lds, stream, x, codes, scales, ts, y, M, N, K,
-                       rounds, out_f32);
+    if (one) return launch_fk_kernel<k_skinny_fk<MR, IMPL, K32, true, true>>(grid, p.waves, lds, stream, x, codes, scales, ts, y, M, N, K, rounds, out_f32);
+    return launch_fk_kernel<k_skinny_fk<MR, IMPL, K32, true, false>>(grid, p.waves, lds, stream, x, codes, scales, ts, y, M, N, K, rounds, out_f32);
   }
-  return hipGetLastError();
+  if (one) return launch_fk_kernel<k_skinny_fk<MR, IMPL, K32, false, true>>(grid, p.waves, lds, stream, x, codes, scales, ts, y, M, N, K, rounds, out_f32);
+  return launch_fk_kernel<k_skinny_fk<MR, IMPL, K32, false, false>>(grid, p.waves, lds, stream, x, codes, scales, ts, y, M, N, K, rounds, out_f32);
 }
 
 template <int MT, int IMPL, bool K32>
