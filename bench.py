@@ -321,6 +321,7 @@ def main(argv=None):
 
     if not args.no_shapes:
         result["decoder_shapes"] = decoder_shapes(args, stream, time_op, src[0])
+        result["decoder_model_32_layers"] = decoder_model(args, stream, src[0])
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(args, w_host, xs, packed(1), step_bytes)
@@ -393,6 +394,92 @@ def decoder_shapes(args, stream, time_op, w_dev):
         out["large_m"][f"{name}_n{n}_k{k}"] = res
         del qs, ws
         torch.cuda.empty_cache()
+    return out
+
+
+def decoder_model(args, stream, w_dev):
+    """The full synthetic 32-layer decoder (hidden 4096, MLP width 14336;
+    per layer q, k, v, o 4096 x 4096, gate and up n = 14336, k = 4096, down
+    n = 4096, k = 14336): one FourOverSix quantization pass over all 224
+    fp32 matrices (31.1 GB, amax pass + quantizer per matrix), and one
+    sequential pass of the 224 W4A16 GEMMs at M = 1 and at M = 48 over the
+    4.38 GB of packed weights, each pass replayed from one HIP graph.  The
+    fp32 weights are the single layer's Student-t matrix tiled to each
+    shape (timing does not depend on the values)."""
+    import torch
+
+    import bit_gemm_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    layers = 32
+    shapes = [(name, n, k) for name, n, k in synth.decoder_layer_shapes()]
+    # fp32 model: one flat buffer, a view per matrix
+    sizes = [n * k for _, n, k in shapes] * layers
+    total = sum(sizes)
+    flat = torch.empty(total, dtype=torch.float32, device=dev)
+    views, off = [], 0
+    for li in range(layers):
+        for _, n, k in shapes:
+            v = flat[off:off + n * k].view(n, k)
+            v.copy_(w_dev.repeat((n + N - 1) // N, (k + K - 1) // K)[:n, :k])
+            views.append(v)
+            off += n * k
+    packed = [nv.NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                             torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+                             torch.empty(1, dtype=torch.float32, device=dev),
+                             torch.empty(1, dtype=torch.float32, device=dev),
+                             torch.empty((n, k // 16), dtype=torch.uint8, device=dev))
+              for _ in range(layers) for _, n, k in shapes]
+    torch.cuda.synchronize()
+
+    def replay_time(fn, reps=3):
+        with torch.cuda.stream(stream):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps
+
+    def quant_pass():
+        for v, q in zip(views, packed):
+            nv.quantize_fos(v, out=q)
+
+    tq = replay_time(quant_pass)
+    wsum = float(total)
+    out = {"layers": layers, "weights": int(total), "fp32_bytes": int(4 * total),
+           "packed_bytes": int(sum(bytes_gemm_weights(n, k) for _, n, k in shapes) * layers),
+           "quantize_pass_ms": round(tq * 1e3, 3),
+           "quantize_weights_per_s": round(wsum / tq, 1),
+           "quantize_gbs_with_amax_pass": round(wsum * (4 + 4.625) / tq / 1e9, 1),
+           "quantize_gbs_single_read": round(wsum * 4.625 / tq / 1e9, 1)}
+    del flat, views
+    torch.cuda.empty_cache()
+    for m in (1, 48):
+        xs = {k: synth.activations(m, k, synth.activation_seed(m)).to(dev) for k in {k for _, _, k in shapes}}
+        ys = {n: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for n in {n for _, n, _ in shapes}}
+        ws = torch.empty(max(16, max(nv.workspace_size(m, n, k) for _, n, k in shapes)), dtype=torch.uint8,
+                         device=dev)
+
+        def gemm_pass():
+            for q in packed:
+                n, k = q.codes.shape[0], q.codes.shape[1] * 2
+                nv.w4a16_gemm(xs[k], q, out=ys[n], workspace=ws)
+
+        tg = replay_time(gemm_pass)
+        gbs = out["packed_bytes"] / tg / 1e9
+        out[f"gemm_pass_m{m}"] = {"us": round(tg * 1e6, 1), "weight_gbs": round(gbs, 1),
+                                  "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                  "us_per_layer": round(tg * 1e6 / layers, 2)}
+    del packed
+    torch.cuda.empty_cache()
     return out
 
 
