@@ -12,7 +12,7 @@
 //    with few independent accumulators; the 16x16x32 shape needs more than a
 //    wave holds here), 64 k per step, two LDS stages (the next step's weights
 //    are dequantized and its activations stored while the current step's
-//    MFMAs run, one barrier per step), loads two steps ahead.
+//    MFMAs run, one barrier per step), global loads two steps ahead.
 //    Configurations: m <= 64: one 64-token tile x 256 weight rows (4 waves),
 //    or x 128 rows for long K; larger m: 256 x 256 with 8 waves (each
 //    64 x 128) when there are enough such tiles to fill the GPU, else
@@ -220,19 +220,22 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
   const int wn = wave / WGM, wm = wave % WGM;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
 
-  u32x4_t cv[WA];
-  uint32_t sv[WA];
-  u32x4_t xv[WB][4];
-  auto load_step = [&](int k0) {
+  // one step of loader data in registers (codes, scales, activations)
+  struct Regs {
+    u32x4_t cv[WA];
+    uint32_t sv[WA];
+    u32x4_t xv[WB][4];
+  };
+  auto load_step = [&](Regs& R, int k0) {
 #pragma unroll
     for (int i = 0; i < WA; ++i) {
       const int tile = WA * wave + i;
       if (tile >= NT) break;
       const int row = n0 + 32 * tile + r32;
       const int rowc = min(row, N - 1);
-      cv[i] = *reinterpret_cast<const u32x4_t*>(codes + (int64_t)rowc * (K / 2) + k0 / 2 + 16 * h);
+      R.cv[i] = *reinterpret_cast<const u32x4_t*>(codes + (int64_t)rowc * (K / 2) + k0 / 2 + 16 * h);
       const uint32_t s2 = *reinterpret_cast<const uint16_t*>(scales + (int64_t)rowc * (K / 16) + k0 / 16 + 2 * h);
-      sv[i] = row < N ? s2 : 0u;  // sigma 0: rows past N contribute zeros
+      R.sv[i] = row < N ? s2 : 0u;  // sigma 0: rows past N contribute zeros
     }
 #pragma unroll
     for (int j = 0; j < WB; ++j) {
@@ -242,20 +245,20 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
       const int m = min(m0 + 32 * tile + r32, M - 1);
       const uint16_t* xp = x + (int64_t)m * K + k0 + 32 * h;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) xv[j][q] = *reinterpret_cast<const u32x4_t*>(xp + 8 * q);
+      for (int q = 0; q < 4; ++q) R.xv[j][q] = *reinterpret_cast<const u32x4_t*>(xp + 8 * q);
     }
   };
-  auto store_step = [&](uint8_t* st) {
+  auto store_step = [&](const Regs& R, uint8_t* st) {
     uint8_t* sA = st;
     uint8_t* sB = st + A_BYTES;
 #pragma unroll
     for (int i = 0; i < WA; ++i) {
       const int tile = WA * wave + i;
       if (tile >= NT) break;
-      const float sg0 = scale_value(sv[i] & 0xFFu), sg1 = scale_value((sv[i] >> 8) & 0xFFu);
+      const float sg0 = scale_value(R.sv[i] & 0xFFu), sg1 = scale_value((R.sv[i] >> 8) & 0xFFu);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const uint4 o = dequant8u<IMPL>(cv[i][ks], ks < 2 ? sg0 : sg1);
+        const uint4 o = dequant8u<IMPL>(R.cv[i][ks], ks < 2 ? sg0 : sg1);
         *reinterpret_cast<uint4*>(sA + ((ks * NT + tile) * 64 + lane) * 16) = o;
       }
     }
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
       if (tile >= MT) break;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        *reinterpret_cast<u32x4_t*>(sB + ((ks * MT + tile) * 64 + lane) * 16) = xv[j][ks];
+        *reinterpret_cast<u32x4_t*>(sB + ((ks * MT + tile) * 64 + lane) * 16) = R.xv[j][ks];
     }
   };
 
@@ -280,10 +283,12 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
   const int s0 = blockIdx.z * steps_per;
   const int nsteps = min(K / 64 - s0, steps_per);  // >= 1 (the plan has no empty split)
   const int kbase = s0 * 64;
-  load_step(kbase);
-  store_step(lds);
-  if (nsteps > 1) load_step(kbase + 64);
-  for (int s = 0; s < nsteps; ++s) {
+
+  // One step: MFMAs on LDS stage s % 2 while stage (s + 1) % 2 is filled
+  // from R (step s + 1) and R is reloaded with step s + 2.  (Two register
+  // sets, loads three steps ahead, measured slower: the extra VGPRs cost
+  // more occupancy than the longer prefetch gains.)
+  auto iter = [&](int s, Regs& R) {
     __syncthreads();  // stage s % 2 complete; nobody reads stage (s + 1) % 2 any more
     const uint8_t* sA = lds + (s & 1) * STAGE;
     const uint8_t* sB = sA + A_BYTES;
@@ -295,8 +300,8 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
     for (int j = 0; j < WMT; ++j)
       bfr[0][j] = *reinterpret_cast<const bf16x8_t*>(sB + ((WMT * wm + j) * 64 + lane) * 16);
     if (s + 1 < nsteps) {
-      store_step(lds + ((s + 1) & 1) * STAGE);
-      if (s + 2 < nsteps) load_step(kbase + (s + 2) * 64);
+      store_step(R, lds + ((s + 1) & 1) * STAGE);
+      if (s + 2 < nsteps) load_step(R, kbase + (s + 2) * 64);
     }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -315,7 +320,13 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
         for (int b = 0; b < WMT; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[c][a], bfr[c][b], acc[a][b], 0, 0, 0);
     }
-  }
+  };
+
+  Regs R;
+  load_step(R, kbase);
+  store_step(R, lds);
+  if (nsteps > 1) load_step(R, kbase + 64);
+  for (int s = 0; s < nsteps; ++s) iter(s, R);  // stores step s + 1, loads step s + 2
 
   // D of a 32 x 32 tile: lane l, value v -> weight row 8 (v / 4) + 4 (l / 32)
   // + v % 4, token l % 32.  With a K split: raw fp32 partials to plane z.
