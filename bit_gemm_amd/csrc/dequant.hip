@@ -10,11 +10,6 @@
 namespace nvfp4 {
 namespace {
 
-__device__ __forceinline__ float scale_value(uint32_t s) {
-  const float v = e4m3_decode(s & 0x7Fu);
-  return (s & 0x80u) ? -v : v;
-}
-
 // One thread per 16 output bytes: 8 elements (bf16 output, half a block) or
 // 4 elements (fp32 output, a quarter block), so the stores of a wave cover
 // 1 KiB contiguously.  FP4 codes are decoded by the gfx950 conversion with
@@ -29,7 +24,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
   const float s_t = tensor_scale[0];
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nthreads; t += stride) {
-    const float sigma = scale_value(scales[t * E / 16]);
+    const float sigma = scale_at<kConvHw, 0>(scales[t * E / 16]);
     float v[E];
     if constexpr (F32) {
       const uint32_t c = reinterpret_cast<const uint16_t*>(codes)[t];

@@ -57,11 +57,6 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sigma) {
   return __builtin_bit_cast(bf16x8_t, o);
 }
 
-__device__ __forceinline__ float scale_value(uint32_t s) {
-  const float v = e4m3_decode(s & 0x7Fu);
-  return (s & 0x80u) ? -v : v;
-}
-
 __device__ __forceinline__ void store_out(void* y, int64_t idx, float v, int out_f32) {
   if (out_f32)
     reinterpret_cast<float*>(y)[idx] = v;
@@ -175,7 +170,7 @@ __device__ __forceinline__ void compute_round(const Round<MR>& R, uint16_t* xs, 
 #pragma unroll
   for (int s = 0; s < kSpw; ++s) {
     const uint32_t s2 = sok ? (R.sw[s >> 1] >> (16 * (s & 1))) & 0xFFFFu : 0u;
-    const float sg0 = scale_value(s2 & 0xFFu), sg1 = scale_value(s2 >> 8);
+    const float sg0 = scale_at<IMPL, 0>(s2), sg1 = scale_at<IMPL, 1>(s2);
     const bool lo = (R.ok >> s) & 1u, hi = (R.ok >> (4 + s)) & 1u;
     bf16x8_t a[4];
     a[0] = dequant8<IMPL>(lo ? R.cw[s][0] : 0u, sg0);
@@ -304,7 +299,7 @@ __device__ __forceinline__ void compute_round_dot(const Round<MR>& R, uint16_t* 
 #pragma unroll
   for (int s = 0; s < kSpw; ++s) {
     const uint32_t s2 = sok ? (R.sw[s >> 1] >> (16 * (s & 1))) & 0xFFFFu : 0u;
-    const float sg0 = scale_value(s2 & 0xFFu), sg1 = scale_value(s2 >> 8);
+    const float sg0 = scale_at<IMPL, 0>(s2), sg1 = scale_at<IMPL, 1>(s2);
     const bool lo = (R.ok >> s) & 1u, hi = (R.ok >> (4 + s)) & 1u;
     const uint32_t d0 = lo ? R.cw[s][0] : 0u, d1 = lo ? R.cw[s][1] : 0u;
     const uint32_t d2 = hi ? R.cw[s][2] : 0u, d3 = hi ? R.cw[s][3] : 0u;
@@ -505,7 +500,7 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
 #pragma unroll
   for (int ks = 0; ks < kMaxSteps; ++ks) {
     if (ks < nks) {
-      const float sg0 = scale_value(sb[ks] & 0xFFu), sg1 = scale_value((sb[ks] >> 8) & 0xFFu);
+      const float sg0 = scale_at<IMPL, 0>(sb[ks]), sg1 = scale_at<IMPL, 1>(sb[ks]);
       bf16x8_t a[4];
       a[0] = dequant8<IMPL>(cw[ks][0], sg0);
       a[1] = dequant8<IMPL>(cw[ks][1], sg0);
@@ -546,6 +541,178 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
     if (m >= M) continue;
     float* dst = ws + blockIdx.y * mn + (int64_t)m * N + nbase;
     if ((N & 3) == 0 && nbase + 3 < N) {  // 16-byte aligned: nbase and N are multiples of 4
+      *reinterpret_cast<float4*>(dst) = float4{acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]};
+      continue;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (nbase + i < N) dst[i] = acc[mt][i];
+  }
+}
+
+// Loads whose completion the kernel waits for itself.  The compiler's own
+// wait insertion counts LDS DMA copies as a different kind of vector-memory
+// event from plain loads, and with both kinds in flight it can only wait for
+// everything (vmcnt(0)); loads written as inline asm are invisible to it, and
+// wait_vm below (which takes the loaded registers as operands, so nothing
+// that reads them can move above it) waits for exactly as many as needed.
+// (The asm bodies are compiled for the device only: the host pass of a HIP
+// source also reads device functions and has no VGPR constraint.)
+template <int OFF>
+__device__ __forceinline__ void load_b128_async(u32x4_t& d, const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(d) : "v"(p), "i"(OFF) : "memory");
+#endif
+}
+template <int OFF>
+__device__ __forceinline__ void load_u16_async(uint32_t& d, const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_ushort %0, %1, off offset:%2" : "=v"(d) : "v"(p), "i"(OFF) : "memory");
+#endif
+}
+// Wait until at most V vector-memory operations of this wave are
+// outstanding (loads return in issue order); V is capped at 63, the
+// counter's limit, which only waits longer.
+template <int V>
+__device__ __forceinline__ void wait_vm(u32x4_t& c, uint32_t& sbv) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(c), "+v"(sbv) : "n"(V > 63 ? 63 : V) : "memory");
+#endif
+}
+
+// LDS DMA of 16 bytes per lane: lane l's bytes land at dst + 16 l (dst is
+// wave-uniform).
+__device__ __forceinline__ void copy16_to_lds(const uint16_t* src, uint8_t* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+#endif
+}
+
+// Per-lane state of k_skinny_pipe, shared by its compile-time step loops.
+template <int MT, int NKS>
+struct PipeState {
+  u32x4_t cw[NKS];           // codes of step s: 32 codes of row r16 at k = 32 g
+  uint32_t sb[NKS];          // the two scale bytes of those codes
+  const uint8_t* crow;       // codes of this lane's row and quarter, chunk start
+  const uint8_t* srow;       // scales, same
+  const uint16_t* xsrc[MT];  // x pieces this lane copies, chunk start
+  f32x4_t acc[MT];
+};
+
+constexpr int pipe_ops_per_step(int mt) { return 2 + mt; }  // codes, scales, MT x copies
+
+// Issue the loads of steps S .. NKS-1, in step order.
+template <int S, int MT, int NKS>
+__device__ __forceinline__ void pipe_issue(PipeState<MT, NKS>& P, uint8_t* lds, int wave) {
+  load_b128_async<S * (kStepK / 2)>(P.cw[S], P.crow);
+  load_u16_async<S * (kStepK / 16)>(P.sb[S], P.srow);
+#pragma unroll
+  for (int i = 0; i < MT; ++i) copy16_to_lds(P.xsrc[i] + S * kStepK, lds + 1024 * (S * 4 * MT + wave + 4 * i));
+  asm volatile("" ::: "memory");
+  if constexpr (S + 1 < NKS) pipe_issue<S + 1, MT, NKS>(P, lds, wave);
+}
+
+// Compute steps S .. NKS-1, each once its own loads have landed.
+template <int S, int MT, int IMPL, int NKS>
+__device__ __forceinline__ void pipe_compute(PipeState<MT, NKS>& P, const uint8_t* lds, int g,
+                                             int r16) {
+  wait_vm<(NKS - 1 - S) * pipe_ops_per_step(MT)>(P.cw[S], P.sb[S]);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+  const float sg0 = scale_at<IMPL, 0>(P.sb[S]), sg1 = scale_at<IMPL, 1>(P.sb[S]);
+  bf16x8_t a[4];
+  a[0] = dequant8<IMPL>(P.cw[S][0], sg0);
+  a[1] = dequant8<IMPL>(P.cw[S][1], sg0);
+  a[2] = dequant8<IMPL>(P.cw[S][2], sg1);
+  a[3] = dequant8<IMPL>(P.cw[S][3], sg1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      // token row 16 mt + r16, 16-byte piece 4 g + j, swizzled by r16
+      const int off = S * 4096 * MT + 256 * (16 * mt + r16) + 16 * ((4 * g + j) ^ r16);
+      const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(lds + off);
+      P.acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, bv),
+                                                          P.acc[mt], 0, 0, 0);
+    }
+  }
+  if constexpr (S + 1 < NKS) pipe_compute<S + 1, MT, IMPL, NKS>(P, lds, g, r16);
+}
+
+// Pipelined split-K kernel (16 < m <= 64, K a multiple of 128): the tile of
+// k_skinny (64 weight rows x one K chunk; x staged in LDS in B-operand
+// order by the LDS DMA and shared by the 4 waves), but each K step's loads
+// (codes, scales, then the step's x pieces) are issued together in step
+// order, and step s is computed as soon as its own loads have landed: a
+// vmcnt wait that allows exactly the loads issued after step s to be
+// outstanding (loads return in issue order), then a bare s_barrier (no
+// fence: a workgroup fence would wait for every LDS DMA in flight) so that
+// the x pieces copied by the other waves are there too.  The loop over the
+// NKS steps is unrolled at compile time and every chunk is exactly NKS
+// steps (K a multiple of NKS * 128): no step is conditional, so the
+// compiler cannot sink a step's loads into its compute.
+template <int MT, int IMPL, int NKS>
+__global__ __launch_bounds__(256) void k_skinny_pipe(const uint16_t* __restrict__ x,
+                                                     const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales,
+                                                     const float* __restrict__ tensor_scale,
+                                                     void* __restrict__ y, float* __restrict__ ws,
+                                                     int M, int N, int K, int out_f32) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int g = lane >> 4;
+  const int r16 = lane & 15;
+
+  const int k0 = blockIdx.y * (NKS * kStepK);
+
+  PipeState<MT, NKS> P;
+  // rows past N read row N-1 (real data, finite); their outputs are dropped
+  const int row = blockIdx.x * kRowsPerWg + wave * 16 + r16;
+  const int rowc = min(row, N - 1);
+  P.crow = codes + (int64_t)rowc * (K / 2) + k0 / 2 + 16 * g;
+  P.srow = scales + (int64_t)rowc * (K / 16) + k0 / 16 + 2 * g;
+  // x of one step: 16 MT token rows x 256 bytes, copied by 4 MT LDS DMA
+  // instructions (wave w issues c = w + 4 i), each reading whole cache
+  // lines: 4 rows x 256 contiguous bytes, lane l -> row 4 c + l / 16 and
+  // 16-byte piece q = (l % 16) ^ (row % 16).  The step lands row-major
+  // (256-byte rows) with piece q of row r at slot q ^ (r % 16), so the B
+  // fragment reads (16 rows, the same piece) hit 16 different bank groups.
+  // Rows >= M repeat row M-1 (finite data): a B column only feeds the
+  // output column of its own token, and those outputs are not stored.
+#pragma unroll
+  for (int i = 0; i < MT; ++i) {
+    const int rr = 4 * (wave + 4 * i) + (lane >> 4);
+    const int m = min(rr, M - 1);
+    P.xsrc[i] = x + (int64_t)m * K + k0 + 8 * ((lane & 15) ^ (rr & 15));
+  }
+  pipe_issue<0, MT, NKS>(P, lds, wave);
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) P.acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  pipe_compute<0, MT, IMPL, NKS>(P, lds, g, r16);
+  const f32x4_t* acc = P.acc;
+
+  const int nbase = blockIdx.x * kRowsPerWg + wave * 16 + 4 * g;
+  if (gridDim.y == 1) {
+    const float s_t = tensor_scale[0];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r16;
+      if (m >= M) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * s_t, out_f32);
+    }
+    return;
+  }
+  const int64_t mn = (int64_t)M * N;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + r16;
+    if (m >= M) continue;
+    float* dst = ws + blockIdx.y * mn + (int64_t)m * N + nbase;
+    if ((N & 3) == 0 && nbase + 3 < N) {
       *reinterpret_cast<float4*>(dst) = float4{acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]};
       continue;
     }
@@ -661,6 +828,21 @@ hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
   return launch_fk_kernel<k_skinny_fk<MR, IMPL, K32, false, false>>(grid, p.waves, lds, stream, x, codes, scales, ts, y, M, N, K, rounds, out_f32);
 }
 
+template <int MT, int IMPL, int NKS>
+hipError_t launch_pipe(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
+                       const uint8_t* codes, const uint8_t* scales, const float* ts, void* y,
+                       float* ws, int M, int N, int K, int out_f32) {
+  const size_t lds = (size_t)NKS * 4 * MT * 1024;
+  hipError_t e = set_lds_limit<k_skinny_pipe<MT, IMPL, NKS>>(lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((N + kRowsPerWg - 1) / kRowsPerWg), (unsigned)p.splits);
+  hipLaunchKernelGGL((k_skinny_pipe<MT, IMPL, NKS>), grid, dim3(256), lds, stream, x, codes,
+                     scales, ts, y, ws, M, N, K, out_f32);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_split_reduce(ws, ts, y, (int64_t)M * N, p.splits, out_f32, stream);
+}
+
 template <int MT, int IMPL, bool K32>
 hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
                      const uint8_t* codes, const uint8_t* scales, const float* ts, void* y,
@@ -676,6 +858,19 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
         default: return launch_fk<16, IMPL, K32>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
       }
     }
+  }
+  if (p.nks > 0) {
+    if constexpr (K32) {
+      switch (p.nks) {
+        case 4: return launch_pipe<MT, IMPL, 4>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
+        case 8: return launch_pipe<MT, IMPL, 8>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
+        default:
+          if constexpr (MT <= 2)
+            return launch_pipe<MT, IMPL, 16>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
+          return hipErrorInvalidValue;
+      }
+    }
+    return hipErrorInvalidValue;
   }
   auto fn = k_skinny<MT, IMPL, K32>;
   const size_t lds = (size_t)(p.kchunk / kStepK) * 4 * MT * 4 * 16 * 16;
@@ -736,6 +931,31 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
     return p;
   }
   const int64_t tiles = (n + kRowsPerWg - 1) / kRowsPerWg;
+  if (k > 0 && k % kStepK == 0) {
+    // pipelined kernel: chunks of exactly NKS in {4, 8, 16} steps (NKS
+    // dividing the K steps), the x chunk (NKS * MT KiB) within the LDS budget
+    const int64_t lds_steps = kLdsBudget / (4 * mt * 1024);
+    int64_t nks = 0;
+    if (forced_splits > 0) {
+      const int64_t sp = forced_splits > ksteps ? ksteps : forced_splits;
+      const int64_t want = (ksteps + sp - 1) / sp;
+      if ((want == 4 || want == 8 || want == 16) && want <= lds_steps && ksteps % want == 0)
+        nks = want;
+    } else if (ksteps % 4 == 0) {
+      // 4-step chunks: the most workgroups and the smallest LDS footprint
+      // (up to 3 workgroups per CU); measured fastest on 4096 x 4096,
+      // 14336 x 4096 and 4096 x 14336 for m = 17 .. 64 (longer chunks keep
+      // fewer, longer-lived workgroups per CU and hide less latency)
+      nks = 4;
+    }
+    if (nks > 0) {
+      p.nks = (int)nks;
+      p.kchunk = (int)(nks * kStepK);
+      p.splits = (int)(ksteps / nks);
+      p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+      return p;
+    }
+  }
   int64_t splits = forced_splits;
   if (splits <= 0) splits = (256 + tiles / 2) / tiles;  // about one workgroup per CU
   if (splits < 1) splits = 1;

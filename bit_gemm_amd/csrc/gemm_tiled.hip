@@ -58,10 +58,6 @@ __device__ __forceinline__ uint4 dequant8u(uint32_t d, float sigma) {
   return o;
 }
 
-__device__ __forceinline__ float scale_value(uint32_t s) {
-  const float v = e4m3_decode(s & 0x7Fu);
-  return (s & 0x80u) ? -v : v;
-}
 
 template <int IMPL, bool K32>
 __global__ __launch_bounds__(256) void k_tiled(const uint16_t* __restrict__ x,
@@ -121,7 +117,7 @@ __global__ __launch_bounds__(256) void k_tiled(const uint16_t* __restrict__ x,
     }
   };
   auto store_step = [&]() {
-    const float sg0 = scale_value(sb0), sg1 = scale_value(sb1);
+    const float sg0 = scale_at<IMPL, 0>(sb0), sg1 = scale_at<IMPL, 0>(sb1);
     const int rl = t >> 1, nt = rl >> 4, rr = rl & 15;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -255,7 +251,7 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
     for (int i = 0; i < WA; ++i) {
       const int tile = WA * wave + i;
       if (tile >= NT) break;
-      const float sg0 = scale_value(R.sv[i] & 0xFFu), sg1 = scale_value((R.sv[i] >> 8) & 0xFFu);
+      const float sg0 = scale_at<IMPL, 0>(R.sv[i]), sg1 = scale_at<IMPL, 1>(R.sv[i]);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const uint4 o = dequant8u<IMPL>(R.cv[i][ks], ks < 2 ? sg0 : sg1);

@@ -23,12 +23,14 @@ hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, const flo
 // Skinny (m <= 64) path.  splits == 0: full-K kernel with `waves` waves per
 // workgroup.  splits >= 1: split-K kernel over `kchunk`-wide K chunks, plus a
 // reduction kernel when splits > 1 (fp32 partials [splits, m, n] in the
-// workspace).
+// workspace); nks > 0 selects the pipelined split-K kernel with nks K steps
+// unrolled (K a multiple of 128), nks == 0 the general one.
 struct SkinnyPlan {
   int splits;
   int kchunk;
   int waves;
   int steps_per_wave;
+  int nks;
   size_t ws_bytes;
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits);

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "launchers.h"
+
 #include <atomic>
 
 namespace nvfp4 {
@@ -43,10 +45,30 @@ __device__ __forceinline__ float e4m3_rne(float u, uint32_t* code) {
 }
 
 // Value of an E4M3 bit pattern with the sign bit clear (0x00..0x7E).
+// Branch free (both forms, then a select): the GEMM kernels decode two
+// scales per K step and lane.
 __device__ __forceinline__ float e4m3_decode(uint32_t c) {
-  uint32_t e = (c >> 3) & 15u, m = c & 7u;
-  if (e == 0) return (float)m * 0x1p-9f;
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  const float sub = (float)m * 0x1p-9f;
+  const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
+}
+
+// Signed value of the E4M3 block scale in byte J of `word`.  kConvHw:
+// gfx950's OCP E4M3 -> fp32 conversion with a byte selector (exact: every
+// E4M3 value is an fp32; checked over all 256 bytes at each byte position by
+// nvfp4_selftest_cvt), one instruction.  Otherwise the bit decode above.
+// The NaN patterns 0x7F / 0xFF are never written by the quantizer.
+template <int IMPL, int J>
+__device__ __forceinline__ float scale_at(uint32_t word) {
+  static_assert(J >= 0 && J < 4, "byte selector");
+  if constexpr (IMPL == kConvHw) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)word, J);
+  } else {
+    const uint32_t b = (word >> (8 * J)) & 0xFFu;
+    const float v = e4m3_decode(b & 0x7Fu);
+    return (b & 0x80u) ? -v : v;
+  }
 }
 
 // E2M1 magnitude index (0..7 <-> 0, .5, 1, 1.5, 2, 3, 4, 6) of v >= 0, round

@@ -1,5 +1,6 @@
-// Validation of the gfx950 scaled FP4 conversion instructions against the
-// library's portable ALU rounding and decoding (nvfp4_device.h).  The
+// Validation of the gfx950 scaled FP4 and the FP8 (E4M3) conversion
+// instructions against the library's portable ALU rounding and decoding
+// (nvfp4_device.h).  The
 // hardware path (NVFP4_IMPL_HWCVT) is only the default when every counter
 // here is zero on the device.
 #include "launchers.h"
@@ -90,6 +91,24 @@ __global__ __launch_bounds__(256) void k_decode(uint32_t* counters) {
 #undef DEC16_AT
   }
   count(&counters[5], bad5);
+  // [6] E4M3 scale decode by the fp8 conversion, each byte position: the
+  // signed bit decode for every byte, NaN for the two NaN patterns
+  uint32_t bad6 = 0u;
+  if (scode == 0) {
+    const uint32_t other = (byte ^ 0x3Cu) * 0x01010101u;
+    const float mag = e4m3_decode(byte & 0x7Fu);
+    const float want = (byte & 0x80u) ? -mag : mag;
+    const bool nan_pattern = (byte & 0x7Fu) == 0x7Fu;
+#define E4M3_AT(J)                                                                        \
+  {                                                                                       \
+    const uint32_t wj = (other & ~(0xFFu << (8 * J))) | (byte << (8 * J));               \
+    const float v = scale_at<kConvHw, J>(wj);                                             \
+    bad6 += (nan_pattern ? (v == v) : (__float_as_uint(v) != __float_as_uint(want))) ? 1u : 0u; \
+  }
+    E4M3_AT(0) E4M3_AT(1) E4M3_AT(2) E4M3_AT(3)
+#undef E4M3_AT
+  }
+  count(&counters[6], bad6);
 }
 
 __global__ void k_zero8(uint32_t* c) {

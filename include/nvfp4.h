@@ -179,7 +179,8 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *   m <= 16 -> memory-bound skinny kernel, one launch, a workgroup per 16
  *     weight rows over the whole K;
  *   16 < m <= 64 -> split-K skinny kernel with activations shared through
- *     LDS by 64 weight rows, plus a reduction kernel, when k % 64 != 0 or
+ *     LDS by 64 weight rows, plus a reduction kernel, when m <= 48 and
+ *     k % 128 == 0 (chunks of 512, pipelined), or when k % 64 != 0 or
  *     n * k <= 2^25; else the tiled kernel;
  *   m > 64 -> the tiled kernel.
  * The tiled kernel (bf16 MFMA): when k % 64 == 0, one 64-token tile x 256
@@ -215,8 +216,9 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
 NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);
 
 /*
- * nvfp4_selftest_cvt - validation of the gfx950 FP4 conversion
- * instructions against the library's portable ALU rounding and decoding.
+ * nvfp4_selftest_cvt - validation of the gfx950 FP4 and FP8 (E4M3)
+ * conversion instructions against the library's portable ALU rounding and
+ * decoding.
  * Runs on `stream` and writes 8 uint32 counters to the device buffer
  * `counters_out`:
  *  [0] fp32 -> FP4 code mismatches over every non-NaN fp32 bit pattern
@@ -229,7 +231,9 @@ NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);
  *  [3] FP4 byte -> 2 x bf16 with scale sigma, against val * sigma,
  *  [4] number of fp32 values tested in [0],
  *  [5] FP4 byte -> 2 x bf16 decode at unit scale (256 bytes, from each of
- *      the four byte positions), [6..7] reserved (0).
+ *      the four byte positions),
+ *  [6] E4M3 scale byte -> fp32 decode (256 bytes, sign included, from each
+ *      of the four byte positions; NaN for 0x7F and 0xFF), [7] reserved (0).
  * Used by the tests to decide whether NVFP4_IMPL_HWCVT is exact.
  */
 NVFP4_API int nvfp4_selftest_cvt(uint32_t* counters_out, void* stream);

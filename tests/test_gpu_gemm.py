@@ -80,6 +80,32 @@ def test_forced_split_k(split):
     assert _rel(y, ref) <= 1e-5
 
 
+# The pipelined split-K skinny kernel (k % 128 == 0): chunks of 4, 8 or 16
+# K steps of 128 (automatic = 4; a forced split count selects it when it
+# gives exactly one of those), 1 to 4 token tiles of 16, ragged n and m.
+PIPE_CASES = [
+    # (m, n, k, split_k): split 0 = automatic
+    (17, 200, 2048, 0), (32, 64, 2048, 2), (40, 1000, 2048, 0), (49, 130, 2048, 2), (64, 200, 2048, 0),
+    (20, 100, 2048, 1), (1, 300, 2048, 4), (7, 64, 2048, 2), (16, 333, 2048, 1), (64, 64, 512, 0),
+    (33, 65, 1536, 3), (45, 190, 2048, 2), (48, 4000, 128, 0),
+]
+
+
+@pytest.mark.parametrize("impl", [nv.IMPL_PORTABLE, nv.IMPL_HWCVT])
+def test_pipe_kernel_configs(impl):
+    for i, (m, n, k, split) in enumerate(PIPE_CASES):
+        print("pipe case", m, n, k, split, "impl", impl, flush=True)
+        w = synth.student_t_weights(n, k, seed=800 + i)
+        q, r = _quant(w)
+        x = synth.activations(m, k, seed=900 + i)
+        ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+        for dt in (torch.bfloat16, torch.float32):
+            y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt, path=nv.PATH_SKINNY, split_k=split, impl=impl)
+            torch.cuda.synchronize()
+            e = _rel(y, ref)
+            assert e <= TOL[dt], (m, n, k, split, dt, e)
+
+
 @pytest.mark.parametrize("path", [nv.PATH_SKINNY, nv.PATH_TILED])
 def test_one_hot_exact(path):
     """x = e_k with s_t a power of two: y[:, n] = W_hat[n, k] exactly."""

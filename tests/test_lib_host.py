@@ -100,8 +100,11 @@ def test_dispatch_and_workspace_plan(L):
     P = L.nvfp4_w4a16_gemm_path
     assert P(1, 4096, 4096) == S and P(16, 14336, 14336) == S
     assert P(48, 4096, 4096) == S and P(64, 4096, 4096) == S and P(65, 4096, 4096) == T
-    assert P(17, 14336, 4096) == T and P(48, 14336, 4096) == T
-    assert P(17, 4096, 14336) == T and P(32, 4096, 14336) == T
+    # the pipelined skinny kernel up to m = 48 (k % 128 == 0), then the
+    # tiled kernel on the larger shapes
+    assert P(17, 14336, 4096) == S and P(48, 14336, 4096) == S and P(49, 14336, 4096) == T
+    assert P(17, 4096, 14336) == S and P(48, 4096, 14336) == S and P(64, 4096, 14336) == T
+    assert P(48, 14336, 4160) == T  # k % 128 != 0, large: tiled
     assert P(48, 14336, 4112) == S and P(64, 4096, 4112) == S  # k % 64 != 0
     assert P(4096, 4096, 4096) == T
     assert L.nvfp4_w4a16_gemm_workspace_size(0, 4096, 4096) == 0
@@ -111,8 +114,8 @@ def test_dispatch_and_workspace_plan(L):
     # multiple of 64 takes the single-stage kernel, no split
     T = nv.PATH_TILED
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(64, 4096, 4096, T, 0) == 16 * 4 * 64 * 4096
-    assert L.nvfp4_w4a16_gemm_workspace_size(48, 14336, 4096) == 8 * 4 * 48 * 14336
-    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 14336) == 14 * 4 * 48 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(48, 14336, 4096, T, 0) == 8 * 4 * 48 * 14336
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(48, 4096, 14336, T, 0) == 14 * 4 * 48 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(128, 4096, 4096) == 16 * 4 * 128 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(4096, 4096, 4096) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size(1024, 14336, 4096) == 0
@@ -129,7 +132,10 @@ def test_dispatch_and_workspace_plan(L):
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
             ws = L.nvfp4_w4a16_gemm_workspace_size(m, n, k)
             assert ws == 0 or ((ws - C) % (4 * m * n) == 0 and ws <= 64 * 4 * m * n + C)
-    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 4096) == C + 4 * 4 * 48 * 4096
+    # k % 128 == 0: K chunks of 512 (4 steps of 128)
+    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 4096) == C + 8 * 4 * 48 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(48, 14336, 4096) == C + 8 * 4 * 48 * 14336
+    assert L.nvfp4_w4a16_gemm_workspace_size(17, 4096, 14336) == C + 28 * 4 * 17 * 4096
     # explicit split K
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 2048, nv.PATH_SKINNY, 1) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 4) == C + 4 * 4 * 8 * 4096
