@@ -1,0 +1,41 @@
+"""The pipelined split-K skinny kernels issue their weight loads as inline
+asm and wait for them with counted vmcnt waits.  Compile them for gfx950
+(device assembly, the library's own flags) and check that no instruction
+touches a load's destination register before the wait that covers it."""
+
+import os
+import subprocess
+
+import pytest
+
+from bit_gemm_amd import build
+from asm_waits import check_assembly, check_kernel
+
+
+def test_checker_flags_early_reads():
+    # a load, then a read of its destination before any wait
+    lines = ["global_load_dwordx4 v[4:7], v[0:1], off", "v_mov_b32_e32 v8, v5", "s_waitcnt vmcnt(0)"]
+    assert check_kernel(lines) == ["v_mov_b32_e32 v8, v5"]
+    # two loads in order: after vmcnt(1) the first has landed, the second not
+    lines = ["global_load_dwordx4 v[4:7], v[0:1], off", "global_load_dword v9, v[0:1], off",
+             "s_waitcnt vmcnt(1)", "v_mov_b32_e32 v8, v5", "v_add_u32_e32 v10, v9, v9",
+             "s_waitcnt vmcnt(0)", "v_add_u32_e32 v11, v9, v9"]
+    assert check_kernel(lines) == ["v_add_u32_e32 v10, v9, v9"]
+    # LDS DMA and stores count in the order but have no register result
+    lines = ["global_load_dword v9, v[0:1], off", "global_load_lds_dwordx4 v[2:3], off",
+             "s_waitcnt vmcnt(1)", "v_mov_b32_e32 v8, v9"]
+    assert check_kernel(lines) == []
+
+
+@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc") and not os.environ.get("HIPCC"),
+                    reason="hipcc not available")
+def test_pipe_kernels_wait_before_use(tmp_path):
+    src = os.path.join(build.CSRC, "gemm_skinny.hip")
+    out = tmp_path / "gemm_skinny.s"
+    flags = [f for f in build.COMMON if f != "-fPIC"]
+    cmd = [build.hipcc(), *flags, "-x", "hip", "--offload-device-only", "-S", src, "-o", str(out)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    found, bad = check_assembly(out.read_text(), r"k_skinny_pipe")
+    assert found >= 20, found  # MT 1..4 x chunk lengths x 2 conversion implementations
+    assert bad == [], bad[:10]
