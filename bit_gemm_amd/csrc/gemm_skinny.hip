@@ -919,7 +919,13 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   SkinnyPlan p{};
   const int mt = (int)((m + 15) / 16);
   const int64_t ksteps = (k + kStepK - 1) / kStepK;
-  if (forced_splits <= 0 && mt == 1 && k > 0) {
+  // 8 < m <= 16 with more 16-row workgroups than CUs: the full-K kernel's
+  // 16-token build needs ~141 KiB of LDS per workgroup (one per CU), so its
+  // workgroups run in several serial rounds; the pipelined split-K kernel is
+  // faster there (14336 x 4096 at m = 12 / 16: 16.6 / 17.4 us against
+  // 20.5 / 20.6 us).
+  const bool pipe_small = forced_splits <= 0 && m > 8 && (n + 15) / 16 > 256 && k % 512 == 0;
+  if (forced_splits <= 0 && mt == 1 && k > 0 && !pipe_small) {
     // full K per workgroup: one 512-wide slice per wave and round, up to 8
     // waves (longer K loops over rounds)
     int64_t waves = (k + kWaveK - 1) / kWaveK;

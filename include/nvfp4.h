@@ -171,13 +171,14 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *            nvfp4_w4a16_gemm_workspace_size(m, n, k) bytes, 16-byte
  *            aligned (may be NULL when that size is 0).  Scratch: its
  *            contents on entry do not matter.  Calls that may run
- *            concurrently must use distinct workspaces.  m <= 16 needs
- *            none (size 0); it holds fp32 partial sums [splits, m, n]
- *            whenever a path splits K.
+ *            concurrently must use distinct workspaces.  The full-K
+ *            kernel (m <= 16, see below) needs none (size 0); it holds fp32
+ *            partial sums [splits, m, n] whenever a path splits K.
  * Dispatch (the lower-latency kernel for the shape, [Recap] section 1, as
  * measured on MI355X; nvfp4_w4a16_gemm_path tells which):
  *   m <= 16 -> memory-bound skinny kernel, one launch, a workgroup per 16
- *     weight rows over the whole K;
+ *     weight rows over the whole K (except 8 < m <= 16 with n > 4096 and
+ *     k % 512 == 0: the pipelined split-K kernel below);
  *   16 < m <= 64 -> split-K skinny kernel with activations shared through
  *     LDS by 64 weight rows, plus a reduction kernel, when m <= 48 and
  *     k % 128 == 0 (chunks of 512, pipelined), or when k % 64 != 0 or

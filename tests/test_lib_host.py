@@ -126,7 +126,10 @@ def test_dispatch_and_workspace_plan(L):
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 1) == 0
     for m in (1, 8, 16):  # the full-K skinny kernel needs no workspace
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
-            assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0
+            if m > 8 and n > 4096:  # 8 < m <= 16 with > 256 row tiles: pipelined split-K
+                assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == (k // 512) * 4 * m * n
+            else:
+                assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0
     C = 0  # the workspace holds only the fp32 partials [splits, m, n]
     for m in (17, 48):
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
