@@ -54,6 +54,9 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--dispatch-sweep", action="store_true",
+                    help="also time both GEMM paths at M = 1 ... 256 on the decoder shapes against the "
+                         "automatic dispatch (adds ~1 minute)")
     ap.add_argument("--no-shapes", action="store_true",
                     help="skip the per-shape GEMM report on the MLP and large-M decoder layers")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
@@ -319,6 +322,8 @@ def main(argv=None):
         "kernel_source_sha": kernel_source_hash(),
     }
 
+    if args.dispatch_sweep:
+        result["dispatch_sweep"] = dispatch_sweep(args, stream, time_op, src[0])
     if not args.no_shapes:
         result["decoder_shapes"] = decoder_shapes(args, stream, time_op, src[0])
         result["decoder_model_32_layers"] = decoder_model(args, stream, src[0])
@@ -393,6 +398,56 @@ def decoder_shapes(args, stream, time_op, w_dev):
                       "path": "skinny" if nv.gemm_path(m, n, k) == nv.PATH_SKINNY else "tiled"}
         out["large_m"][f"{name}_n{n}_k{k}"] = res
         del qs, ws
+        torch.cuda.empty_cache()
+    return out
+
+
+SWEEP_SHAPES = [("attn", 4096, 4096), ("up_gate", 14336, 4096), ("down", 4096, 14336)]
+SWEEP_M = [1, 2, 4, 8, 12, 16, 24, 32, 40, 48, 56, 64, 96, 128, 192, 256]
+
+
+def dispatch_sweep(args, stream, time_op, w_dev):
+    """Both GEMM paths (their own automatic plans) at M = 1 ... 256 on the
+    three decoder shapes, beside the path the automatic dispatch picks: the
+    pages' rule is that the lower-latency kernel wins, so the dispatch is
+    right where it picks the faster one.  Cold rotating copies as in
+    decoder_shapes; the skinny path exists for m <= 64."""
+    import torch
+
+    import bit_gemm_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for name, n, k in SWEEP_SHAPES:
+        wb = bytes_gemm_weights(n, k)
+        count = max(8, int((1 << 30) // wb))
+        w = w_dev.repeat((n + N - 1) // N, (k + K - 1) // K)[:n, :k].contiguous()
+        q = nv.quantize_fos(w)
+        del w
+        codes = q.codes.unsqueeze(0).repeat(count, 1, 1)
+        scales = q.scales.unsqueeze(0).repeat(count, 1, 1)
+        qs = [nv.NVFP4Weight(codes[i], scales[i], q.tensor_scale, q.amax, None) for i in range(count)]
+        need = max(nv.workspace_size(m, n, k, p) for m in SWEEP_M for p in (nv.PATH_SKINNY, nv.PATH_TILED)
+                   if p == nv.PATH_TILED or m <= 64)
+        ws = torch.empty(max(16, need), dtype=torch.uint8, device=dev)
+        rows = {}
+        for m in SWEEP_M:
+            x = synth.activations(m, k, synth.activation_seed(m)).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            t = {}
+            for pname, p in (("skinny", nv.PATH_SKINNY), ("tiled", nv.PATH_TILED)):
+                if p == nv.PATH_SKINNY and m > 64:
+                    continue
+                launches = count if m <= 64 else 16
+                t[pname] = round(time_op(lambda r: nv.w4a16_gemm(x, qs[r % count], out=y, workspace=ws, path=p),
+                                         launches), 3)
+            auto = "skinny" if nv.gemm_path(m, n, k) == nv.PATH_SKINNY else "tiled"
+            best = min(t, key=t.get)
+            rows[m] = {"us": t, "auto": auto, "fastest": best,
+                       "auto_over_fastest": round(t[auto] / t[best], 3)}
+        out[f"{name}_n{n}_k{k}"] = rows
+        del qs, codes, scales, ws
         torch.cuda.empty_cache()
     return out
 
