@@ -426,13 +426,27 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k, int forced_splits) {
     const int64_t tiles = (n + bn - 1) / bn;
     splits = (448 + tiles / 2) / tiles;
   } else {
+    // Measured on MI355X over M = 96 ... 4096 on 4096 x 4096 and 14336 x 4096
+    // (every configuration x K splits 1 ... 16): 256 x 256 tiles (8 waves)
+    // win once there are >= 128 of them, or >= 48 on wide matrices
+    // (n >= 8192) with m > 128, with K split to about 256 workgroups;
+    // otherwise 128 x 128 tiles with K split to about 512 workgroups (at
+    // least 8 steps of 64 per split: 4096 x 4096 at m = 96 takes 8 splits,
+    // 4096 x 14336 takes 16).
     const int64_t tiles256 = ((n + 255) / 256) * ((m + 255) / 256);
-    p.kernel = tiles256 >= 128 ? 2 : 1;
-    if (p.kernel == 1) {
-      // few 128 x 128 tiles: split K until there are about two workgroups per CU
+    if (tiles256 >= 128 || (n >= 8192 && m > 128 && tiles256 >= 48)) {
+      p.kernel = 2;
+      splits = (256 + tiles256 / 2) / tiles256;
+      if (splits > 4) splits = 4;
+    } else {
+      p.kernel = 1;
       const int64_t tiles = ((n + 127) / 128) * ((m + 127) / 128);
-      if (tiles < 512) splits = (512 + tiles - 1) / tiles;
+      splits = 512 / tiles;
+      if (splits > nsteps / 8) splits = nsteps / 8;
     }
+    int64_t pow2 = 1;  // measured best counts are powers of two
+    while (pow2 * 2 <= splits) pow2 *= 2;
+    splits = pow2;
   }
   if (splits > cap) splits = cap;
   if (splits > 16) splits = 16;
