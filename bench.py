@@ -54,6 +54,9 @@ def parse_args(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--kernel-reps", type=int, default=20, help="launches per graph when timing one kernel")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg (profiling runs)")
+    ap.add_argument("--profile-large-m", action="store_true",
+                    help="only run the large-M GEMM configurations a few times, eagerly, for "
+                         "rocprofv3 counter collection; prints the run list")
     ap.add_argument("--dispatch-sweep", action="store_true",
                     help="also time both GEMM paths at M = 1 ... 256 on the decoder shapes against the "
                          "automatic dispatch (adds ~1 minute)")
@@ -146,6 +149,10 @@ def main(argv=None):
 
     # ---------------- inputs -------------------------------------------------
     w_host = synth.student_t_weights(N, K, W_SEED)
+    if args.profile_large_m:
+        runs = profile_large_m(torch.from_numpy(w_host).to(dev))
+        print(json.dumps({"metric": "large-M GEMM runs for counter collection", "runs": runs}), flush=True)
+        return 0
     src = [torch.from_numpy(w_host).to(dev) for _ in range(ROT_SRC)]
     xs = {m: synth.activations(m, K, synth.activation_seed(m)).to(dev) for m in M_LIST}
     ys = {m: torch.empty((m, N), dtype=torch.bfloat16, device=dev) for m in M_LIST}
@@ -404,6 +411,39 @@ def decoder_shapes(args, stream, time_op, w_dev):
 
 SWEEP_SHAPES = [("attn", 4096, 4096), ("up_gate", 14336, 4096), ("down", 4096, 14336)]
 SWEEP_M = [1, 2, 4, 8, 12, 16, 24, 32, 40, 48, 56, 64, 96, 128, 192, 256]
+
+
+PROFILE_M = [256, 1024, 4096]
+
+
+def profile_large_m(w_dev):
+    """A short, eager run of the large-M configurations for counter
+    collection (rocprofv3 --kernel-trace / --pmc): for each shape in
+    LARGE_SHAPES and M in PROFILE_M, one warm-up and three launches of the
+    automatic-path GEMM on the current stream, in this fixed order (so
+    dispatches map to configurations by their order)."""
+    import torch
+
+    import bit_gemm_amd as nv
+    import synth
+
+    dev = torch.device("cuda:0")
+    runs = []
+    for name, n, k in LARGE_SHAPES:
+        w = w_dev.repeat((n + N - 1) // N, (k + K - 1) // K)[:n, :k].contiguous()
+        q = nv.quantize_fos(w)
+        del w
+        for m in PROFILE_M:
+            x = synth.activations(m, k, synth.activation_seed(m)).to(dev)
+            y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(16, nv.workspace_size(m, n, k)), dtype=torch.uint8, device=dev)
+            for _ in range(4):
+                nv.w4a16_gemm(x, q, out=y, workspace=ws)
+            torch.cuda.synchronize()
+            runs.append({"shape": f"{name}_n{n}_k{k}", "m": m, "launches": 4, "flops": 2 * m * n * k,
+                         "path": "skinny" if nv.gemm_path(m, n, k) == nv.PATH_SKINNY else "tiled",
+                         "workspace_bytes": nv.workspace_size(m, n, k)})
+    return runs
 
 
 def dispatch_sweep(args, stream, time_op, w_dev):
