@@ -3,22 +3,24 @@
 // The pages switch to another kernel above M ~ 48 ("SOAR 2026 Recap ...",
 // section "1. Quantization and GEMM dispatch"), there an FP4 x FP4 MMA.  Here
 // the activations stay bf16 (W4A16) and the weights are dequantized to bf16
-// (val * sigma is exact in bf16) into LDS, because the NVFP4 block scales
+// (val * sigma is exact in bf16), because the NVFP4 block scales
 // (E4M3 per 16) are not the block-scale layout of gfx950's scaled MFMA.
 //
-// Two kernels:
-//  * k_lm (K a multiple of 64): BN weight rows x BM tokens per workgroup,
-//    v_mfma_f32_32x32x16_bf16 (the 32x32 shape keeps the matrix cores busy
-//    with few independent accumulators; the 16x16x32 shape needs more than a
-//    wave holds here), 64 k per step, two LDS stages (the next step's weights
-//    are dequantized and its activations stored while the current step's
-//    MFMAs run, one barrier per step), global loads two steps ahead.
-//    Configurations: m <= 64: one 64-token tile x 256 weight rows (4 waves),
-//    or x 128 rows for long K; larger m: 256 x 256 with 8 waves (each
-//    64 x 128) when there are enough such tiles to fill the GPU, else
-//    128 x 128 with 4 waves.  With few tiles the K loop is split over
-//    workgroups (fp32 partials, then a reduction kernel adds them in split
-//    order).
+// Three kernels:
+//  * k_lmr (K a multiple of 64, m > 128): 256 weight rows x 128 tokens per
+//    workgroup, each wave dequantizing its 64 weight rows straight into MFMA
+//    A fragments (the weights never touch LDS) while the activations arrive
+//    in LDS by DMA; v_mfma_f32_32x32x16_bf16, two waves per SIMD.
+//  * k_lm (K a multiple of 64, m <= 128): BN weight rows x BM tokens per
+//    workgroup, v_mfma_f32_32x32x16_bf16 (the 32x32 shape keeps the matrix
+//    cores busy with few independent accumulators; the 16x16x32 shape needs
+//    more than a wave holds here), 64 k per step, two LDS stages (the next
+//    step's weights are dequantized and its activations stored while the
+//    current step's MFMAs run, one barrier per step), global loads two steps
+//    ahead.  Configurations: m <= 64: one 64-token tile x 256 weight rows
+//    (4 waves), or x 128 rows for long K; 64 < m <= 128: 128 x 128.
+//  With few tiles the K loop is split over workgroups (fp32 partials, then
+//  a reduction kernel adds them in split order).
 //  * k_tiled (any K): 128 x 128 x 64 tiles, 4 waves of 4 x 4
 //    v_mfma_f32_16x16x32_bf16, one LDS stage.
 #include "launchers.h"
@@ -375,6 +377,204 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_lmr: large-M kernel with the weights in registers.  A workgroup covers
+// 256 weight rows x BM tokens with 4 waves; wave w owns rows 64 w .. +64 (two
+// 32-row MFMA A tiles) against all BM tokens.  Per 64-k step:
+//  * each lane loads, for each of its two rows, the 32 codes (16 bytes) and
+//    the 2 scale bytes of its k half (h = lane / 32: k0 + 32 h .. +32), and
+//    dequantizes them straight into A fragments - the weights never touch
+//    LDS (in k_lm their dequantized stores and fragment loads were most of
+//    the LDS traffic);
+//  * the step's activations (BM rows x 128 bytes) arrive in LDS by DMA,
+//    shared by the 4 waves: DMA instruction c copies token rows 8 c .. +8,
+//    whole cache lines, lane l -> row 8 c + l / 8, 16-byte piece
+//    (l % 8) ^ ((row / 2) % 8), so piece q of row r lands at slot
+//    q ^ ((r / 2) % 8) and the B fragment reads of 16 rows hit 16 bank
+//    groups.
+// k order: MFMA ks of a step pairs logical k 0..7 with physical k 8 ks .. +8
+// and logical k 8..15 with 32 + 8 ks .. +8, on both operands.
+// Pipeline: weights two steps ahead (two register sets), activations one
+// step ahead (two LDS stages).  The loads are inline asm with counted waits
+// (the compiler cannot count LDS DMA and plain loads together); every step
+// issues the same loads (addresses clamped to the last step at the end), so
+// the wait count is the same at every step.
+// blockIdx.z = K split as in k_lm.
+template <int BM, int IMPL>
+__global__ __launch_bounds__(256, 2) void k_lmr(const uint16_t* __restrict__ x,
+                                             const uint8_t* __restrict__ codes,
+                                             const uint8_t* __restrict__ scales,
+                                             const float* __restrict__ tensor_scale,
+                                             void* __restrict__ y, float* __restrict__ ws, int M,
+                                             int N, int K, int steps_per, int out_f32) {
+  constexpr int MTILES = BM / 32;  // 32-token MFMA B tiles
+  constexpr int NDMA = BM / 32;    // DMA instructions per wave per step (BM rows x 128 B / 4 waves)
+  constexpr int STAGE = BM * 128;
+  constexpr int WOPS = 4;          // weight loads per step: 2 x codes, 2 x scales
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int h = lane >> 5, r32 = lane & 31;
+  const int n0 = blockIdx.x * 256, m0 = blockIdx.y * BM;
+  const int s0 = blockIdx.z * steps_per;
+  const int nsteps = min(K / 64 - s0, steps_per);  // >= 1 (the plan has no empty split)
+  const int kbase = s0 * 64;
+
+  // weight rows of this lane (rows past N read row N - 1; not stored)
+  const uint8_t* cp[2];
+  const uint8_t* sp[2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int row = min(n0 + 64 * wave + 32 * a + r32, N - 1);
+    cp[a] = codes + (int64_t)row * (K / 2) + kbase / 2 + 16 * h;
+    sp[a] = scales + (int64_t)row * (K / 16) + kbase / 16 + 2 * h;
+  }
+  // activation pieces this lane copies (token rows past M read row M - 1)
+  const uint16_t* xp[NDMA];
+#pragma unroll
+  for (int i = 0; i < NDMA; ++i) {
+    const int rho = 8 * (wave + 4 * i) + (lane >> 3);
+    const int m = min(m0 + rho, M - 1);
+    xp[i] = x + (int64_t)m * K + kbase + 8 * ((lane & 7) ^ ((rho >> 1) & 7));
+  }
+
+  struct WRegs {
+    u32x4_t c[2];
+    uint32_t s[2];
+  };
+  auto issue_w = [&](WRegs& W, int step) {
+    step = min(step, nsteps - 1);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) load_b128_async<0>(W.c[a], cp[a] + 32 * step);
+#pragma unroll
+    for (int a = 0; a < 2; ++a) load_u16_async<0>(W.s[a], sp[a] + 4 * step);
+  };
+  auto issue_x = [&](int step) {
+    const int st = step & 1;
+    step = min(step, nsteps - 1);
+#pragma unroll
+    for (int i = 0; i < NDMA; ++i)
+      copy16_to_lds(xp[i] + 64 * step, lds + st * STAGE + 1024 * (wave + 4 * i));
+    asm volatile("" ::: "memory");
+  };
+
+  f32x16_t acc[2][MTILES];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < MTILES; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  // One step: wait for its weights (set W) and activations (stage s % 2) -
+  // only the weights issued one step earlier may still be in flight - then
+  // a barrier (every wave's copies have landed, and every wave is done with
+  // stage (s + 1) % 2), dequantize, issue the loads of steps s + 1 (copies)
+  // and s + 2 (weights, into W), and run the MFMAs.
+  auto step = [&](int s, WRegs& W) {
+    wait_vm4<WOPS>(W.c[0], W.c[1], W.s[0], W.s[1]);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    bf16x8_t af[4][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+      const float sg0 = scale_at<IMPL, 0>(W.s[a]), sg1 = scale_at<IMPL, 1>(W.s[a]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        af[ks][a] = __builtin_bit_cast(bf16x8_t, dequant8u<IMPL>(W.c[a][ks], ks < 2 ? sg0 : sg1));
+    }
+    issue_x(s + 1);
+    issue_w(W, s + 2);
+    const uint8_t* st = lds + (s & 1) * STAGE;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int b = 0; b < MTILES; ++b) {
+        const int rho = 32 * b + r32;
+        const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(
+            st + 128 * rho + 16 * ((4 * h + ks) ^ ((rho >> 1) & 7)));
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks][a], bv, acc[a][b], 0, 0, 0);
+      }
+    }
+  };
+
+  WRegs W0, W1;
+  issue_w(W0, 0);
+  issue_x(0);
+  issue_w(W1, 1);
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, W0);
+    if (s + 1 < nsteps) step(s + 1, W1);
+  }
+  wait_vm_all();  // the tail's clamped copies must land before the workgroup's LDS is released
+
+  // D of a 32 x 32 tile: lane l, value v -> weight row 8 (v / 4) + 4 (l / 32)
+  // + v % 4, token l % 32.  With a K split: raw fp32 partials to plane z.
+  const bool partial = gridDim.z > 1;
+  float* plane = ws + (int64_t)blockIdx.z * M * N;
+  const float s_t = partial ? 1.0f : tensor_scale[0];
+#pragma unroll
+  for (int b = 0; b < MTILES; ++b) {
+    const int m = m0 + 32 * b + r32;
+    if (m >= M) continue;
+#pragma unroll
+    for (int a = 0; a < 2; ++a) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 64 * wave + 32 * a + 8 * q + 4 * h;
+        const float v0 = acc[a][b][4 * q] * s_t, v1 = acc[a][b][4 * q + 1] * s_t;
+        const float v2 = acc[a][b][4 * q + 2] * s_t, v3 = acc[a][b][4 * q + 3] * s_t;
+        const int64_t idx = (int64_t)m * N + n;
+        if (partial) {
+          if ((N & 3) == 0 && n + 3 < N) {
+            *reinterpret_cast<float4*>(plane + idx) = make_float4(v0, v1, v2, v3);
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (n + i < N) plane[idx + i] = vv[i];
+          }
+        } else if ((N & 3) == 0 && n + 3 < N) {
+          if (out_f32) {
+            *reinterpret_cast<float4*>(reinterpret_cast<float*>(y) + idx) = make_float4(v0, v1, v2, v3);
+          } else {
+            uint2 v;
+            v.x = bf16_rne_bits(v0) | (bf16_rne_bits(v1) << 16);
+            v.y = bf16_rne_bits(v2) | (bf16_rne_bits(v3) << 16);
+            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(y) + idx) = v;
+          }
+        } else {
+          const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (n + i >= N) continue;
+            if (out_f32)
+              reinterpret_cast<float*>(y)[idx + i] = vv[i];
+            else
+              reinterpret_cast<uint16_t*>(y)[idx + i] = (uint16_t)bf16_rne_bits(vv[i]);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int BM, int IMPL>
+hipError_t launch_lmr(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
+                      const float* ts, void* y, float* ws, int M, int N, int K, int splits,
+                      int steps_per, int out_f32, hipStream_t stream) {
+  constexpr size_t lds = 2 * (size_t)BM * 128;
+  hipError_t e = set_lds_limit<k_lmr<BM, IMPL>>(lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((N + 255) / 256), (unsigned)((M + BM - 1) / BM), (unsigned)splits);
+  hipLaunchKernelGGL((k_lmr<BM, IMPL>), grid, dim3(256), lds, stream, x, codes, scales, ts, y, ws,
+                     M, N, K, steps_per, out_f32);
+  e = hipGetLastError();
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_split_reduce(ws, ts, y, (int64_t)M * N, splits, out_f32, stream);
+}
+
 template <int BN, int BM, int WGN, int WGM, int IMPL>
 hipError_t launch_lm(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                      const float* ts, void* y, float* ws, int M, int N, int K, int splits,
@@ -395,15 +595,15 @@ hipError_t launch_lm_plan(const TiledPlan& p, const uint16_t* x, const uint8_t* 
                           const uint8_t* scales, const float* ts, void* y, float* ws, int M, int N,
                           int K, int out_f32, hipStream_t stream) {
   switch (p.kernel) {
-    case 2:
-      return launch_lm<256, 256, 4, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
-                                             p.steps_per_split, out_f32, stream);
     case 3:
       return launch_lm<128, 64, 2, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
                                             p.steps_per_split, out_f32, stream);
     case 4:
       return launch_lm<256, 64, 4, 1, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
                                             p.steps_per_split, out_f32, stream);
+    case 5:
+      return launch_lmr<128, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
+                                   p.steps_per_split, out_f32, stream);
     default:
       return launch_lm<128, 128, 2, 2, IMPL>(x, codes, scales, ts, y, ws, M, N, K, p.splits,
                                              p.steps_per_split, out_f32, stream);
@@ -425,25 +625,26 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k, int forced_splits) {
     const int64_t bn = p.kernel == 3 ? 128 : 256;
     const int64_t tiles = (n + bn - 1) / bn;
     splits = (448 + tiles / 2) / tiles;
+  } else if (m > 128) {
+    // k_lmr (weights in registers, 256 x 128 tiles, two waves per SIMD):
+    // measured faster than the LDS-staged kernels from m = 256 on every
+    // decoder shape (e.g. 4096 x 4096 x 4096: 142 us against 181 us; 4096 x
+    // 14336 at m = 1024: 149 against 212 us), K split to about 256
+    // workgroups with at least 16 steps of 64 per split
+    p.kernel = 5;
+    const int64_t tiles = ((n + 255) / 256) * ((m + 127) / 128);
+    splits = 256 / tiles;
+    if (splits > nsteps / 16) splits = nsteps / 16;
   } else {
-    // Measured on MI355X over M = 96 ... 4096 on 4096 x 4096 and 14336 x 4096
-    // (every configuration x K splits 1 ... 16): 256 x 256 tiles (8 waves)
-    // win once there are >= 128 of them, or >= 48 on wide matrices
-    // (n >= 8192) with m > 128, with K split to about 256 workgroups;
-    // otherwise 128 x 128 tiles with K split to about 512 workgroups (at
-    // least 8 steps of 64 per split: 4096 x 4096 at m = 96 takes 8 splits,
-    // 4096 x 14336 takes 16).
-    const int64_t tiles256 = ((n + 255) / 256) * ((m + 255) / 256);
-    if (tiles256 >= 128 || (n >= 8192 && m > 128 && tiles256 >= 48)) {
-      p.kernel = 2;
-      splits = (256 + tiles256 / 2) / tiles256;
-      if (splits > 4) splits = 4;
-    } else {
-      p.kernel = 1;
-      const int64_t tiles = ((n + 127) / 128) * ((m + 127) / 128);
-      splits = 512 / tiles;
-      if (splits > nsteps / 8) splits = nsteps / 8;
-    }
+    // 64 < m <= 128: 128 x 128 tiles with K split to about 512 workgroups
+    // (at least 8 steps of 64 per split: 4096 x 4096 at m = 96 takes 8
+    // splits, 4096 x 14336 takes 16)
+    p.kernel = 1;
+    const int64_t tiles = ((n + 127) / 128) * ((m + 127) / 128);
+    splits = 512 / tiles;
+    if (splits > nsteps / 8) splits = nsteps / 8;
+  }
+  if (m > 64) {
     int64_t pow2 = 1;  // measured best counts are powers of two
     while (pow2 * 2 <= splits) pow2 *= 2;
     splits = pow2;

@@ -45,10 +45,11 @@ hipError_t launch_split_reduce(const float* ws, const float* tensor_scale, void*
                                int splits, int out_f32, hipStream_t stream);
 
 // Tiled bf16-MFMA path (any m).  kernel: 0 = 128 x 128 single-stage kernel
-// (any K); two-stage kernels (K a multiple of 64), weight rows x tokens per
-// workgroup: 1 = 128 x 128, 2 = 256 x 256, 3 = 128 x 64, 4 = 256 x 64; they
-// may split K over `splits` workgroups of `steps_per_split` 64-wide steps
-// (fp32 partials [splits, m, n] in the workspace, then the reduction).
+// (any K); kernels for K a multiple of 64, weight rows x tokens per
+// workgroup: 1 = 128 x 128, 3 = 128 x 64, 4 = 256 x 64 (weights and
+// activations staged in LDS), 5 = 256 x 128 with the weights in registers;
+// they may split K over `splits` workgroups of `steps_per_split` 64-wide
+// steps (fp32 partials [splits, m, n] in the workspace, then the reduction).
 struct TiledPlan {
   int kernel;
   int splits;

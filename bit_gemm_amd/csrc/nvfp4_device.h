@@ -118,6 +118,60 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
 
 // Host side: above 64 KiB a kernel must opt in to more dynamic LDS (gfx950
 // has 160 KiB per CU; 1 KiB is left for the kernels' static LDS).  Done once per kernel:
+// Loads whose completion the kernel waits for itself.  The compiler's own
+// wait insertion counts LDS DMA copies as a different kind of vector-memory
+// event from plain loads, and with both kinds in flight it can only wait for
+// everything (vmcnt(0)); loads written as inline asm are invisible to it, and
+// wait_vm below (which takes the loaded registers as operands, so nothing
+// that reads them can move above it) waits for exactly as many as needed.
+// (The asm bodies are compiled for the device only: the host pass of a HIP
+// source also reads device functions and has no VGPR constraint.)
+template <int OFF>
+__device__ __forceinline__ void load_b128_async(u32x4_t& d, const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(d) : "v"(p), "i"(OFF) : "memory");
+#endif
+}
+template <int OFF>
+__device__ __forceinline__ void load_u16_async(uint32_t& d, const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_ushort %0, %1, off offset:%2" : "=v"(d) : "v"(p), "i"(OFF) : "memory");
+#endif
+}
+// Wait until at most V vector-memory operations of this wave are
+// outstanding (loads return in issue order); V is capped at 63, the
+// counter's limit, which only waits longer.
+template <int V>
+__device__ __forceinline__ void wait_vm(u32x4_t& c, uint32_t& sbv) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(c), "+v"(sbv) : "n"(V > 63 ? 63 : V) : "memory");
+#endif
+}
+
+// LDS DMA of 16 bytes per lane: lane l's bytes land at dst + 16 l (dst is
+// wave-uniform).
+__device__ __forceinline__ void copy16_to_lds(const uint16_t* src, uint8_t* dst) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+#endif
+}
+
+// Wait until at most V vector-memory operations of this wave are
+// outstanding, binding two 16-byte and two 4-byte loaded values (see wait_vm).
+template <int V>
+__device__ __forceinline__ void wait_vm4(u32x4_t& a, u32x4_t& b, uint32_t& c, uint32_t& e) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(e) : "n"(V > 63 ? 63 : V) : "memory");
+#endif
+}
+
+// Wait until every vector-memory operation of this wave has completed.
+__device__ __forceinline__ void wait_vm_all() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#endif
+}
+
 // the flag is per template argument, i.e. per kernel instantiation.
 template <auto Kernel>
 hipError_t set_lds_limit(size_t lds) {

@@ -185,8 +185,9 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *     n * k <= 2^25; else the tiled kernel;
  *   m > 64 -> the tiled kernel.
  * The tiled kernel (bf16 MFMA): when k % 64 == 0, one 64-token tile x 256
- * (or, for k >= 8192, 128) weight rows for m <= 64, else 256 x 256 or
- * 128 x 128 tiles; K is split over workgroups (fp32 partials in the
+ * (or, for k >= 8192, 128) weight rows for m <= 64, 128 x 128 tiles for
+ * m <= 128, else 256 weight rows x 128 tokens with the weights dequantized
+ * in registers; K is split over workgroups (fp32 partials in the
  * workspace, one reduction kernel) when there are few tiles.  Other k:
  * 128 x 128 single-stage tiles.
  */

@@ -1,7 +1,8 @@
-"""The pipelined split-K skinny kernels issue their weight loads as inline
-asm and wait for them with counted vmcnt waits.  Compile them for gfx950
-(device assembly, the library's own flags) and check that no instruction
-touches a load's destination register before the wait that covers it."""
+"""The pipelined split-K skinny kernels and the large-M kernel with the
+weights in registers issue their weight loads as inline asm and wait for
+them with counted vmcnt waits.  Compile them for gfx950 (device assembly,
+the library's own flags) and check that no instruction touches a load's
+destination register before the wait that covers it."""
 
 import os
 import subprocess
@@ -29,13 +30,17 @@ def test_checker_flags_early_reads():
 
 @pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc") and not os.environ.get("HIPCC"),
                     reason="hipcc not available")
-def test_pipe_kernels_wait_before_use(tmp_path):
-    src = os.path.join(build.CSRC, "gemm_skinny.hip")
-    out = tmp_path / "gemm_skinny.s"
+@pytest.mark.parametrize("source,pattern,minimum", [
+    ("gemm_skinny.hip", r"k_skinny_pipe", 20),  # MT 1..4 x chunk lengths x 2 conversion implementations
+    ("gemm_tiled.hip", r"k_lmr", 2),             # weights-in-registers large-M kernel, 2 implementations
+])
+def test_counted_waits_cover_every_use(tmp_path, source, pattern, minimum):
+    src = os.path.join(build.CSRC, source)
+    out = tmp_path / (source + ".s")
     flags = [f for f in build.COMMON if f != "-fPIC"]
     cmd = [build.hipcc(), *flags, "-x", "hip", "--offload-device-only", "-S", src, "-o", str(out)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
-    found, bad = check_assembly(out.read_text(), r"k_skinny_pipe")
-    assert found >= 20, found  # MT 1..4 x chunk lengths x 2 conversion implementations
+    found, bad = check_assembly(out.read_text(), pattern)
+    assert found >= minimum, found
     assert bad == [], bad[:10]

@@ -190,12 +190,14 @@ def test_large_m_config_sampled_rows(layer):
         assert np.isfinite(y).all()
 
 
-# Two-stage tiled kernel configurations (K a multiple of 64): 256 x 256 tiles
-# when there are >= 128 of them, else 128 x 128; one 64-token tile with 256
-# (or, for K >= 8192, 128) weight rows for M <= 64, K split over workgroups;
-# ragged M and N, odd N (scalar stores), a single K step.
+# Tiled kernel configurations for K a multiple of 64: M > 128 the kernel
+# with the weights in registers (256 x 128 tiles; an odd number of K steps,
+# a single one, K split over workgroups); 64 < M <= 128: 128 x 128 tiles;
+# one 64-token tile with 256 (or, for K >= 8192, 128) weight rows for
+# M <= 64; ragged M and N, odd N (scalar stores).
 LM_SHAPES = [(1000, 8000, 192), (300, 700, 256), (257, 4100, 64), (130, 1001, 128), (5, 333, 128),
-             (40, 300, 8192), (33, 520, 1024), (64, 1000, 512)]
+             (40, 300, 8192), (33, 520, 1024), (64, 1000, 512), (100, 1001, 192), (128, 600, 4096),
+             (200, 260, 4096)]
 
 
 @pytest.mark.parametrize("impl", [nv.IMPL_PORTABLE, nv.IMPL_HWCVT])

@@ -109,19 +109,23 @@ def test_dispatch_and_workspace_plan(L):
     assert P(4096, 4096, 4096) == T
     assert L.nvfp4_w4a16_gemm_workspace_size(0, 4096, 4096) == 0
     # tiled path: m <= 64 one 64-token tile, K split to ~450 workgroups;
-    # larger m: 256 x 256 tiles (>= 128 of them, or >= 48 when n >= 8192 and
-    # m > 128) split to ~256 workgroups (<= 4), else 128 x 128 tiles split
-    # to ~512 workgroups (<= 8), powers of two; >= 4 steps of 64 per split,
-    # at most 16 splits; K not a multiple of 64 takes the single-stage
-    # kernel, no split
+    # 64 < m <= 128: 128 x 128 tiles split to ~512 workgroups (>= 8 steps
+    # per split); m > 128: 256 x 128 tiles split to ~256 workgroups (<= 4);
+    # powers of two, >= 4 steps of 64 per split, at most 16 splits; K not a
+    # multiple of 64 takes the single-stage kernel, no split
     T = nv.PATH_TILED
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(64, 4096, 4096, T, 0) == 16 * 4 * 64 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(48, 14336, 4096, T, 0) == 8 * 4 * 48 * 14336
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(48, 4096, 14336, T, 0) == 14 * 4 * 48 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(128, 4096, 4096) == 8 * 4 * 128 * 4096
-    assert L.nvfp4_w4a16_gemm_workspace_size(256, 14336, 4096) == 4 * 4 * 256 * 14336  # 56 tiles of 256
-    assert L.nvfp4_w4a16_gemm_workspace_size(512, 14336, 4096) == 2 * 4 * 512 * 14336
-    assert L.nvfp4_w4a16_gemm_workspace_size(2048, 4096, 4096) == 2 * 4 * 2048 * 4096
+    # m > 128: 256 x 128 tiles (weights in registers), K split to ~256 workgroups
+    # with >= 16 steps of 64 per split
+    assert L.nvfp4_w4a16_gemm_workspace_size(256, 4096, 14336) == 8 * 4 * 256 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(256, 4096, 4096) == 4 * 4 * 256 * 4096  # 32 tiles
+    assert L.nvfp4_w4a16_gemm_workspace_size(256, 14336, 4096) == 2 * 4 * 256 * 14336  # 112 tiles
+    assert L.nvfp4_w4a16_gemm_workspace_size(512, 14336, 4096) == 0  # 224 tiles
+    assert L.nvfp4_w4a16_gemm_workspace_size(1024, 4096, 14336) == 2 * 4 * 1024 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(2048, 4096, 4096) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size(4096, 4096, 4096) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size(1024, 14336, 4096) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size(1024, 4096, 4096) == 2 * 4 * 1024 * 4096
