@@ -11,8 +11,9 @@ Sources (web pages; cited by title and section only):
 
 * [Notes07] "SOAR Weekly Champion Notes 07 | Vanilla Xiao Zhang: NVFP4
   Quantization Improvements and Speculative Decoding in Practice",
-  sections "01 Background: Where standard NVFP4 quantization error comes from"
-  and "02 FourOverSix: Adaptively choosing between M=6 and M=4".
+  sections "01 Background: Where standard NVFP4 quantization error comes from",
+  "02 FourOverSix: Adaptively choosing between M=6 and M=4" and "03 How we
+  integrated it" (FourOverSix scales fixed before GPTQ).
 * [Recap] "SOAR 2026 Recap: From Compute Limits to the Open-Source Ecosystem",
   section "1. Quantization and GEMM dispatch".
 
@@ -28,6 +29,9 @@ codecs  E2M1 and E4M3 encode/decode written from the format definitions.
 fos     FourOverSix quantizer: vectorized numpy path and a scalar pure-Python
         path (the two are cross-checked by the tests).
 gemm    Dequantization and the float64 GEMM reference.
+gptq    GPTQ column updates inside the FourOverSix scales (fixed first), the
+        inverse-Hessian factor from calibration activations, and the
+        explicit inverse-Hessian form used to pin it.
 
 Parity status: every function here is pinned by ``-m "not gpu"`` tests against
 something other than itself (the pages' printed value set, torch's
@@ -46,3 +50,4 @@ from .codecs import (  # noqa: F401
 )
 from .fos import quantize_fos, quantize_fos_scalar, FosResult, block_sse  # noqa: F401
 from .gemm import dequant, dequant_f64, gemm_ref  # noqa: F401
+from .gptq import gptq_fos, gptq_fos_obs, hessian_factor  # noqa: F401
