@@ -62,6 +62,9 @@ def parse_args(argv=None):
                          "automatic dispatch (adds ~1 minute)")
     ap.add_argument("--no-shapes", action="store_true",
                     help="skip the per-shape GEMM report on the MLP and large-M decoder layers")
+    ap.add_argument("--no-gptq", action="store_true", help="skip the GPTQ (FourOverSix scales) report")
+    ap.add_argument("--gptq-only", action="store_true",
+                    help="only the GPTQ calls on the 4096x4096 layer (for rocprofv3 runs), then exit")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
     ap.add_argument("--eager", action="store_true",
                     help="launch the steps directly instead of from HIP graphs (for counter "
@@ -149,6 +152,10 @@ def main(argv=None):
 
     # ---------------- inputs -------------------------------------------------
     w_host = synth.student_t_weights(N, K, W_SEED)
+    if args.gptq_only:
+        print(json.dumps({"metric": "GPTQ within FourOverSix scales", "gptq": gptq_report(
+            args, torch.from_numpy(w_host).to(dev))}), flush=True)
+        return 0
     if args.profile_large_m:
         runs = profile_large_m(torch.from_numpy(w_host).to(dev))
         print(json.dumps({"metric": "large-M GEMM runs for counter collection", "runs": runs}), flush=True)
@@ -335,6 +342,8 @@ def main(argv=None):
         result["decoder_shapes"] = decoder_shapes(args, stream, time_op, src[0])
         result["decoder_model_32_layers"] = decoder_model(args, stream, src[0])
 
+    if not args.no_gptq:
+        result["gptq"] = gptq_report(args, src[0])
     if not args.no_cpu_baseline:
         result["cpu_baseline"], result["parity"] = cpu_baseline(args, w_host, xs, packed(1), step_bytes)
     print(json.dumps(result), flush=True)
@@ -414,6 +423,63 @@ SWEEP_M = [1, 2, 4, 8, 12, 16, 24, 32, 40, 48, 56, 64, 96, 128, 192, 256]
 
 
 PROFILE_M = [256, 1024, 4096]
+
+
+# fp32 vector ALU rate for separate multiply and subtract (no fused
+# multiply-add, no packed fp32): 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz
+ALU_F32_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12
+GPTQ_CALIB_SEED = 4242
+
+
+def gptq_report(args, w_dev):
+    """GPTQ inside fixed FourOverSix scales on the 4096 x 4096 layer: U (upper
+    Cholesky factor of the damped inverse Hessian) from seeded synthetic
+    calibration activations (8192 x 4096, N(0,1) x per-channel U(1,2)),
+    computed with torch.linalg in float64 outside the timed region; then the
+    average duration of whole calls (quantizer + copy + 64 panel and 63
+    trailing-update kernels) with HIP events on the call's stream.
+
+    The trailing updates bound it: each element w[r, l] receives one product
+    and one subtraction per earlier column j < l, n k (k - 1) / 2 of each,
+    on the fp32 vector ALU (the contract forbids fusing them)."""
+    import torch
+
+    import bit_gemm_amd as nv
+    import synth
+
+    dev = w_dev.device
+    n, k = w_dev.shape
+    x = torch.from_numpy(synth.calibration_activations(2 * k, k, GPTQ_CALIB_SEED)).to(dev)
+    h = 2.0 * (x.T @ x)
+    del x
+    h += 0.01 * torch.mean(torch.diag(h)) * torch.eye(k, dtype=torch.float64, device=dev)
+    hinv = torch.cholesky_inverse(torch.linalg.cholesky(h))
+    u = torch.linalg.cholesky(hinv, upper=True).to(torch.float32).contiguous()
+    del h, hinv
+    ws = torch.empty(nv.gptq_workspace_size(n, k), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    q = None
+    for _ in range(2):
+        q = nv.quantize_fos_gptq(w_dev, u, workspace=ws)
+    torch.cuda.synchronize()
+    reps = 5
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for _ in range(reps):
+        q = nv.quantize_fos_gptq(w_dev, u, workspace=ws)
+    ev1.record(stream)
+    ev1.synchronize()
+    ms = ev0.elapsed_time(ev1) / reps
+    rtn = nv.quantize_fos(w_dev)
+    torch.cuda.synchronize()
+    moved = float((q.codes != rtn.codes).to(torch.float32).mean().item())
+    ops = 2 * n * k * (k - 1) // 2
+    tops = ops / (ms * 1e-3) / 1e12
+    return {"n": n, "k": k, "ms_per_call": round(ms, 4), "launches": 2 + 2 * (k // 64) - 1,
+            "update_ops": ops, "achieved_tops": round(tops, 2),
+            "roofline": {"bound": "alu", "achieved": round(tops, 2), "peak": round(ALU_F32_OPS_PEAK_T, 2),
+                         "unit": "T fp32 ops/s (mul, sub unfused)", "frac": round(tops / ALU_F32_OPS_PEAK_T, 4)},
+            "code_bytes_changed_vs_rtn": round(moved, 4)}
 
 
 def profile_large_m(w_dev):

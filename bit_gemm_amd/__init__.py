@@ -49,6 +49,9 @@ _c_size = ctypes.c_size_t
 SIGNATURES = {
     "nvfp4_quantize_fos": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "nvfp4_quantize_fos_ex": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_p]),
+    "nvfp4_quantize_fos_gptq_workspace_size": (_c_size, [_c_i64, _c_i64]),
+    "nvfp4_quantize_fos_gptq": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                         _c_size, _c_p]),
     "nvfp4_tensor_amax": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
     "nvfp4_dequant": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p]),
     "nvfp4_w4a16_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
@@ -145,6 +148,42 @@ def quantize_fos(w: torch.Tensor, amax: Optional[torch.Tensor] = None, with_mask
     _check(lib().nvfp4_quantize_fos_ex(
         _ptr(w), n, k, _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale), _ptr(out.codes),
         _ptr(out.scales), _ptr(out.m4_mask), impl, _stream(dev)))
+    return out
+
+
+def gptq_workspace_size(n: int, k: int) -> int:
+    return int(lib().nvfp4_quantize_fos_gptq_workspace_size(n, k))
+
+
+def quantize_fos_gptq(w: torch.Tensor, hinv_u: torch.Tensor, amax: Optional[torch.Tensor] = None,
+                      with_mask: bool = True, workspace: Optional[torch.Tensor] = None) -> NVFP4Weight:
+    """FourOverSix scales fixed first, then GPTQ's column updates inside them.
+
+    ``hinv_u``: float32 [k, k] GPU matrix, the upper Cholesky factor of the
+    inverse Hessian (only its upper triangle is read)."""
+    _need_gpu(w, "w", torch.float32)
+    _need_gpu(hinv_u, "hinv_u", torch.float32)
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D")
+    n, k = w.shape
+    if tuple(hinv_u.shape) != (k, k):
+        raise ValueError(f"hinv_u must be [{k}, {k}], got {tuple(hinv_u.shape)}")
+    dev = w.device
+    out = NVFP4Weight(
+        codes=torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+        scales=torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+        tensor_scale=torch.empty(1, dtype=torch.float32, device=dev),
+        amax=torch.empty(1, dtype=torch.float32, device=dev),
+        m4_mask=torch.empty((n, k // 16), dtype=torch.uint8, device=dev) if with_mask else None,
+    )
+    if amax is not None:
+        _need_gpu(amax, "amax", torch.float32)
+    ws = gptq_workspace_size(n, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _check(lib().nvfp4_quantize_fos_gptq(
+        _ptr(w), n, k, _ptr(hinv_u), _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale), _ptr(out.codes),
+        _ptr(out.scales), _ptr(out.m4_mask), _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
 
 

@@ -148,6 +148,44 @@ NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const 
   return NVFP4_OK;
 }
 
+NVFP4_API size_t nvfp4_quantize_fos_gptq_workspace_size(int64_t n, int64_t k) {
+  if (n < 0 || k < 0 || n >= kMaxDim || k >= kMaxDim || (n > 0 && k > kMaxElems / n)) return 0;
+  return nvfp4::gptq_workspace_bytes(n, k);
+}
+
+NVFP4_API int nvfp4_quantize_fos_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u,
+                                      const float* amax_in, float* amax_out, float* tensor_scale,
+                                      uint8_t* codes, uint8_t* scales, uint8_t* m4_mask,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (k % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k=%lld: GPTQ needs k %% 64 == 0", (long long)k);
+  const bool empty = (n == 0 || k == 0);
+  if (!amax_out || !tensor_scale) return fail(NVFP4_ERR_INVALID_VALUE, "amax_out and tensor_scale are required");
+  if (!empty && (!w || !codes || !scales || !hinv_u))
+    return fail(NVFP4_ERR_INVALID_VALUE, "w, hinv_u, codes and scales are required");
+  if (!aligned(amax_out, 4) || !aligned(tensor_scale, 4) || (amax_in && !aligned(amax_in, 4)))
+    return fail(NVFP4_ERR_MISALIGNED, "scalar arguments must be 4-byte aligned");
+  if (!empty && (!aligned(w, 16) || !aligned(codes, 16) || !aligned(scales, 16) || !aligned(hinv_u, 16) ||
+                 (m4_mask && !aligned(m4_mask, 16))))
+    return fail(NVFP4_ERR_MISALIGNED, "w, hinv_u, codes, scales and m4_mask must be 16-byte aligned");
+  const size_t need = empty ? 0 : nvfp4::gptq_workspace_bytes(n, k);
+  if (need > 0) {
+    if (workspace_bytes < need)
+      return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!workspace) return fail(NVFP4_ERR_INVALID_VALUE, "workspace is NULL");
+    if (!aligned(workspace, 16)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  }
+  int ci = 0;
+  if ((st = resolve_impl(NVFP4_IMPL_DEFAULT, &ci))) return st;
+  if ((st = check_device())) return st;
+  hipError_t e = nvfp4::launch_gptq(w, n, k, hinv_u, amax_in, amax_out, tensor_scale, codes, scales,
+                                    m4_mask, workspace, ci, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gptq launch");
+  return NVFP4_OK;
+}
+
 NVFP4_API int nvfp4_tensor_amax(const float* w, int64_t n, int64_t k, float* amax_out, void* stream) {
   g_last_error.clear();
   if (n < 0 || k < 0) return fail(NVFP4_ERR_INVALID_VALUE, "negative dimension");

@@ -62,6 +62,14 @@ hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scal
                         int out_f32, const TiledPlan& plan, void* workspace, int impl,
                         hipStream_t stream);
 
+// GPTQ inside FourOverSix scales (k % 64 == 0): workspace of
+// gptq_workspace_bytes(n, k) (working copy of w, one panel of errors).
+size_t gptq_workspace_bytes(int64_t n, int64_t k);
+hipError_t launch_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u,
+                       const float* amax_in, float* amax_out, float* tensor_scale,
+                       uint8_t* codes, uint8_t* scales, uint8_t* m4_mask, void* workspace,
+                       int impl, hipStream_t stream);
+
 hipError_t launch_selftest_cvt(uint32_t* counters, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -137,6 +137,37 @@ NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const 
                                     uint8_t* scales, uint8_t* m4_mask, int impl, void* stream);
 
 /*
+ * nvfp4_quantize_fos_gptq - FourOverSix block scales fixed first, then GPTQ's
+ * error-compensating column updates inside them ([Notes07] section 03 "How we
+ * integrated it": scale estimation and the M=6 / M=4 choice, then the GPTQ
+ * iterations; GPTQ is the published method of Frantar et al., 2022).
+ *
+ * Step 1 is nvfp4_quantize_fos on w (amax_in / amax_out / tensor_scale /
+ * scales / m4_mask as there).  Step 2 quantizes the columns of a working
+ * copy of w in order, with each block's fixed scale (the quantizer's C5-C7),
+ * and after column j subtracts e_j * U[j, l] from every later column l,
+ * e_j = (w_j - w_hat_j) / U[j, j]; codes receives the result.  Each element
+ * gets its updates in increasing j, one fp32 product and one fp32
+ * subtraction each, so the result is exactly reproducible.
+ *
+ * hinv_u     device fp32 [k, k] row-major: the upper Cholesky factor U of
+ *            the inverse Hessian (H^-1 = U^T U; H from calibration
+ *            activations X, e.g. 2 X^T X plus damping); only the upper
+ *            triangle is read; diagonal > 0.
+ * workspace  device buffer of >= nvfp4_quantize_fos_gptq_workspace_size(n, k)
+ *            bytes, 16-byte aligned (working copy of w and one panel of
+ *            errors); contents on entry do not matter.
+ * k % 64 == 0 (columns are processed 64 at a time); other arguments as
+ * nvfp4_quantize_fos.  Launches: the quantizer, a copy, then 2 kernels per 64
+ * columns.
+ */
+NVFP4_API size_t nvfp4_quantize_fos_gptq_workspace_size(int64_t n, int64_t k);
+NVFP4_API int nvfp4_quantize_fos_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u,
+                                      const float* amax_in, float* amax_out, float* tensor_scale,
+                                      uint8_t* codes, uint8_t* scales, uint8_t* m4_mask,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_dequant - W_hat from the packed format ([Notes07] section 02:
  * "dequant" of a block with its scale).
  *

@@ -47,11 +47,21 @@ F32 = np.float32
 def hessian_factor(x, damp: float = 0.01) -> np.ndarray:
     """U (fp32, upper triangular) with H^-1 = U^T U, H = 2 X^T X + damp *
     mean(diag) * I, from calibration activations x [s, k], computed in float64
-    (GPTQ's damped Hessian; the damping keeps H positive definite)."""
+    (GPTQ's damped Hessian; the damping keeps H positive definite).  H^-1
+    comes from H's own Cholesky factor (LAPACK potrf, then potri), the usual
+    route for a symmetric positive definite inverse."""
+    from scipy.linalg import lapack
+
     x = np.asarray(x, dtype=np.float64)
     h = 2.0 * (x.T @ x)
     h[np.diag_indices_from(h)] += damp * float(np.mean(np.diag(h)))
-    hinv = np.linalg.inv(h)
+    c, info = lapack.dpotrf(h, lower=True)
+    if info != 0:
+        raise np.linalg.LinAlgError(f"H is not positive definite (potrf info {info})")
+    hinv, info = lapack.dpotri(c, lower=True)  # lower triangle of H^-1
+    if info != 0:
+        raise np.linalg.LinAlgError(f"potri info {info}")
+    hinv = np.tril(hinv) + np.tril(hinv, -1).T
     lower = np.linalg.cholesky(hinv)  # hinv = L L^T
     return np.ascontiguousarray(lower.T).astype(F32)  # U = L^T: hinv = U^T U
 

@@ -49,6 +49,15 @@ def activations(m: int, k: int, seed: int) -> torch.Tensor:
     return torch.from_numpy(x).to(torch.bfloat16)
 
 
+def calibration_activations(s: int, k: int, seed: int) -> np.ndarray:
+    """float64 [s, k] calibration inputs: N(0, 1) draws with a per-channel
+    scale drawn from U(1, 2), so the Hessian X^T X is far from diagonal in
+    relative terms (uneven channel energies, random correlations)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((s, k))
+    return x * (1.0 + rng.random(k))
+
+
 def tiny(seed: int = 0):
     """256 x 256 weights ~ 0.02 N(0,1) and one activation row, one generator."""
     rng = np.random.default_rng(seed)

@@ -61,6 +61,25 @@ def test_quantize_rejects_bad_arguments_on_host(L):
     assert L.nvfp4_quantize_fos_ex(FAKE, 4, 32, None, FAKE, FAKE, FAKE, FAKE, None, 7, None) == 1
 
 
+def test_gptq_rejects_bad_arguments_on_host(L):
+    g = L.nvfp4_quantize_fos_gptq
+    ws = L.nvfp4_quantize_fos_gptq_workspace_size(4, 128)
+    assert ws == 4 * 128 * 4 + 4 * 64 * 4
+    assert L.nvfp4_quantize_fos_gptq_workspace_size(-1, 128) == 0
+    assert L.nvfp4_quantize_fos_gptq_workspace_size(0, 128) == 0
+    args = lambda **kw: [kw.get("w", FAKE), kw.get("n", 4), kw.get("k", 128), kw.get("u", FAKE), None,
+                         FAKE, FAKE, FAKE, FAKE, None, kw.get("wsp", FAKE), kw.get("wsb", ws), None]
+    assert g(*args(k=96)) == 2  # k % 64
+    assert "k % 64" in L.nvfp4_last_error().decode()
+    assert g(*args(k=24)) == 2  # k % 16 first
+    assert g(*args(u=None)) == 1
+    assert g(*args(w=None)) == 1
+    assert g(*args(u=ODD)) == 3
+    assert g(*args(wsb=ws - 1)) == 4
+    assert g(*args(wsp=None)) == 1
+    assert g(*args(wsp=ODD)) == 3
+
+
 def test_gemm_rejects_bad_arguments_on_host(L):
     g = L.nvfp4_w4a16_gemm_ex
     args = lambda m, n, k, **kw: dict(dict(x=FAKE, c=FAKE, s=FAKE, t=FAKE, y=FAKE, m=m, n=n, k=k, dt=0,
