@@ -158,8 +158,8 @@ NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const 
  *            bytes, 16-byte aligned (working copy of w and one panel of
  *            errors); contents on entry do not matter.
  * k % 64 == 0 (columns are processed 64 at a time); other arguments as
- * nvfp4_quantize_fos.  Launches: the quantizer, a copy, then 2 kernels per 64
- * columns.
+ * nvfp4_quantize_fos.  Launches: the quantizer, then per 64 columns a panel
+ * kernel and (except after the last panel) a trailing-update kernel.
  */
 NVFP4_API size_t nvfp4_quantize_fos_gptq_workspace_size(int64_t n, int64_t k);
 NVFP4_API int nvfp4_quantize_fos_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u,
