@@ -400,10 +400,15 @@ def decoder_shapes(args, stream, time_op, w_dev):
         del qs, ws
         torch.cuda.empty_cache()
 
+    out["w4a4"] = {"note": "activations quantized to NVFP4 (amax pass + quantization kernel writing codes, "
+                           "scales and block-scaled bf16 values), then the bf16-MFMA GEMM; tflops over the "
+                           "whole call against the bf16 MFMA peak",
+                   "shapes": {}}
     for name, n, k in LARGE_SHAPES:
         qs = copies(n, k, 4)
         ws = torch.empty(max(16, max(nv.workspace_size(m, n, k) for m in LARGE_M)), dtype=torch.uint8, device=dev)
-        res = {}
+        ws4 = torch.empty(max(nv.w4a4_workspace_size(m, n, k) for m in LARGE_M), dtype=torch.uint8, device=dev)
+        res, res4 = {}, {}
         for m in LARGE_M:
             x = synth.activations(m, k, synth.activation_seed(m)).to(dev)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -412,8 +417,19 @@ def decoder_shapes(args, stream, time_op, w_dev):
             tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
             res[m] = {"us": round(us, 3), "tflops": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                       "path": "skinny" if nv.gemm_path(m, n, k) == nv.PATH_SKINNY else "tiled"}
+            us4 = time_op(lambda r: nv.w4a4_gemm(x, qs[r % 4], out=y, workspace=ws4), launches)
+            act = nv.quantize_act(x)
+            usq = time_op(lambda r: nv.quantize_act(x, out=act), launches)
+            tf4 = 2.0 * m * n * k / (us4 * 1e-6) / 1e12
+            qbytes = m * k * (2 + 2 + 2 + 0.5 + 1 / 16)  # amax read, read, bf16 + codes + scales written
+            res4[m] = {"us": round(us4, 3), "tflops": round(tf4, 1),
+                       "frac_mfma_bf16": round(tf4 / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "act_quant_us": round(usq, 3),
+                       "act_quant_gbs": round(qbytes / (usq * 1e-6) / 1e9, 1)}
+            del act
         out["large_m"][f"{name}_n{n}_k{k}"] = res
-        del qs, ws
+        out["w4a4"]["shapes"][f"{name}_n{n}_k{k}"] = res4
+        del qs, ws, ws4
         torch.cuda.empty_cache()
     return out
 

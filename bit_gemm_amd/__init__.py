@@ -60,6 +60,9 @@ SIGNATURES = {
     "nvfp4_w4a16_gemm_ex": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size,
                                      _c_int, _c_int, _c_int, _c_p]),
     "nvfp4_w4a16_gemm_path": (_c_int, [_c_i64, _c_i64, _c_i64]),
+    "nvfp4_quantize_act": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
+    "nvfp4_w4a4_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "nvfp4_w4a4_gemm": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size, _c_p]),
     "nvfp4_selftest_cvt": (_c_int, [_c_p, _c_p]),
     "nvfp4_status_string": (ctypes.c_char_p, [_c_int]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
@@ -237,6 +240,68 @@ def w4a16_gemm(x: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.b
     _check(lib().nvfp4_w4a16_gemm_ex(
         _ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), m, n, k, code,
         _ptr(workspace), ws_bytes, path, split_k, impl, _stream(dev)))
+    return out
+
+
+@dataclass
+class NVFP4Act:
+    """NVFP4 activations [m, k] (standard block scale) and, optionally, their
+    block-scaled bf16 values val * sigma."""
+
+    codes: torch.Tensor  # uint8 [m, k/2]
+    scales: torch.Tensor  # uint8 [m, k/16]
+    tensor_scale: torch.Tensor  # float32 [1]
+    amax: torch.Tensor  # float32 [1]
+    blockscaled: Optional[torch.Tensor]  # bf16 [m, k] or None
+
+
+def quantize_act(x: torch.Tensor, amax: Optional[torch.Tensor] = None, with_blockscaled: bool = True,
+                 out: Optional[NVFP4Act] = None) -> NVFP4Act:
+    """NVFP4 quantization of bf16 [m, k] GPU activations (W4A4 input side)."""
+    _need_gpu(x, "x", torch.bfloat16)
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
+    m, k = x.shape
+    dev = x.device
+    out = out if out is not None else NVFP4Act(
+        codes=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+        scales=torch.empty((m, k // 16), dtype=torch.uint8, device=dev),
+        tensor_scale=torch.empty(1, dtype=torch.float32, device=dev),
+        amax=torch.empty(1, dtype=torch.float32, device=dev),
+        blockscaled=torch.empty((m, k), dtype=torch.bfloat16, device=dev) if with_blockscaled else None,
+    )
+    if amax is not None:
+        _need_gpu(amax, "amax", torch.float32)
+    _check(lib().nvfp4_quantize_act(_ptr(x), m, k, _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale),
+                                    _ptr(out.codes), _ptr(out.scales), _ptr(out.blockscaled), _stream(dev)))
+    return out
+
+
+def w4a4_workspace_size(m: int, n: int, k: int) -> int:
+    return int(lib().nvfp4_w4a4_gemm_workspace_size(m, n, k))
+
+
+def w4a4_gemm(x: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.bfloat16,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = NVFP4(x) @ W_hat^T for bf16 [m, k] activations (W4A4)."""
+    _need_gpu(x, "x", torch.bfloat16)
+    m, k = x.shape
+    n, kw = q.shape
+    if kw != k:
+        raise ValueError(f"x has k={k}, weights k={kw}")
+    code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    _need_gpu(out, "out", out_dtype)
+    need = w4a4_workspace_size(m, n, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256) + 256, dtype=torch.uint8, device=x.device)
+    ws = workspace
+    off = (-ws.data_ptr()) % 256  # the workspace must be 256-byte aligned
+    if off:
+        ws = ws[off:]
+    _check(lib().nvfp4_w4a4_gemm(_ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), m, n, k,
+                                 code, _ptr(ws), ws.numel(), _stream(x.device)))
     return out
 
 

@@ -308,6 +308,82 @@ NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_
                              workspace_bytes, NVFP4_PATH_AUTO, 0, NVFP4_IMPL_DEFAULT, stream);
 }
 
+NVFP4_API int nvfp4_quantize_act(const void* x, int64_t m, int64_t k, const float* amax_in,
+                                 float* amax_out, float* tensor_scale, uint8_t* codes,
+                                 uint8_t* scales, void* x_blockscaled, void* stream) {
+  g_last_error.clear();
+  int st = check_nk(m, k);
+  if (st) return st;
+  const bool empty = (m == 0 || k == 0);
+  if (!amax_out || !tensor_scale) return fail(NVFP4_ERR_INVALID_VALUE, "amax_out and tensor_scale are required");
+  if (!empty && (!x || !codes || !scales)) return fail(NVFP4_ERR_INVALID_VALUE, "x, codes and scales are required");
+  if (!aligned(amax_out, 4) || !aligned(tensor_scale, 4) || (amax_in && !aligned(amax_in, 4)))
+    return fail(NVFP4_ERR_MISALIGNED, "scalar arguments must be 4-byte aligned");
+  if (!empty && (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16) ||
+                 (x_blockscaled && !aligned(x_blockscaled, 16))))
+    return fail(NVFP4_ERR_MISALIGNED, "x, codes, scales and x_blockscaled must be 16-byte aligned");
+  if ((st = check_device())) return st;
+  hipError_t e = nvfp4::launch_quantize_act(static_cast<const uint16_t*>(x), m, k, amax_in, amax_out,
+                                            tensor_scale, codes, scales, static_cast<uint16_t*>(x_blockscaled),
+                                            nullptr, nullptr, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "quantize_act launch");
+  return NVFP4_OK;
+}
+
+// W4A4 workspace: 256 bytes of scalars (amax, activation tensor scale, the
+// product of both tensor scales), the block-scaled bf16 activations, their
+// codes and scales, then the GEMM's own workspace; each piece 256-aligned.
+static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
+static size_t w4a4_act_bytes(int64_t m, int64_t k) {
+  const size_t e = (size_t)m * (size_t)k;
+  return 256 + round256(2 * e) + round256(e / 2) + round256(e / 16);
+}
+
+NVFP4_API size_t nvfp4_w4a4_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim ||
+      m > kMaxElems / k || m > kMaxElems / n)
+    return 0;
+  return w4a4_act_bytes(m, k) + nvfp4_w4a16_gemm_workspace_size(m, n, k);
+}
+
+NVFP4_API int nvfp4_w4a4_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
+                              const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                              int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (m < 0) return fail(NVFP4_ERR_INVALID_VALUE, "negative m=%lld", (long long)m);
+  if (m >= kMaxDim || (m > 0 && n > 0 && m > kMaxElems / n) || (m > 0 && k > 0 && m > kMaxElems / k))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "m=%lld too large", (long long)m);
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_F32)
+    return fail(NVFP4_ERR_INVALID_VALUE, "out_dtype %d", out_dtype);
+  if (m == 0 || n == 0) return NVFP4_OK;
+  if (!y || !tensor_scale) return fail(NVFP4_ERR_INVALID_VALUE, "y and tensor_scale are required");
+  if (k > 0 && (!x || !codes || !scales)) return fail(NVFP4_ERR_INVALID_VALUE, "x, codes and scales are required");
+  if (!aligned(y, 16) || !aligned(tensor_scale, 4) || (k > 0 && (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16))))
+    return fail(NVFP4_ERR_MISALIGNED, "x, codes, scales, y must be 16-byte aligned");
+  if (k == 0) return nvfp4_w4a16_gemm(x, codes, scales, tensor_scale, y, m, n, k, out_dtype, nullptr, 0, stream);
+  const size_t act = w4a4_act_bytes(m, k);
+  const size_t gws = nvfp4_w4a16_gemm_workspace_size(m, n, k);
+  if (workspace_bytes < act + gws)
+    return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, act + gws);
+  if (!workspace) return fail(NVFP4_ERR_INVALID_VALUE, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if ((st = check_device())) return st;
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  float* sc = reinterpret_cast<float*>(base);  // [0] amax, [1] s_t of x, [2] product of tensor scales
+  const size_t e = (size_t)m * (size_t)k;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(base + 256);
+  uint8_t* xc = base + 256 + round256(2 * e);
+  uint8_t* xsc = xc + round256(e / 2);
+  hipError_t he = nvfp4::launch_quantize_act(static_cast<const uint16_t*>(x), m, k, nullptr, sc, sc + 1, xc, xsc,
+                                             xs, tensor_scale, sc + 2, reinterpret_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "quantize_act launch");
+  // the bf16 MFMA GEMM of the block-scaled activations, scaled once by the
+  // product of both tensor scales
+  return nvfp4_w4a16_gemm(xs, codes, scales, sc + 2, y, m, n, k, out_dtype, base + act, gws, stream);
+}
+
 NVFP4_API int nvfp4_selftest_cvt(uint32_t* counters_out, void* stream) {
   g_last_error.clear();
   if (!counters_out) return fail(NVFP4_ERR_INVALID_VALUE, "counters_out is NULL");

@@ -62,6 +62,13 @@ hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scal
                         int out_f32, const TiledPlan& plan, void* workspace, int impl,
                         hipStream_t stream);
 
+// Activations (bf16 [m, k]) to NVFP4 with the standard block scale; xs
+// (optional) receives val * sigma as bf16; with comb_scale, also writes
+// s_t * w_scale[0] there.
+hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, const float* amax_in,
+                               float* amax_out, float* tensor_scale, uint8_t* codes,
+                               uint8_t* scales, uint16_t* xs, const float* w_scale,
+                               float* comb_scale, hipStream_t stream);
 // GPTQ inside FourOverSix scales (k % 64 == 0): workspace of
 // gptq_workspace_bytes(n, k) (working copy of w, one panel of errors).
 size_t gptq_workspace_bytes(int64_t n, int64_t k);

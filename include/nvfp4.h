@@ -249,6 +249,50 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
 NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);
 
 /*
+ * nvfp4_quantize_act - bf16 activations to NVFP4 for the W4A4 product
+ * ([Recap] section 1: above about 48 tokens the pages' GEMM takes NVFP4
+ * activations too).  The weights' format with the standard block scale (no
+ * FourOverSix choice): s_t = fl32(amax / 2688) (1 if 0) from the activations'
+ * own amax (or amax_in), sigma = E4M3_RNE(min(fl32(a / fl32(6 s_t)), 448))
+ * per 16 elements along k, codes = E2M1_RNE(fl32(|x| R)) with
+ * R = min(1 / fl32(sigma s_t), FLT_MAX) (0 for sigma = 0), sign bit from x.
+ *
+ * x              device bf16 [m, k] row-major, k % 16 == 0, 16-byte aligned.
+ * codes, scales  device outputs [m, k/2] and [m, k/16] as the weights'.
+ * x_blockscaled  optional device bf16 [m, k]: sign * val * sigma (exact in
+ *                bf16; the tensor scale not applied).
+ * amax_in, amax_out, tensor_scale: as nvfp4_quantize_fos.
+ * Launches: a zero fill and a max reduction (without amax_in), then one
+ * quantization kernel.  Bit-exact and deterministic.
+ */
+NVFP4_API int nvfp4_quantize_act(const void* x, int64_t m, int64_t k, const float* amax_in,
+                                 float* amax_out, float* tensor_scale, uint8_t* codes,
+                                 uint8_t* scales, void* x_blockscaled, void* stream);
+
+/*
+ * nvfp4_w4a4_gemm - y = xhat @ W_hat^T with xhat the NVFP4 quantization of
+ * the activations (nvfp4_quantize_act) and W_hat the packed weights
+ * ([Recap] section 1, the W4A4 path).
+ *
+ * gfx950's scaled FP4 matrix instructions take one power-of-two scale per
+ * 32 elements, so they cannot multiply NVFP4's E4M3 scale per 16 exactly;
+ * this entry point quantizes the activations, writes their block-scaled
+ * values (exact in bf16) to the workspace, and runs the W4A16 GEMM on them
+ * (path chosen as nvfp4_w4a16_gemm does) with the product of both tensor
+ * scales applied once in the epilogue.  Same accuracy contract as
+ * nvfp4_w4a16_gemm, against the W4A4 reference.
+ *
+ * Arguments as nvfp4_w4a16_gemm; workspace: device, 256-byte aligned, at
+ * least nvfp4_w4a4_gemm_workspace_size(m, n, k) bytes (activation scalars,
+ * block-scaled values, codes and scales, then the GEMM's workspace);
+ * caller-owned scratch; contents on entry do not matter.
+ */
+NVFP4_API size_t nvfp4_w4a4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
+NVFP4_API int nvfp4_w4a4_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
+                              const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                              int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_selftest_cvt - validation of the gfx950 FP4 and FP8 (E4M3)
  * conversion instructions against the library's portable ALU rounding and
  * decoding.

@@ -80,6 +80,26 @@ def test_gptq_rejects_bad_arguments_on_host(L):
     assert g(*args(wsp=ODD)) == 3
 
 
+def test_w4a4_rejects_bad_arguments_on_host(L):
+    qa = L.nvfp4_quantize_act
+    assert qa(FAKE, 4, 24, None, FAKE, FAKE, FAKE, FAKE, None, None) == 2  # k % 16
+    assert qa(None, 4, 32, None, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    assert qa(FAKE, 4, 32, None, FAKE, FAKE, FAKE, FAKE, ODD, None) == 3  # x_blockscaled
+    e = 8 * 64
+    act = 256 + 1024 + 256 + 256  # scalars, bf16 values, codes, scales (256-byte pieces)
+    assert L.nvfp4_w4a4_gemm_workspace_size(8, 32, 64) == act + L.nvfp4_w4a16_gemm_workspace_size(8, 32, 64)
+    assert L.nvfp4_w4a4_gemm_workspace_size(0, 32, 64) == 0
+    assert L.nvfp4_w4a4_gemm_workspace_size(8, 32, 24) == 0
+    ws = L.nvfp4_w4a4_gemm_workspace_size(8, 32, 64)
+    g = L.nvfp4_w4a4_gemm
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 0, FAKE, ws - 1, None) == 4
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 0, FAKE + 16, ws, None) == 3  # workspace alignment
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 5, FAKE, ws, None) == 1
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 24, 0, FAKE, ws, None) == 2
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 64, 0, None, 0, None) == 0  # empty: no work
+    assert e == 512
+
+
 def test_gemm_rejects_bad_arguments_on_host(L):
     g = L.nvfp4_w4a16_gemm_ex
     args = lambda m, n, k, **kw: dict(dict(x=FAKE, c=FAKE, s=FAKE, t=FAKE, y=FAKE, m=m, n=n, k=k, dt=0,
