@@ -452,8 +452,8 @@ def gptq_report(args, w_dev):
     Cholesky factor of the damped inverse Hessian) from seeded synthetic
     calibration activations (8192 x 4096, N(0,1) x per-channel U(1,2)),
     computed with torch.linalg in float64 outside the timed region; then the
-    average duration of whole calls (amax and quantizer kernels, 64 panel and
-    63 trailing-update kernels) with HIP events on the call's stream.
+    average duration of whole calls (amax and quantizer kernels, then one
+    kernel per 64 columns) with HIP events on the call's stream.
 
     The trailing updates bound it: each element w[r, l] receives one product
     and one subtraction per earlier column j < l, n k (k - 1) / 2 of each,
@@ -491,7 +491,7 @@ def gptq_report(args, w_dev):
     moved = float((q.codes != rtn.codes).to(torch.float32).mean().item())
     ops = 2 * n * k * (k - 1) // 2
     tops = ops / (ms * 1e-3) / 1e12
-    return {"n": n, "k": k, "ms_per_call": round(ms, 4), "launches": 3 + 2 * (k // 64) - 1,
+    return {"n": n, "k": k, "ms_per_call": round(ms, 4), "launches": 3 + k // 64,
             "update_ops": ops, "achieved_tops": round(tops, 2),
             "roofline": {"bound": "alu", "achieved": round(tops, 2), "peak": round(ALU_F32_OPS_PEAK_T, 2),
                          "unit": "T fp32 ops/s (mul, sub unfused)", "frac": round(tops / ALU_F32_OPS_PEAK_T, 4)},

@@ -70,7 +70,7 @@ hipError_t launch_quantize_act(const uint16_t* x, int64_t m, int64_t k, const fl
                                uint8_t* scales, uint16_t* xs, const float* w_scale,
                                float* comb_scale, hipStream_t stream);
 // GPTQ inside FourOverSix scales (k % 64 == 0): workspace of
-// gptq_workspace_bytes(n, k) (working copy of w, one panel of errors).
+// gptq_workspace_bytes(n, k) (working copy of w, two panels of errors).
 size_t gptq_workspace_bytes(int64_t n, int64_t k);
 hipError_t launch_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u,
                        const float* amax_in, float* amax_out, float* tensor_scale,

@@ -155,11 +155,11 @@ NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const 
  *            activations X, e.g. 2 X^T X plus damping); only the upper
  *            triangle is read; diagonal > 0.
  * workspace  device buffer of >= nvfp4_quantize_fos_gptq_workspace_size(n, k)
- *            bytes, 16-byte aligned (working copy of w and one panel of
+ *            bytes, 16-byte aligned (working copy of w and two panels of
  *            errors); contents on entry do not matter.
  * k % 64 == 0 (columns are processed 64 at a time); other arguments as
- * nvfp4_quantize_fos.  Launches: the quantizer, then per 64 columns a panel
- * kernel and (except after the last panel) a trailing-update kernel.
+ * nvfp4_quantize_fos.  Launches: the quantizer, then one kernel per 64
+ * columns (the panel and the previous panel's trailing update together).
  */
 NVFP4_API size_t nvfp4_quantize_fos_gptq_workspace_size(int64_t n, int64_t k);
 NVFP4_API int nvfp4_quantize_fos_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u,

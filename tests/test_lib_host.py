@@ -64,7 +64,7 @@ def test_quantize_rejects_bad_arguments_on_host(L):
 def test_gptq_rejects_bad_arguments_on_host(L):
     g = L.nvfp4_quantize_fos_gptq
     ws = L.nvfp4_quantize_fos_gptq_workspace_size(4, 128)
-    assert ws == 4 * 128 * 4 + 4 * 64 * 4
+    assert ws == 4 * 128 * 4 + 2 * 4 * 64 * 4  # working copy + two panels of errors
     assert L.nvfp4_quantize_fos_gptq_workspace_size(-1, 128) == 0
     assert L.nvfp4_quantize_fos_gptq_workspace_size(0, 128) == 0
     args = lambda **kw: [kw.get("w", FAKE), kw.get("n", 4), kw.get("k", 128), kw.get("u", FAKE), None,
