@@ -64,7 +64,9 @@ def parse_args(argv=None):
                     help="skip the per-shape GEMM report on the MLP and large-M decoder layers")
     ap.add_argument("--no-gptq", action="store_true", help="skip the GPTQ (FourOverSix scales) report")
     ap.add_argument("--gptq-only", action="store_true",
-                    help="only the GPTQ calls on the 4096x4096 layer (for rocprofv3 runs), then exit")
+                    help="only the GPTQ report (for rocprofv3 runs), then exit")
+    ap.add_argument("--gptq-shape", default=None,
+                    help="restrict the GPTQ report to one shape (w4096x4096, up_gate or down)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
     ap.add_argument("--eager", action="store_true",
                     help="launch the steps directly instead of from HIP graphs (for counter "
@@ -447,13 +449,18 @@ ALU_F32_OPS_PEAK_T = 256 * 4 * 16 * 2.4e9 / 1e12
 GPTQ_CALIB_SEED = 4242
 
 
+GPTQ_SHAPES = [("w4096x4096", 4096, 4096), ("up_gate", 14336, 4096), ("down", 4096, 14336)]
+
+
 def gptq_report(args, w_dev):
-    """GPTQ inside fixed FourOverSix scales on the 4096 x 4096 layer: U (upper
+    """GPTQ inside fixed FourOverSix scales on the decoder shapes: U (upper
     Cholesky factor of the damped inverse Hessian) from seeded synthetic
-    calibration activations (8192 x 4096, N(0,1) x per-channel U(1,2)),
-    computed with torch.linalg in float64 outside the timed region; then the
-    average duration of whole calls (amax and quantizer kernels, then one
-    kernel per 64 columns) with HIP events on the call's stream.
+    calibration activations (2k x k, N(0,1) x per-channel U(1,2)), computed
+    with torch.linalg in float64 outside the timed region; then the average
+    duration of whole calls (amax and quantizer kernels, then one kernel per
+    64 columns) with HIP events on the call's stream.  The 4096 x 4096 layer
+    is the bench's own matrix; the MLP shapes tile it (the time does not
+    depend on the values).
 
     The trailing updates bound it: each element w[r, l] receives one product
     and one subtraction per earlier column j < l, n k (k - 1) / 2 of each,
@@ -464,38 +471,56 @@ def gptq_report(args, w_dev):
     import synth
 
     dev = w_dev.device
-    n, k = w_dev.shape
-    x = torch.from_numpy(synth.calibration_activations(2 * k, k, GPTQ_CALIB_SEED)).to(dev)
-    h = 2.0 * (x.T @ x)
-    del x
-    h += 0.01 * torch.mean(torch.diag(h)) * torch.eye(k, dtype=torch.float64, device=dev)
-    hinv = torch.cholesky_inverse(torch.linalg.cholesky(h))
-    u = torch.linalg.cholesky(hinv, upper=True).to(torch.float32).contiguous()
-    del h, hinv
-    ws = torch.empty(nv.gptq_workspace_size(n, k), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
-    q = None
-    for _ in range(2):
-        q = nv.quantize_fos_gptq(w_dev, u, workspace=ws)
-    torch.cuda.synchronize()
-    reps = 5
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(reps):
-        q = nv.quantize_fos_gptq(w_dev, u, workspace=ws)
-    ev1.record(stream)
-    ev1.synchronize()
-    ms = ev0.elapsed_time(ev1) / reps
-    rtn = nv.quantize_fos(w_dev)
-    torch.cuda.synchronize()
-    moved = float((q.codes != rtn.codes).to(torch.float32).mean().item())
-    ops = 2 * n * k * (k - 1) // 2
-    tops = ops / (ms * 1e-3) / 1e12
-    return {"n": n, "k": k, "ms_per_call": round(ms, 4), "launches": 3 + k // 64,
-            "update_ops": ops, "achieved_tops": round(tops, 2),
+    factors = {}
+
+    def factor(k):
+        if k not in factors:
+            x = torch.from_numpy(synth.calibration_activations(2 * k, k, GPTQ_CALIB_SEED)).to(dev)
+            h = 2.0 * (x.T @ x)
+            del x
+            h += 0.01 * torch.mean(torch.diag(h)) * torch.eye(k, dtype=torch.float64, device=dev)
+            hinv = torch.cholesky_inverse(torch.linalg.cholesky(h))
+            del h
+            factors[k] = torch.linalg.cholesky(hinv, upper=True).to(torch.float32).contiguous()
+            del hinv
+            torch.cuda.empty_cache()
+        return factors[k]
+
+    out = {}
+    for name, n, k in GPTQ_SHAPES:
+        if args.gptq_shape and name != args.gptq_shape:
+            continue
+        w = w_dev if (n, k) == tuple(w_dev.shape) else \
+            w_dev.repeat((n + N - 1) // N, (k + K - 1) // K)[:n, :k].contiguous()
+        u = factor(k)
+        ws = torch.empty(nv.gptq_workspace_size(n, k), dtype=torch.uint8, device=dev)
+        q = None
+        for _ in range(2):
+            q = nv.quantize_fos_gptq(w, u, workspace=ws)
+        torch.cuda.synchronize()
+        reps = 5 if k <= 4096 else 3
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            q = nv.quantize_fos_gptq(w, u, workspace=ws)
+        ev1.record(stream)
+        ev1.synchronize()
+        ms = ev0.elapsed_time(ev1) / reps
+        rtn = nv.quantize_fos(w)
+        torch.cuda.synchronize()
+        moved = float((q.codes != rtn.codes).to(torch.float32).mean().item())
+        ops = 2 * n * k * (k - 1) // 2
+        tops = ops / (ms * 1e-3) / 1e12
+        out[f"{name}_n{n}_k{k}"] = {
+            "n": n, "k": k, "ms_per_call": round(ms, 4), "launches": 3 + k // 64, "update_ops": ops,
+            "achieved_tops": round(tops, 2),
             "roofline": {"bound": "alu", "achieved": round(tops, 2), "peak": round(ALU_F32_OPS_PEAK_T, 2),
                          "unit": "T fp32 ops/s (mul, sub unfused)", "frac": round(tops / ALU_F32_OPS_PEAK_T, 4)},
             "code_bytes_changed_vs_rtn": round(moved, 4)}
+        del w, ws, q, rtn
+        torch.cuda.empty_cache()
+    return out
 
 
 def profile_large_m(w_dev):

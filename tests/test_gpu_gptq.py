@@ -130,3 +130,18 @@ def test_gptq_full_size_sampled_rows():
     assert np.array_equal(q.scales.cpu().numpy()[rows], r.scales)
     assert np.array_equal(q.m4_mask.cpu().numpy()[rows], r.m4_mask)
     assert q.tensor_scale.cpu().numpy()[0].view(np.uint32) == np.float32(r.tensor_scale).view(np.uint32)
+
+
+def test_gptq_many_panels_any_triangular_factor():
+    # 128 panels, rows that fill no panel workgroup.  Any upper-triangular U
+    # with a positive diagonal is a valid factor (U^T U is then SPD); a
+    # synthetic one avoids a 8192-channel Hessian inverse on the host.
+    n, k = 12, 8192
+    rng = np.random.default_rng(31)
+    w = synth.student_t_weights(n, k, 32)
+    u = np.triu(rng.standard_normal((k, k), dtype=np.float32) * np.float32(0.3 / np.sqrt(k)), 1)
+    u[np.diag_indices(k)] = (1.0 + 0.5 * rng.random(k)).astype(np.float32)
+    q = _run(w, u)
+    r = oracle.gptq_fos(w, u)
+    _assert_same(q, r, f"{n}x{k}")
+    assert not np.array_equal(r.codes, oracle.quantize_fos(w).codes)
