@@ -161,6 +161,9 @@ NVFP4_API int nvfp4_quantize_fos_gptq(const float* w, int64_t n, int64_t k, cons
   int st = check_nk(n, k);
   if (st) return st;
   if (k % 64 != 0) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k=%lld: GPTQ needs k %% 64 == 0", (long long)k);
+  // the largest launch (first trailing update) must stay below 2^32 work-items
+  if ((k / 64) * ((n + 63) / 64) + (n + 15) / 16 >= ((int64_t)1 << 24))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "n=%lld, k=%lld: too large for one GPTQ launch", (long long)n, (long long)k);
   const bool empty = (n == 0 || k == 0);
   if (!amax_out || !tensor_scale) return fail(NVFP4_ERR_INVALID_VALUE, "amax_out and tensor_scale are required");
   if (!empty && (!w || !codes || !scales || !hinv_u))

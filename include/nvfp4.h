@@ -157,7 +157,8 @@ NVFP4_API int nvfp4_quantize_fos_ex(const float* w, int64_t n, int64_t k, const 
  * workspace  device buffer of >= nvfp4_quantize_fos_gptq_workspace_size(n, k)
  *            bytes, 16-byte aligned (working copy of w and two panels of
  *            errors); contents on entry do not matter.
- * k % 64 == 0 (columns are processed 64 at a time); other arguments as
+ * k % 64 == 0 (columns are processed 64 at a time) and (k/64)(n/64) below
+ * 2^24 (one launch's grid; beyond HBM capacity anyway); other arguments as
  * nvfp4_quantize_fos.  Launches: the quantizer, then one kernel per 64
  * columns (the panel and the previous panel's trailing update together).
  */

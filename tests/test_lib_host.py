@@ -78,6 +78,7 @@ def test_gptq_rejects_bad_arguments_on_host(L):
     assert g(*args(wsb=ws - 1)) == 4
     assert g(*args(wsp=None)) == 1
     assert g(*args(wsp=ODD)) == 3
+    assert g(*args(n=1 << 20, k=1 << 16)) == 2  # launch grid beyond 2^32 work-items
 
 
 def test_w4a4_rejects_bad_arguments_on_host(L):
