@@ -95,6 +95,7 @@ int check_nk(int64_t n, int64_t k) {
 // skinny path keeps m <= 64.
 int choose_path(int64_t m, int64_t n, int64_t k, int path) {
   if (path != NVFP4_PATH_AUTO) return path;
+  if (n >= ((int64_t)1 << 27)) return NVFP4_PATH_TILED;  // beyond the skinny kernels' grid
   if (m <= 16) return NVFP4_PATH_SKINNY;
   if (m > 64) return NVFP4_PATH_TILED;
   // measured crossovers: the pipelined split-K skinny kernel is faster than
@@ -269,6 +270,10 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
   const int p = choose_path(m, n, k, path);
   if (p == NVFP4_PATH_SKINNY && m > 64)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "the skinny path takes m <= 64 (m=%lld)", (long long)m);
+  // a launch grid stays below 2^32 work-items: the skinny kernels run up to
+  // 512 threads per 16 weight rows
+  if (p == NVFP4_PATH_SKINNY && n >= ((int64_t)1 << 27))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "the skinny path takes n < 2^27 (n=%lld)", (long long)n);
   if (m == 0 || n == 0) return NVFP4_OK;
   if (!y || !tensor_scale) return fail(NVFP4_ERR_INVALID_VALUE, "y and tensor_scale are required");
   if (k > 0 && (!x || !codes || !scales)) return fail(NVFP4_ERR_INVALID_VALUE, "x, codes and scales are required");

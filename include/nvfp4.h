@@ -215,7 +215,9 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *     LDS by 64 weight rows, plus a reduction kernel, when m <= 48 and
  *     k % 128 == 0 (chunks of 512, pipelined), or when k % 64 != 0 or
  *     n * k <= 2^25; else the tiled kernel;
- *   m > 64 -> the tiled kernel.
+ *   m > 64 -> the tiled kernel;
+ *   n >= 2^27 -> the tiled kernel at any m (the skinny kernels' grid would
+ *     pass 2^32 work-items; forcing NVFP4_PATH_SKINNY there is an error).
  * The tiled kernel (bf16 MFMA): when k % 64 == 0, one 64-token tile x 256
  * (or, for k >= 8192, 128) weight rows for m <= 64, 128 x 128 tiles for
  * m <= 128, else 256 weight rows x 128 tokens with the weights dequantized

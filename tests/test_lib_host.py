@@ -135,6 +135,15 @@ def test_dequant_rejects_bad_arguments_on_host(L):
     assert d(None, None, None, None, 0, 32, 0, None) == 0  # empty: nothing to do
 
 
+def test_huge_row_counts_take_the_tiled_path(L):
+    # the skinny kernels' grid would pass 2^32 work-items from n = 2^27 rows
+    assert L.nvfp4_w4a16_gemm_path(1, 1 << 27, 16) == nv.PATH_TILED
+    assert L.nvfp4_w4a16_gemm_path(1, (1 << 27) - 1, 16) == nv.PATH_SKINNY
+    g = L.nvfp4_w4a16_gemm_ex
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1 << 27, 16, 0, None, 0, nv.PATH_SKINNY, 0, 0, None) == 2
+    assert "2^27" in L.nvfp4_last_error().decode()
+
+
 def test_dispatch_and_workspace_plan(L):
     S, T = nv.PATH_SKINNY, nv.PATH_TILED
     P = L.nvfp4_w4a16_gemm_path
