@@ -34,6 +34,9 @@ gptq    GPTQ column updates inside the FourOverSix scales (fixed first), the
         explicit inverse-Hessian form used to pin it.
 w4a4    Activation quantization to NVFP4 (standard M=6 block scale) and the
         float64 reference of the W4A4 product.
+qat     Quantization-aware training of a linear layer: forward on the FP4
+        weights, input gradient through the same weights, STE weight
+        gradient.
 
 Parity status: every function here is pinned by ``-m "not gpu"`` tests against
 something other than itself (the pages' printed value set, torch's
@@ -54,3 +57,4 @@ from .fos import quantize_fos, quantize_fos_scalar, FosResult, block_sse  # noqa
 from .gemm import dequant, dequant_f64, gemm_ref  # noqa: F401
 from .gptq import gptq_fos, gptq_fos_obs, hessian_factor  # noqa: F401
 from .w4a4 import ActResult, act_blockscaled, quantize_act, w4a4_gemm_ref  # noqa: F401
+from .qat import qat_forward, qat_input_grad, qat_weight_grad  # noqa: F401
