@@ -297,9 +297,17 @@ def main(argv=None):
     dominant = max(kernels, key=lambda k: kernels[k]["us"])
     dk = kernels[dominant]
     traffic = read_traffic_summary(dominant)
+    # streaming ceiling on this GPU: torch's device copy of the 64 MiB fp32
+    # matrix (cold rotating sources and destinations), read + write bytes
+    dsts = [torch.empty_like(src[0]) for _ in range(4)]
+    copy_bytes = 2 * src[0].numel() * 4
+    copy_us = time_op(lambda r: dsts[r % 4].copy_(src[r % ROT_SRC]), L)
+    copy_gbs = copy_bytes / (copy_us * 1e-6) / 1e9
+    del dsts
     roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(dk["gbs"], 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(dk["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": round(dk["us"], 3)}
+                "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": round(dk["us"], 3),
+                "stream_copy_gbs": round(copy_gbs, 1), "frac_of_stream_copy": round(dk["gbs"] / copy_gbs, 4)}
 
     gemm_w_bytes = sum(bytes_gemm_weights(N, K) for _ in M_LIST)
     gemm_us = sum(kernels[f"gemm_m{m}"]["us"] for m in M_LIST)
@@ -406,11 +414,14 @@ def decoder_shapes(args, stream, time_op, w_dev):
                            "scales and block-scaled bf16 values), then the bf16-MFMA GEMM; tflops over the "
                            "whole call against the bf16 MFMA peak",
                    "shapes": {}}
+    out["qat_input_grad"] = {"note": "dx = dy @ W_hat on the packed weights (the backward GEMM of "
+                                     "quantization-aware training); tflops against the bf16 MFMA peak",
+                             "shapes": {}}
     for name, n, k in LARGE_SHAPES:
         qs = copies(n, k, 4)
         ws = torch.empty(max(16, max(nv.workspace_size(m, n, k) for m in LARGE_M)), dtype=torch.uint8, device=dev)
         ws4 = torch.empty(max(nv.w4a4_workspace_size(m, n, k) for m in LARGE_M), dtype=torch.uint8, device=dev)
-        res, res4 = {}, {}
+        res, res4, resd = {}, {}, {}
         for m in LARGE_M:
             x = synth.activations(m, k, synth.activation_seed(m)).to(dev)
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
@@ -429,8 +440,18 @@ def decoder_shapes(args, stream, time_op, w_dev):
                        "act_quant_us": round(usq, 3),
                        "act_quant_gbs": round(qbytes / (usq * 1e-6) / 1e9, 1)}
             del act
+            # quantization-aware training's input gradient on the same
+            # weights: dx [m, k] = dy [m, n] @ W_hat
+            dy = synth.activations(m, n, synth.activation_seed(m) + 1).to(dev)
+            dxo = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+            usd = time_op(lambda r: nv.w4a16_gemm_dx(dy, qs[r % 4], out=dxo), launches)
+            tfd = 2.0 * m * n * k / (usd * 1e-6) / 1e12
+            resd[m] = {"us": round(usd, 3), "tflops": round(tfd, 1),
+                       "frac_mfma_bf16": round(tfd / MFMA_BF16_PEAK_TFLOPS, 4)}
+            del dy, dxo
         out["large_m"][f"{name}_n{n}_k{k}"] = res
         out["w4a4"]["shapes"][f"{name}_n{n}_k{k}"] = res4
+        out["qat_input_grad"]["shapes"][f"{name}_n{n}_k{k}"] = resd
         del qs, ws, ws4
         torch.cuda.empty_cache()
     return out

@@ -60,6 +60,9 @@ SIGNATURES = {
     "nvfp4_w4a16_gemm_ex": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size,
                                      _c_int, _c_int, _c_int, _c_p]),
     "nvfp4_w4a16_gemm_path": (_c_int, [_c_i64, _c_i64, _c_i64]),
+    "nvfp4_w4a16_gemm_dx_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
+    "nvfp4_w4a16_gemm_dx": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size,
+                                     _c_p]),
     "nvfp4_quantize_act": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "nvfp4_w4a4_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "nvfp4_w4a4_gemm": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size, _c_p]),
@@ -240,6 +243,34 @@ def w4a16_gemm(x: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.b
     _check(lib().nvfp4_w4a16_gemm_ex(
         _ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), m, n, k, code,
         _ptr(workspace), ws_bytes, path, split_k, impl, _stream(dev)))
+    return out
+
+
+def gemm_dx_workspace_size(m: int, n: int, k: int) -> int:
+    return int(lib().nvfp4_w4a16_gemm_dx_workspace_size(m, n, k))
+
+
+def w4a16_gemm_dx(dy: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.bfloat16,
+                  out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """dx = dy @ W_hat for bf16 [m, n] dy: the input gradient of the linear
+    layer y = x @ W_hat^T (quantization-aware training's backward pass)."""
+    _need_gpu(dy, "dy", torch.bfloat16)
+    if dy.dim() != 2:
+        raise ValueError("dy must be 2-D")
+    m, n = dy.shape
+    nw, k = q.shape
+    if nw != n:
+        raise ValueError(f"dy has n={n}, weights n={nw}")
+    code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
+    if out is None:
+        out = torch.empty((m, k), dtype=out_dtype, device=dy.device)
+    _need_gpu(out, "out", out_dtype)
+    need = gemm_dx_workspace_size(m, n, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+    _check(lib().nvfp4_w4a16_gemm_dx(_ptr(dy), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out),
+                                     m, n, k, code, _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                     _stream(dy.device)))
     return out
 
 

@@ -316,6 +316,43 @@ NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_
                              workspace_bytes, NVFP4_PATH_AUTO, 0, NVFP4_IMPL_DEFAULT, stream);
 }
 
+NVFP4_API size_t nvfp4_w4a16_gemm_dx_workspace_size(int64_t m, int64_t n, int64_t k) {
+  if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim ||
+      m > kMaxElems / k || n > kMaxElems / k)
+    return 0;
+  return nvfp4::plan_gemm_dx(m, n, k).ws_bytes;
+}
+
+NVFP4_API int nvfp4_w4a16_gemm_dx(const void* dy, const uint8_t* codes, const uint8_t* scales,
+                                  const float* tensor_scale, void* dx, int64_t m, int64_t n, int64_t k,
+                                  int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  int st = check_nk(n, k);
+  if (st) return st;
+  if (m < 0) return fail(NVFP4_ERR_INVALID_VALUE, "negative m=%lld", (long long)m);
+  if (m >= kMaxDim || (m > 0 && n > 0 && m > kMaxElems / n) || (m > 0 && k > 0 && m > kMaxElems / k))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "m=%lld too large", (long long)m);
+  if (out_dtype != NVFP4_BF16 && out_dtype != NVFP4_F32)
+    return fail(NVFP4_ERR_INVALID_VALUE, "out_dtype %d", out_dtype);
+  if (m == 0 || k == 0) return NVFP4_OK;
+  if (!dx || !tensor_scale) return fail(NVFP4_ERR_INVALID_VALUE, "dx and tensor_scale are required");
+  if (n > 0 && (!dy || !codes || !scales)) return fail(NVFP4_ERR_INVALID_VALUE, "dy, codes and scales are required");
+  if (!aligned(dx, 16) || !aligned(tensor_scale, 4) || (n > 0 && (!aligned(dy, 16) || !aligned(codes, 16) || !aligned(scales, 16))))
+    return fail(NVFP4_ERR_MISALIGNED, "dy, codes, scales, dx must be 16-byte aligned");
+  const nvfp4::DxPlan plan = nvfp4::plan_gemm_dx(m, n, k);
+  if (plan.ws_bytes > 0) {
+    if (workspace_bytes < plan.ws_bytes)
+      return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, plan.ws_bytes);
+    if (!workspace) return fail(NVFP4_ERR_INVALID_VALUE, "workspace is NULL");
+    if (!aligned(workspace, 16)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  }
+  if ((st = check_device())) return st;
+  hipError_t e = nvfp4::launch_gemm_dx(static_cast<const uint16_t*>(dy), codes, scales, tensor_scale, dx, m, n, k,
+                                       out_dtype == NVFP4_F32, plan, workspace, reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "gemm_dx launch");
+  return NVFP4_OK;
+}
+
 NVFP4_API int nvfp4_quantize_act(const void* x, int64_t m, int64_t k, const float* amax_in,
                                  float* amax_out, float* tensor_scale, uint8_t* codes,
                                  uint8_t* scales, void* x_blockscaled, void* stream) {

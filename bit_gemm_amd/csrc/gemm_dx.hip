@@ -1,0 +1,220 @@
+// Input-gradient GEMM of an NVFP4 linear layer on gfx950: dx = dy @ W_hat.
+//
+// "SOAR 2026 Recap: From Compute Limits to the Open-Source Ecosystem",
+// section "3. EAGLE-3 speculative decoding and hybrid architecture
+// adaptation", its "Draft training" part: quantization-aware training runs
+// the forward GEMM on the FP4 weights and passes gradients straight through
+// to the master weights.  The backward pass then needs dx = dy @ W_hat on the
+// same packed weights (the weight gradient dy^T x has no FP4 operand).
+//
+// Here the reduction runs over the weight rows n and the output over the
+// weight columns k, so a lane cannot read its MFMA operand straight from the
+// row-major packed layout: each 64-row step of the weights is dequantized
+// (hardware FP4 decode at unit scale, times sigma: exact in bf16) and stored
+// transposed in LDS, [k][n], beside the step's dy tile, [m][n]; both are then
+// read as v_mfma_f32_32x32x16_bf16 fragments (8 consecutive n per lane).
+// A workgroup covers 128 dy rows x 128 weight columns with 4 waves of 64 x 64
+// (2 x 2 MFMA tiles); the next step's global loads are in registers while
+// the current step's MFMAs run.  fp32 accumulation; s_t applied once.
+#include "launchers.h"
+#include "nvfp4_device.h"
+
+#pragma clang fp contract(off)
+
+namespace nvfp4 {
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+constexpr int kTM = 128;        // dy rows per workgroup
+constexpr int kTK = 128;        // weight columns (outputs) per workgroup
+constexpr int kTN = 64;         // weight rows (reduction) per step
+constexpr int kRow = kTN + 8;   // LDS row of 64 bf16 + 16 bytes of padding (bank spread, 16-byte aligned)
+
+// 8 codes of `d` (element i at bits 4i) times sigma, as 8 bf16 (exact).
+template <int J>
+__device__ __forceinline__ void decode2(uint32_t d, float sigma, float* v) {
+  const auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, J);  // byte J of d
+  v[2 * J] = p[0] * sigma;
+  v[2 * J + 1] = p[1] * sigma;
+}
+__device__ __forceinline__ void decode8(uint32_t d, float sigma, float* v) {
+  decode2<0>(d, sigma, v);
+  decode2<1>(d, sigma, v);
+  decode2<2>(d, sigma, v);
+  decode2<3>(d, sigma, v);
+}
+
+__device__ __forceinline__ uint32_t bf16_hi_exact(float f) { return __float_as_uint(f) >> 16; }
+
+struct DxLoads {
+  u32x4_t dy[4];     // this thread's 4 x 8 bf16 of dy
+  uint2 code[2];     // 16 codes of weight rows 2p and 2p+1, one block
+  uint32_t sc[2];    // their scale bytes
+};
+
+__global__ __launch_bounds__(256) void k_gemm_dx(const uint16_t* __restrict__ dy,
+                                                 const uint8_t* __restrict__ codes,
+                                                 const uint8_t* __restrict__ scales,
+                                                 const float* __restrict__ tensor_scale,
+                                                 void* __restrict__ dx, float* __restrict__ ws,
+                                                 int M, int N, int K, int steps_per, int out_f32) {
+  __shared__ __attribute__((aligned(16))) uint16_t as[kTM * kRow];  // dy[m][n]
+  __shared__ __attribute__((aligned(16))) uint16_t bs[kTK * kRow];  // W_hat[n][k] stored as [k][n]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k0 = blockIdx.x * kTK, m0 = blockIdx.y * kTM;
+  // this workgroup's share of the reduction: steps [s_begin, s_end) of 64 rows
+  const int s_begin = blockIdx.z * steps_per;
+  const int s_end = min((N + kTN - 1) / kTN, s_begin + steps_per);
+
+  // dy: thread -> tile row ar = tid / 2, n half ah = tid % 2 (4 pieces of 8)
+  const int ar = tid >> 1, ah = tid & 1;
+  const uint16_t* dyrow = dy + (int64_t)min(m0 + ar, M - 1) * N;  // rows past M: not stored
+  const bool vec = (N & 7) == 0;  // rows of dy are 16-byte aligned
+  // weights: thread -> row pair p = tid % 32 (rows 2p, 2p + 1), block kb = tid / 32
+  const int wp = tid & 31, kb = tid >> 5;
+  const int kcol = k0 + 16 * kb;  // first weight column of the block
+  const bool kin = kcol < K;      // K % 16 == 0: a block is all in or all out
+
+  auto load = [&](DxLoads& L, int s) {
+    const int n0 = s * kTN;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = n0 + 32 * ah + 8 * i;
+      if (vec && n + 8 <= N) {
+        L.dy[i] = *reinterpret_cast<const u32x4_t*>(dyrow + n);
+      } else {  // unaligned rows, or the ragged end of a row: zeros past N
+        uint32_t w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = n + 2 * e < N ? dyrow[n + 2 * e] : 0u;
+          const uint32_t hi = n + 2 * e + 1 < N ? dyrow[n + 2 * e + 1] : 0u;
+          w[e] = lo | (hi << 16);
+        }
+        L.dy[i] = u32x4_t{w[0], w[1], w[2], w[3]};
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int n = n0 + 2 * wp + r;
+      if (kin && n < N) {  // rows past N and blocks past K contribute zero
+        L.code[r] = *reinterpret_cast<const uint2*>(codes + (int64_t)n * (K / 2) + kcol / 2);
+        L.sc[r] = scales[(int64_t)n * (K / 16) + kcol / 16];
+      } else {
+        L.code[r] = make_uint2(0u, 0u);
+        L.sc[r] = 0u;
+      }
+    }
+  };
+  auto store = [&](const DxLoads& L) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(&as[ar * kRow + 32 * ah + 8 * i]) = L.dy[i];
+    // rows 2p and 2p + 1 of one block: 16 columns, each a bf16 pair (n, n + 1)
+    float v0[16], v1[16];
+    const float s0 = e4m3_decode(L.sc[0] & 0x7Fu), s1 = e4m3_decode(L.sc[1] & 0x7Fu);
+    decode8(L.code[0].x, s0, v0);
+    decode8(L.code[0].y, s0, v0 + 8);
+    decode8(L.code[1].x, s1, v1);
+    decode8(L.code[1].y, s1, v1 + 8);
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+      *reinterpret_cast<uint32_t*>(&bs[(16 * kb + c) * kRow + 2 * wp]) =
+          bf16_hi_exact(v0[c]) | (bf16_hi_exact(v1[c]) << 16);
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  // wave tile: dy rows 64 (wave / 2) .. +64, weight columns 64 (wave % 2) .. +64
+  const int wm = 64 * (wave >> 1), wk = 64 * (wave & 1);
+  const int r32 = lane & 31, h = lane >> 5;
+  DxLoads cur, nxt;
+  if (s_begin < s_end) load(cur, s_begin);
+  for (int s = s_begin; s < s_end; ++s) {
+    __syncthreads();  // the previous step's fragments have been read
+    store(cur);
+    if (s + 1 < s_end) load(nxt, s + 1);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kTN / 16; ++ks) {
+      bf16x8_t af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+        af[a] = *reinterpret_cast<const bf16x8_t*>(&as[(wm + 32 * a + r32) * kRow + 16 * ks + 8 * h]);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+        bf[b] = *reinterpret_cast<const bf16x8_t*>(&bs[(wk + 32 * b + r32) * kRow + 16 * ks + 8 * h]);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+    cur = nxt;
+  }
+
+  // D of a 32 x 32 tile: lane l, value v -> dy row 8 (v / 4) + 4 (l / 32) + v % 4,
+  // weight column l % 32.  With a split reduction: raw fp32 partials to
+  // plane z of the workspace (the reduction kernel applies s_t).
+  const bool partial = gridDim.z > 1;
+  float* plane = ws + (int64_t)blockIdx.z * M * K;
+  const float s_t = partial ? 1.0f : tensor_scale[0];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int k = k0 + wk + 32 * b + r32;
+      if (k >= K) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm + 32 * a + 8 * (v / 4) + 4 * h + (v % 4);
+        if (m >= M) continue;
+        const float o = acc[a][b][v] * s_t;
+        const int64_t idx = (int64_t)m * K + k;
+        if (partial)
+          plane[idx] = o;
+        else if (out_f32)
+          reinterpret_cast<float*>(dx)[idx] = o;
+        else
+          reinterpret_cast<uint16_t*>(dx)[idx] = (uint16_t)bf16_rne_bits(o);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+DxPlan plan_gemm_dx(int64_t m, int64_t n, int64_t k) {
+  DxPlan p{1, 0, 0};
+  const int64_t steps = (n + kTN - 1) / kTN;
+  const int64_t tiles = ((k + kTK - 1) / kTK) * ((m + kTM - 1) / kTM);
+  int splits = 1;
+  // split the reduction over workgroups until about 512 of them run, while
+  // each keeps at least 4 steps of 64 weight rows
+  while (tiles * splits * 2 <= 512 && steps / (splits * 2) >= 4) splits *= 2;
+  p.steps_per = (int)((steps + splits - 1) / splits);
+  p.splits = p.steps_per > 0 ? (int)((steps + p.steps_per - 1) / p.steps_per) : 1;
+  if (p.splits < 1) p.splits = 1;
+  p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)k * sizeof(float) : 0;
+  return p;
+}
+
+hipError_t launch_gemm_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* scales,
+                          const float* tensor_scale, void* dx, int64_t m, int64_t n, int64_t k,
+                          int out_f32, const DxPlan& p, void* workspace, hipStream_t stream) {
+  const dim3 grid((unsigned)((k + kTK - 1) / kTK), (unsigned)((m + kTM - 1) / kTM), (unsigned)p.splits);
+  float* ws = reinterpret_cast<float*>(workspace);
+  hipLaunchKernelGGL(k_gemm_dx, grid, dim3(256), 0, stream, dy, codes, scales, tensor_scale, dx, ws,
+                     (int)m, (int)n, (int)k, p.steps_per, out_f32);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_split_reduce(ws, tensor_scale, dx, m * k, p.splits, out_f32, stream);
+}
+
+}  // namespace nvfp4

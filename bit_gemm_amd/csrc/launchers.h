@@ -62,6 +62,19 @@ hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scal
                         int out_f32, const TiledPlan& plan, void* workspace, int impl,
                         hipStream_t stream);
 
+// dx[m, k] = s_t * sum_n dy[m, n] * (val * sigma)[n, k] (bf16 dy, packed W):
+// 128 x 128 output tiles, the reduction split over `splits` workgroups of
+// `steps_per` 64-row steps when tiles are few (fp32 partials [splits, m, k]
+// in the workspace, then the split reduction).
+struct DxPlan {
+  int splits;
+  int steps_per;
+  size_t ws_bytes;
+};
+DxPlan plan_gemm_dx(int64_t m, int64_t n, int64_t k);
+hipError_t launch_gemm_dx(const uint16_t* dy, const uint8_t* codes, const uint8_t* scales,
+                          const float* tensor_scale, void* dx, int64_t m, int64_t n, int64_t k,
+                          int out_f32, const DxPlan& p, void* workspace, hipStream_t stream);
 // Activations (bf16 [m, k]) to NVFP4 with the standard block scale; xs
 // (optional) receives val * sigma as bf16; with comb_scale, also writes
 // s_t * w_scale[0] there.

@@ -252,6 +252,33 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
 NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);
 
 /*
+ * nvfp4_w4a16_gemm_dx - input gradient of an NVFP4 linear layer,
+ * dx = dy @ W_hat, for quantization-aware training ([Recap] section 3,
+ * "Draft training": the forward GEMM runs on the FP4 weights and gradients
+ * pass straight through to the master weights; the weight gradient dy^T x
+ * has no FP4 operand and is the caller's plain GEMM).
+ *
+ * dx[i, j] = s_t * sum over r < n of dy[i, r] * (val * sigma)[r, j]:
+ * fp32 accumulation in any order, rounded once to out_dtype.
+ *
+ * dy         device bf16 [m, n] row-major (the forward output's gradient).
+ * codes, scales, tensor_scale: the packed [n, k] weights, as nvfp4_w4a16_gemm.
+ * dx         device [m, k] of out_dtype (NVFP4_BF16 or NVFP4_F32).
+ * workspace  device, >= nvfp4_w4a16_gemm_dx_workspace_size(m, n, k) bytes
+ *            (0 when the reduction is not split: NULL allowed), 16-byte
+ *            aligned; fp32 partial sums [splits, m, k] when few 128 x 128
+ *            output tiles leave the GPU idle (the reduction over n is then
+ *            split over workgroups and a second kernel adds the planes in
+ *            order).  Scratch; contents on entry do not matter.
+ * Any m, n; k % 16 == 0; pointers 16-byte aligned.  n == 0 writes zeros.
+ * Same accuracy contract as nvfp4_w4a16_gemm; deterministic.
+ */
+NVFP4_API size_t nvfp4_w4a16_gemm_dx_workspace_size(int64_t m, int64_t n, int64_t k);
+NVFP4_API int nvfp4_w4a16_gemm_dx(const void* dy, const uint8_t* codes, const uint8_t* scales,
+                                  const float* tensor_scale, void* dx, int64_t m, int64_t n, int64_t k,
+                                  int out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_quantize_act - bf16 activations to NVFP4 for the W4A4 product
  * ([Recap] section 1: above about 48 tokens the pages' GEMM takes NVFP4
  * activations too).  The weights' format with the standard block scale (no

@@ -101,6 +101,24 @@ def test_w4a4_rejects_bad_arguments_on_host(L):
     assert e == 512
 
 
+def test_gemm_dx_rejects_bad_arguments_on_host(L):
+    g = L.nvfp4_w4a16_gemm_dx
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 24, 0, None, 0, None) == 2  # k % 16
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 32, 0, None, 0, None) == 1
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 32, 3, None, 0, None) == 1  # out dtype
+    assert g(None, FAKE, FAKE, FAKE, FAKE, 4, 8, 32, 0, None, 0, None) == 1
+    assert g(ODD, FAKE, FAKE, FAKE, FAKE, 4, 8, 32, 0, None, 0, None) == 3
+    assert g(FAKE, FAKE, FAKE, FAKE, None, 4, 8, 32, 0, None, 0, None) == 1
+    assert g(None, None, None, FAKE, FAKE, 0, 8, 32, 0, None, 0, None) == 0  # m == 0: nothing to do
+    # few output tiles: the reduction over n is split (fp32 partial planes)
+    ws = L.nvfp4_w4a16_gemm_dx_workspace_size(64, 4096, 4096)
+    assert ws == 16 * 64 * 4096 * 4  # 32 tiles, 64 steps: 16 splits of 4 steps
+    assert L.nvfp4_w4a16_gemm_dx_workspace_size(4096, 4096, 4096) == 0  # 1024 tiles
+    assert L.nvfp4_w4a16_gemm_dx_workspace_size(64, 128, 4096) == 0  # 2 steps: nothing to split
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 4096, 0, FAKE, ws - 1, None) == 4
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 4096, 4096, 0, None, ws, None) == 1
+
+
 def test_gemm_rejects_bad_arguments_on_host(L):
     g = L.nvfp4_w4a16_gemm_ex
     args = lambda m, n, k, **kw: dict(dict(x=FAKE, c=FAKE, s=FAKE, t=FAKE, y=FAKE, m=m, n=n, k=k, dt=0,
