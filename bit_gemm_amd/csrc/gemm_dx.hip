@@ -14,8 +14,11 @@
 // transposed in LDS, [k][n], beside the step's dy tile, [m][n]; both are then
 // read as v_mfma_f32_32x32x16_bf16 fragments (8 consecutive n per lane).
 // A workgroup covers 128 dy rows x 128 weight columns with 4 waves of 64 x 64
-// (2 x 2 MFMA tiles); the next step's global loads are in registers while
-// the current step's MFMAs run.  fp32 accumulation; s_t applied once.
+// (2 x 2 MFMA tiles); two LDS stages: while step s's MFMAs read one stage,
+// the same waves then fill the other with step s + 1 (already in registers)
+// and issue step s + 2's global loads, one barrier per step.  When the tiles
+// are few the reduction over n is split over workgroups (fp32 partials, then
+// the split reduction).  fp32 accumulation; s_t applied once.
 #include "launchers.h"
 #include "nvfp4_device.h"
 
@@ -59,8 +62,9 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint16_t* __restrict__ dy
                                                  const float* __restrict__ tensor_scale,
                                                  void* __restrict__ dx, float* __restrict__ ws,
                                                  int M, int N, int K, int steps_per, int out_f32) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[kTM * kRow];  // dy[m][n]
-  __shared__ __attribute__((aligned(16))) uint16_t bs[kTK * kRow];  // W_hat[n][k] stored as [k][n]
+  // two stages of dy[m][n] and W_hat[n][k] stored as [k][n]
+  __shared__ __attribute__((aligned(16))) uint16_t as2[2][kTM * kRow];
+  __shared__ __attribute__((aligned(16))) uint16_t bs2[2][kTK * kRow];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = blockIdx.x * kTK, m0 = blockIdx.y * kTM;
   // this workgroup's share of the reduction: steps [s_begin, s_end) of 64 rows
@@ -106,7 +110,9 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint16_t* __restrict__ dy
       }
     }
   };
-  auto store = [&](const DxLoads& L) {
+  auto store = [&](const DxLoads& L, int st) {
+    uint16_t* as = as2[st];
+    uint16_t* bs = bs2[st];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<u32x4_t*>(&as[ar * kRow + 32 * ah + 8 * i]) = L.dy[i];
@@ -134,13 +140,17 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint16_t* __restrict__ dy
   // wave tile: dy rows 64 (wave / 2) .. +64, weight columns 64 (wave % 2) .. +64
   const int wm = 64 * (wave >> 1), wk = 64 * (wave & 1);
   const int r32 = lane & 31, h = lane >> 5;
-  DxLoads cur, nxt;
-  if (s_begin < s_end) load(cur, s_begin);
+  DxLoads cur;
+  if (s_begin < s_end) {
+    load(cur, s_begin);
+    store(cur, 0);
+    if (s_begin + 1 < s_end) load(cur, s_begin + 1);
+  }
+  __syncthreads();
   for (int s = s_begin; s < s_end; ++s) {
-    __syncthreads();  // the previous step's fragments have been read
-    store(cur);
-    if (s + 1 < s_end) load(nxt, s + 1);
-    __syncthreads();
+    const int st = (s - s_begin) & 1;
+    const uint16_t* as = as2[st];
+    const uint16_t* bs = bs2[st];
 #pragma unroll
     for (int ks = 0; ks < kTN / 16; ++ks) {
       bf16x8_t af[2], bf[2];
@@ -156,7 +166,11 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint16_t* __restrict__ dy
         for (int b = 0; b < 2; ++b)
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[b], acc[a][b], 0, 0, 0);
     }
-    cur = nxt;
+    // step s + 1 into the other stage (last read in step s - 1, before the
+    // barrier that ended it), then step s + 2's loads
+    if (s + 1 < s_end) store(cur, st ^ 1);
+    if (s + 2 < s_end) load(cur, s + 2);
+    __syncthreads();
   }
 
   // D of a 32 x 32 tile: lane l, value v -> dy row 8 (v / 4) + 4 (l / 32) + v % 4,
