@@ -74,3 +74,39 @@ def test_tiled_gemm_output_beyond_2e31_elements():
     one = oracle.gemm_ref(x[mi:mi + 1].cpu(), codes[ni:ni + 1].cpu().numpy(), scales[ni:ni + 1].cpu().numpy(),
                           np.float32(2.0 ** -9))
     assert abs(float(y[mi, ni].item()) - float(one[0, 0])) <= 1e-4 * max(1.0, abs(float(one[0, 0])))
+
+
+def test_activation_quantizer_beyond_2e31_elements():
+    # bf16 activations of 2.148e9 elements (4.3 GB): codes, scales and the
+    # block-scaled values on rows either side of element 2^31
+    m, k = 32784, 65536
+    g = torch.Generator(device="cuda").manual_seed(33)
+    x = torch.randn((m, k), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    a = nv.quantize_act(x)
+    amax = float(x.float().abs().max().item())
+    torch.cuda.synchronize()
+    assert float(a.amax.item()) == amax
+    rows = _rows_of_interest(m, k)
+    print("rows", rows, flush=True)
+    r = oracle.quantize_act(x[rows].cpu(), amax_in=amax)
+    assert np.array_equal(a.codes[rows].cpu().numpy(), r.codes)
+    assert np.array_equal(a.scales[rows].cpu().numpy(), r.scales)
+    assert np.array_equal(a.blockscaled[rows].float().cpu().numpy(), oracle.act_blockscaled(r))
+
+
+def test_input_grad_output_beyond_2e31_elements():
+    # dx = dy @ W_hat with 2.149e9 output elements (fp32, 8.6 GB)
+    m, n, k = 65552, 128, 32784
+    g = torch.Generator(device="cuda").manual_seed(34)
+    codes = torch.randint(0, 256, (n, k // 2), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    scales = torch.randint(0, 0x7F, (n, k // 16), generator=g, device="cuda", dtype=torch.int32).to(torch.uint8)
+    s_t = torch.tensor([2.0 ** -9], dtype=torch.float32, device="cuda")
+    q = nv.NVFP4Weight(codes, scales, s_t, s_t.clone(), None)
+    dy = (torch.randn((m, n), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    dx = nv.w4a16_gemm_dx(dy, q, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows_m = sorted({0, (1 << 31) // k, (1 << 31) // k + 1, m - 1})
+    cols = [0, 1, k // 2, k - 2, k - 1]
+    ref = oracle.qat_input_grad(dy[rows_m].cpu(), codes.cpu().numpy(), scales.cpu().numpy(), np.float32(2.0 ** -9))
+    got = dx[rows_m][:, cols].double().cpu().numpy()
+    assert np.linalg.norm(got - ref[:, cols]) / np.linalg.norm(ref[:, cols]) <= 1e-5
