@@ -241,7 +241,7 @@ hipError_t launch_quantize_fos(const float* w, int64_t n, int64_t k, const float
   const int64_t nchunks = (nblocks + 63) / 64;  // one 64-block chunk per wave
   int64_t grid = (nchunks + 3) / 4;
   if (grid < 1) grid = 1;  // also writes tensor_scale / amax_out for empty input
-  if (grid > 2048) grid = 2048;  // 8 workgroups per CU, grid-stride beyond
+  if (grid > 4096) grid = 4096;  // one 64-block chunk per wave up to 4096 x 4 chunks, grid-stride beyond
   if (impl == kConvHw)
     hipLaunchKernelGGL(k_fos<kConvHw>, dim3((unsigned)grid), dim3(256), 0, stream, w, nblocks,
                        amax_src, amax_out, tensor_scale, codes, scales, m4_mask);
