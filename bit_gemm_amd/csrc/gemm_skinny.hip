@@ -11,10 +11,14 @@
 //    of a group of K steps are in flight together and the next group is
 //    prefetched while the current one is consumed.
 //  * k_skinny_dot (m <= 2): the same layout with VALU dot products.
-//  * k_skinny + k_reduce (default for 16 < m <= 64, or any explicit
-//    split_k >= 1): 64 rows x one K chunk per workgroup with x staged in LDS
-//    in MFMA B-operand order (shared by the 4 waves), fp32 partials in the
-//    workspace, then a second kernel adds them in chunk order.  (A single
+//  * k_skinny_pipe + k_reduce (16 < m <= 32, or k % 1024 != 0; K % 128 == 0):
+//    64 rows x one K chunk of 512 per workgroup, x staged in LDS by DMA
+//    (shared by the 4 waves), fp32 partials in the workspace, then a second
+//    kernel adds them in chunk order; k_skinny (other K) the same without
+//    the step pipelining.
+//  * k_skinny_str + k_reduce (32 < m <= 64, K % 1024 == 0): one x chunk of
+//    1024 staged per workgroup, then hundreds of weight rows streamed
+//    through it 16 at a time (x read from L2 once per row group).  (A single
 //    launch in which the last workgroup of a tile adds the partials was
 //    measured slower here: the device-coherent stores and loads it needs
 //    cost more than the second launch.)
@@ -684,6 +688,158 @@ __global__ __launch_bounds__(256) void k_skinny_pipe(const uint16_t* __restrict_
   }
 }
 
+// Streaming split-K kernel (16 < m <= 64 on wide matrices): a workgroup
+// stages x[0:m, K chunk] in LDS once (plain loads, the pipelined kernel's
+// swizzled layout) and its 4 waves then stream `rows` weight rows through
+// it, 16 rows (one MFMA A tile) at a time, the next tile's codes and scales
+// in registers while the current one is multiplied.  With many rows per
+// workgroup the activations are read from L2 once per row group instead of
+// once per 64 rows.
+template <int NST>
+struct StrTile {
+  u32x4_t cw[NST];   // codes of step s: 32 codes of row r16 at k = 32 g
+  uint32_t sb[NST];  // their two scale bytes
+};
+
+// Issue the loads of steps S .. NST-1 (inline asm: counted by str_step's waits).
+template <int S, int NST>
+__device__ __forceinline__ void str_load(StrTile<NST>& T, const uint8_t* crow, const uint8_t* srow) {
+  load_b128_async<S * (kStepK / 2)>(T.cw[S], crow);
+  load_u16_async<S * (kStepK / 16)>(T.sb[S], srow);
+  if constexpr (S + 1 < NST) str_load<S + 1, NST>(T, crow, srow);
+}
+
+// Steps S .. NST-1 of one tile.  AFTER = loads issued after this tile's (the
+// next tile's 2 NST); stores issued in between only make the waits stricter.
+template <int S, int MT, int IMPL, int NST, int AFTER>
+__device__ __forceinline__ void str_step(StrTile<NST>& T, const uint8_t* lds, int g, int r16, f32x4_t* acc) {
+  wait_vm<2 * (NST - 1 - S) + AFTER>(T.cw[S], T.sb[S]);
+  const float sg0 = scale_at<IMPL, 0>(T.sb[S]), sg1 = scale_at<IMPL, 1>(T.sb[S]);
+  bf16x8_t a[4];
+  a[0] = dequant8<IMPL>(T.cw[S][0], sg0);
+  a[1] = dequant8<IMPL>(T.cw[S][1], sg0);
+  a[2] = dequant8<IMPL>(T.cw[S][2], sg1);
+  a[3] = dequant8<IMPL>(T.cw[S][3], sg1);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int off = S * 4096 * MT + 256 * (16 * mt + r16) + 16 * ((4 * g + j) ^ r16);
+      const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(lds + off);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, bv), acc[mt], 0, 0, 0);
+    }
+  }
+  asm volatile("" ::: "memory");  // one step's LDS reads at a time (register pressure)
+  if constexpr (S + 1 < NST) str_step<S + 1, MT, IMPL, NST, AFTER>(T, lds, g, r16, acc);
+}
+
+template <int MT, int IMPL, int NST>
+__global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__ x,
+                                                    const uint8_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ scales,
+                                                    const float* __restrict__ tensor_scale,
+                                                    void* __restrict__ y, float* __restrict__ ws, int M,
+                                                    int N, int K, int rows, int out_f32) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches
+  const int g = lane >> 4, r16 = lane & 15;
+  const int k0 = blockIdx.y * (NST * kStepK);
+  const int rg0 = blockIdx.x * rows;
+  // x chunk: step s = 16 MT token rows x 256 bytes, piece q of row r at slot
+  // q ^ (r % 16); rows >= M repeat row M - 1 (their outputs are not stored)
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int pp = tid + 256 * i, r = pp >> 4, q = pp & 15;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(r, M - 1) * K + k0 + kStepK * s + 8 * q);
+      *reinterpret_cast<u32x4_t*>(lds + s * 4096 * MT + 256 * r + 16 * (q ^ (r & 15))) = v;
+    }
+  }
+  __syncthreads();
+  const int ntiles = (min(rows, N - rg0) + 15) / 16;
+  const float s_t = tensor_scale[0];
+  const int64_t mn = (int64_t)M * N;
+  auto row_ptrs = [&](int t, const uint8_t*& cp, const uint8_t*& sp) {
+    const int row = min(rg0 + 16 * t + r16, N - 1);
+    cp = codes + (int64_t)row * (K / 2) + k0 / 2 + 16 * g;
+    sp = scales + (int64_t)row * (K / 16) + k0 / 16 + 2 * g;
+  };
+  auto finish = [&](int t, const f32x4_t* acc) {
+    const int nbase = rg0 + 16 * t + 4 * g;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = mt * 16 + r16;
+      if (m >= M) continue;
+      if (gridDim.y == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * s_t, out_f32);
+      } else {
+        float* dst = ws + blockIdx.y * mn + (int64_t)m * N + nbase;
+        if ((N & 3) == 0 && nbase + 3 < N) {
+          *reinterpret_cast<float4*>(dst) = float4{acc[mt][0], acc[mt][1], acc[mt][2], acc[mt][3]};
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (nbase + i < N) dst[i] = acc[mt][i];
+        }
+      }
+    }
+  };
+  // Every tile's loads are issued unconditionally (past the last tile the
+  // index is clamped: a redundant load of real data), so the code is
+  // straight-line between the loop's uniform branches and the waits the
+  // compiler counts let the next tile's loads stay in flight.
+  StrTile<NST> A, B;
+  const uint8_t *cp, *sp;
+  if (wave < ntiles) {
+    row_ptrs(wave, cp, sp);
+    str_load<0, NST>(A, cp, sp);
+  }
+  for (int t = wave; t < ntiles; t += 8) {
+    row_ptrs(min(t + 4, ntiles - 1), cp, sp);
+    str_load<0, NST>(B, cp, sp);
+    {
+      f32x4_t acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      str_step<0, MT, IMPL, NST, 2 * NST>(A, lds, g, r16, acc);
+      finish(t, acc);
+    }
+    if (t + 4 >= ntiles) {
+      wait_vm_all();  // the redundant loads of B land before the wave ends
+      break;
+    }
+    row_ptrs(min(t + 8, ntiles - 1), cp, sp);
+    str_load<0, NST>(A, cp, sp);
+    {
+      f32x4_t acc[MT];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      str_step<0, MT, IMPL, NST, 2 * NST>(B, lds, g, r16, acc);
+      finish(t + 4, acc);
+    }
+  }
+  wait_vm_all();
+}
+
+template <int MT, int IMPL, int NST>
+hipError_t launch_str(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
+                      const uint8_t* scales, const float* ts, void* y, float* ws, int M, int N, int K,
+                      int out_f32) {
+  const size_t lds = (size_t)NST * 4096 * MT;
+  hipError_t e = set_lds_limit<k_skinny_str<MT, IMPL, NST>>(lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((N + p.str_rows - 1) / p.str_rows), (unsigned)p.splits);
+  hipLaunchKernelGGL((k_skinny_str<MT, IMPL, NST>), grid, dim3(256), lds, stream, x, codes, scales, ts, y, ws,
+                     M, N, K, p.str_rows, out_f32);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.splits == 1) return e;
+  return launch_split_reduce(ws, ts, y, (int64_t)M * N, p.splits, out_f32, stream);
+}
+
 // y = s_t * sum over K chunks (in chunk order) of the fp32 partial sums;
 // four outputs per thread when m * n is a multiple of 4.  The planes are
 // loaded kRedBatch at a time (independent loads in flight together) and
@@ -821,6 +977,14 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
       }
     }
   }
+  if (p.str_rows > 0) {
+    if constexpr (K32 && MT >= 2) {
+      if (p.kchunk == 8 * kStepK)
+        return launch_str<MT, IMPL, 8>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
+      return launch_str<MT, IMPL, 4>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
+    }
+    return hipErrorInvalidValue;
+  }
   if (p.nks > 0) {
     if constexpr (K32) {
       switch (p.nks) {
@@ -899,6 +1063,24 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
     return p;
   }
   const int64_t tiles = (n + kRowsPerWg - 1) / kRowsPerWg;
+  if (forced_splits <= 0 && mt >= 3 && k % (8 * kStepK) == 0) {
+    // 32 < m <= 64: the streaming kernel, K chunks of 1024 and row groups
+    // sized so that about 256 workgroups run (one per CU).  Measured against
+    // the pipelined kernel: 14336 x 4096 / 4096 x 14336 / 4096 x 4096 at
+    // m = 48: 23.3 / 24.6 / 12.2 us against 26.8 / 28.1 / 12.8 us; at
+    // m = 17 .. 32 it is no faster (20.3 against 18.6 us at m = 17 on
+    // 14336 x 4096), so those keep the pipelined kernel.
+    const int64_t splits = k / (8 * kStepK);
+    int64_t groups = 256 / splits;
+    if (groups < 1) groups = 1;
+    const int64_t t16 = (n + 15) / 16;
+    const int64_t per = (t16 + groups - 1) / groups;
+    p.str_rows = (int)(16 * per);
+    p.kchunk = 8 * kStepK;
+    p.splits = (int)splits;
+    p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
+    return p;
+  }
   if (k > 0 && k % kStepK == 0) {
     // pipelined kernel: chunks of exactly NKS in {4, 8, 16} steps (NKS
     // dividing the K steps), the x chunk (NKS * MT KiB) within the LDS budget

@@ -32,6 +32,7 @@ struct SkinnyPlan {
   int steps_per_wave;
   int nks;
   size_t ws_bytes;
+  int str_rows;  // > 0: streaming kernel with row groups of str_rows rows
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits);
 hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* scales,

@@ -211,10 +211,15 @@ def test_dispatch_and_workspace_plan(L):
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
             ws = L.nvfp4_w4a16_gemm_workspace_size(m, n, k)
             assert ws == 0 or ((ws - C) % (4 * m * n) == 0 and ws <= 64 * 4 * m * n + C)
-    # k % 128 == 0: K chunks of 512 (4 steps of 128)
-    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 4096) == C + 8 * 4 * 48 * 4096
-    assert L.nvfp4_w4a16_gemm_workspace_size(48, 14336, 4096) == C + 8 * 4 * 48 * 14336
+    # 16 < m <= 32, k % 128 == 0: K chunks of 512 (4 steps of 128)
+    assert L.nvfp4_w4a16_gemm_workspace_size(32, 4096, 4096) == C + 8 * 4 * 32 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(32, 14336, 4096) == C + 8 * 4 * 32 * 14336
     assert L.nvfp4_w4a16_gemm_workspace_size(17, 4096, 14336) == C + 28 * 4 * 17 * 4096
+    # 32 < m <= 64, k % 1024 == 0: the streaming kernel, K chunks of 1024
+    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 4096) == C + 4 * 4 * 48 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(48, 14336, 4096) == C + 4 * 4 * 48 * 14336
+    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 14336) == C + 14 * 4 * 48 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(33, 65, 1536) == C + 3 * 4 * 33 * 65  # k % 1024 != 0: chunks of 512
     # explicit split K
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 2048, nv.PATH_SKINNY, 1) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 4) == C + 4 * 4 * 8 * 4096
