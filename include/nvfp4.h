@@ -212,8 +212,8 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *     weight rows over the whole K (except 8 < m <= 16 with n > 4096 and
  *     k % 512 == 0: the pipelined split-K kernel below);
  *   16 < m <= 64 -> split-K skinny kernel plus a reduction kernel, when
- *     m <= 48 and k % 128 == 0, or when k % 64 != 0 or n * k <= 2^25; else
- *     the tiled kernel.  Within it: for m > 32 and k % 1024 == 0 the
+ *     k % 1024 == 0, m <= 48 and k % 128 == 0, k % 64 != 0, or
+ *     n * k <= 2^25; else the tiled kernel.  Within it: for m > 32 and k % 1024 == 0 the
  *     streaming kernel (an x chunk of 1024 staged once per workgroup, then
  *     many 16-row weight tiles streamed through it); otherwise activations
  *     shared through LDS by 64 weight rows (chunks of 512, pipelined, when

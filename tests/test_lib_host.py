@@ -169,8 +169,9 @@ def test_dispatch_and_workspace_plan(L):
     assert P(48, 4096, 4096) == S and P(64, 4096, 4096) == S and P(65, 4096, 4096) == T
     # the pipelined skinny kernel up to m = 48 (k % 128 == 0), then the
     # tiled kernel on the larger shapes
-    assert P(17, 14336, 4096) == S and P(48, 14336, 4096) == S and P(49, 14336, 4096) == T
-    assert P(17, 4096, 14336) == S and P(48, 4096, 14336) == S and P(64, 4096, 14336) == T
+    assert P(17, 14336, 4096) == S and P(48, 14336, 4096) == S and P(64, 14336, 4096) == S
+    assert P(17, 4096, 14336) == S and P(48, 4096, 14336) == S and P(64, 4096, 14336) == S
+    assert P(49, 14336, 4608) == T  # k % 1024 != 0 (the streaming kernel needs it): tiled above 48
     assert P(48, 14336, 4160) == T  # k % 128 != 0, large: tiled
     assert P(48, 14336, 4112) == S and P(64, 4096, 4112) == S  # k % 64 != 0
     assert P(4096, 4096, 4096) == T
