@@ -709,10 +709,37 @@ __device__ __forceinline__ void str_load(StrTile<NST>& T, const uint8_t* crow, c
   if constexpr (S + 1 < NST) str_load<S + 1, NST>(T, crow, srow);
 }
 
+// B fragments of one K step: token tile mt, k piece j (4 g + j of the
+// step's 16), this lane's token row 16 mt + r16.
+template <int MT>
+struct StrB {
+  u32x4_t v[4][MT];
+};
+
+template <int S, int MT>
+__device__ __forceinline__ void str_read_b(StrB<MT>& B, const uint8_t* lds, int g, int r16) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      B.v[j][mt] = *reinterpret_cast<const u32x4_t*>(lds + S * 4096 * MT + 256 * (16 * mt + r16) +
+                                                    16 * ((4 * g + j) ^ r16));
+}
+
 // Steps S .. NST-1 of one tile.  AFTER = loads issued after this tile's (the
 // next tile's 2 NST); stores issued in between only make the waits stricter.
+// Step S + 1's B fragments are read from LDS into Bn before step S's MFMAs
+// (which use Bc), so the LDS latency is hidden behind them.  Except with 64
+// tokens and the portable conversion: there the second set of fragments
+// would not fit the architectural registers (the compiler would then copy
+// loaded registers before their wait), so each step reads its own.
 template <int S, int MT, int IMPL, int NST, int AFTER>
-__device__ __forceinline__ void str_step(StrTile<NST>& T, const uint8_t* lds, int g, int r16, f32x4_t* acc) {
+__device__ __forceinline__ void str_step(StrTile<NST>& T, const uint8_t* lds, int g, int r16, f32x4_t* acc,
+                                         StrB<MT>& Bc, StrB<MT>& Bn) {
+  constexpr bool kPf = !(MT >= 4 && IMPL == kConvPortable);
+  if constexpr (S == 0 && kPf) str_read_b<0, MT>(Bc, lds, g, r16);
+  if constexpr (kPf && S + 1 < NST) str_read_b<S + 1, MT>(Bn, lds, g, r16);
+  if constexpr (!kPf) str_read_b<S, MT>(Bc, lds, g, r16);
   wait_vm<2 * (NST - 1 - S) + AFTER>(T.cw[S], T.sb[S]);
   const float sg0 = scale_at<IMPL, 0>(T.sb[S]), sg1 = scale_at<IMPL, 1>(T.sb[S]);
   bf16x8_t a[4];
@@ -721,16 +748,11 @@ __device__ __forceinline__ void str_step(StrTile<NST>& T, const uint8_t* lds, in
   a[2] = dequant8<IMPL>(T.cw[S][2], sg1);
   a[3] = dequant8<IMPL>(T.cw[S][3], sg1);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int off = S * 4096 * MT + 256 * (16 * mt + r16) + 16 * ((4 * g + j) ^ r16);
-      const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(lds + off);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, bv), acc[mt], 0, 0, 0);
-    }
-  }
-  asm volatile("" ::: "memory");  // one step's LDS reads at a time (register pressure)
-  if constexpr (S + 1 < NST) str_step<S + 1, MT, IMPL, NST, AFTER>(T, lds, g, r16, acc);
+    for (int mt = 0; mt < MT; ++mt)
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, Bc.v[j][mt]), acc[mt], 0, 0, 0);
+  if constexpr (S + 1 < NST) str_step<S + 1, MT, IMPL, NST, AFTER>(T, lds, g, r16, acc, Bn, Bc);
 }
 
 template <int MT, int IMPL, int NST>
@@ -805,7 +827,8 @@ __global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__
       f32x4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      str_step<0, MT, IMPL, NST, 2 * NST>(A, lds, g, r16, acc);
+      StrB<MT> b0, b1;
+      str_step<0, MT, IMPL, NST, 2 * NST>(A, lds, g, r16, acc, b0, b1);
       finish(t, acc);
     }
     if (t + 4 >= ntiles) {
@@ -818,7 +841,8 @@ __global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__
       f32x4_t acc[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      str_step<0, MT, IMPL, NST, 2 * NST>(B, lds, g, r16, acc);
+      StrB<MT> b0, b1;
+      str_step<0, MT, IMPL, NST, 2 * NST>(B, lds, g, r16, acc, b0, b1);
       finish(t + 4, acc);
     }
   }
