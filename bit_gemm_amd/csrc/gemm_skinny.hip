@@ -6,17 +6,21 @@
 // the weights from HBM ("SOAR Weekly Champion Notes 08 ...", section "01").
 //
 // Kernels:
-//  * k_skinny_fk (default for 2 < m <= 16): a workgroup owns 16 weight rows
+//  * k_skinny_fk (2 < m <= 16, except 8 < m <= 16 on large matrices: more
+//    than 4096 rows or 2^25 weights, K % 512 == 0, which take the split-K
+//    kernels below): a workgroup owns 16 weight rows
 //    over the whole K and its waves split K; no workspace, one launch.  Loads
 //    of a group of K steps are in flight together and the next group is
 //    prefetched while the current one is consumed.
 //  * k_skinny_dot (m <= 2): the same layout with VALU dot products.
-//  * k_skinny_pipe + k_reduce (16 < m <= 32, or k % 1024 != 0; K % 128 == 0):
+//  * k_skinny_pipe + k_reduce (K % 128 == 0 but K % 1024 != 0: 16 < m <= 64,
+//    and 8 < m <= 16 on large matrices):
 //    64 rows x one K chunk of 512 per workgroup, x staged in LDS by DMA
 //    (shared by the 4 waves), fp32 partials in the workspace, then a second
 //    kernel adds them in chunk order; k_skinny (other K) the same without
 //    the step pipelining.
-//  * k_skinny_str + k_reduce (32 < m <= 64, K % 1024 == 0): one x chunk of
+//  * k_skinny_str + k_reduce (K % 1024 == 0: 16 < m <= 64, and 8 < m <= 16
+//    on large matrices): one x chunk of
 //    1024 staged per workgroup, then hundreds of weight rows streamed
 //    through it 16 at a time (x read from L2 once per row group).  (A single
 //    launch in which the last workgroup of a tile adds the partials was
@@ -1002,7 +1006,7 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
     }
   }
   if (p.str_rows > 0) {
-    if constexpr (K32 && MT >= 2) {
+    if constexpr (K32) {
       if (p.kchunk == 8 * kStepK)
         return launch_str<MT, IMPL, 8>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
       return launch_str<MT, IMPL, 4>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
@@ -1069,12 +1073,14 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   SkinnyPlan p{};
   const int mt = (int)((m + 15) / 16);
   const int64_t ksteps = (k + kStepK - 1) / kStepK;
-  // 8 < m <= 16 with more 16-row workgroups than CUs: the full-K kernel's
-  // 16-token build needs ~141 KiB of LDS per workgroup (one per CU), so its
-  // workgroups run in several serial rounds; the pipelined split-K kernel is
-  // faster there (14336 x 4096 at m = 12 / 16: 16.6 / 17.4 us against
-  // 20.5 / 20.6 us).
-  const bool pipe_small = forced_splits <= 0 && m > 8 && (n + 15) / 16 > 256 && k % 512 == 0;
+  // 8 < m <= 16 on large matrices (more 16-row workgroups than CUs, or more
+  // than 2^25 weights): the full-K kernel's 16-token build needs ~141 KiB of
+  // LDS per workgroup (one per CU), so its workgroups run in several serial
+  // rounds or few of them stream long rows; the split-K kernels are faster
+  // there (14336 x 4096 at m = 16: streaming 15.3, pipelined 17.4, full-K
+  // 20.6 us; 4096 x 14336 at m = 16: streaming 16.6, full-K 20.0 us).
+  const bool pipe_small = forced_splits <= 0 && m > 8 &&
+                          ((n + 15) / 16 > 256 || n * k > ((int64_t)1 << 25)) && k % 512 == 0;
   if (forced_splits <= 0 && mt == 1 && k > 0 && !pipe_small) {
     // full K per workgroup: one 512-wide slice per wave and round, up to 8
     // waves (longer K loops over rounds)
@@ -1087,13 +1093,14 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
     return p;
   }
   const int64_t tiles = (n + kRowsPerWg - 1) / kRowsPerWg;
-  if (forced_splits <= 0 && mt >= 3 && k % (8 * kStepK) == 0) {
-    // 32 < m <= 64: the streaming kernel, K chunks of 1024 and row groups
-    // sized so that about 256 workgroups run (one per CU).  Measured against
-    // the pipelined kernel: 14336 x 4096 / 4096 x 14336 / 4096 x 4096 at
-    // m = 48: 23.3 / 24.6 / 12.2 us against 26.8 / 28.1 / 12.8 us; at
-    // m = 17 .. 32 it is no faster (20.3 against 18.6 us at m = 17 on
-    // 14336 x 4096), so those keep the pipelined kernel.
+  if (forced_splits <= 0 && (mt >= 2 || pipe_small) && k % (8 * kStepK) == 0) {
+    // 16 < m <= 64 (and the large-matrix 8 < m <= 16 above): the streaming
+    // kernel, K chunks of 1024 and row groups sized so that about 256
+    // workgroups run (one per CU).  Measured against the pipelined kernel:
+    // 14336 x 4096 / 4096 x 14336 / 4096 x 4096 at m = 32: 17.5 / 19.3 /
+    // 10.0 us against 21.6 / 23.4 / 10.7 us; at m = 48: 21.0 / 22.3 / 11.4
+    // against 26.8 / 28.1 / 12.8 us (4096 x 4096 at m = 17: 9.6 against
+    // 9.4 us, the one case where it is not faster).
     const int64_t splits = k / (8 * kStepK);
     int64_t groups = 256 / splits;
     if (groups < 1) groups = 1;

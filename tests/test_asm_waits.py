@@ -32,7 +32,7 @@ def test_checker_flags_early_reads():
                     reason="hipcc not available")
 @pytest.mark.parametrize("source,pattern,minimum", [
     ("gemm_skinny.hip", r"k_skinny_pipe", 20),  # MT 1..4 x chunk lengths x 2 conversion implementations
-    ("gemm_skinny.hip", r"k_skinny_str", 4),     # streaming kernel: MT 3, 4 x 2 conversion implementations
+    ("gemm_skinny.hip", r"k_skinny_str", 16),    # streaming kernel: MT 1..4 x chunk lengths x 2 conversion implementations
     ("gemm_tiled.hip", r"k_lmr", 2),             # weights-in-registers large-M kernel, 2 implementations
 ])
 def test_counted_waits_cover_every_use(tmp_path, source, pattern, minimum):

@@ -88,9 +88,15 @@ PIPE_CASES = [
     (17, 200, 2048, 0), (32, 64, 2048, 2), (40, 1000, 2048, 0), (49, 130, 2048, 2), (64, 200, 2048, 0),
     (20, 100, 2048, 1), (1, 300, 2048, 4), (7, 64, 2048, 2), (16, 333, 2048, 1), (64, 64, 512, 0),
     (33, 65, 1536, 3), (45, 190, 2048, 2), (48, 4000, 128, 0),
-    # the streaming kernel (32 < m <= 64, k % 1024 == 0): ragged row groups
-    # and tiles, one K chunk, several chunks
+    # the streaming kernel (16 < m <= 64, k % 1024 == 0): ragged row groups
+    # and tiles, one K chunk, several chunks, one to four token tiles
     (33, 1001, 1024, 0), (48, 4000, 2048, 0), (64, 3000, 3072, 0), (40, 17, 1024, 0), (56, 5000, 4096, 0),
+    (17, 1001, 1024, 0), (32, 4100, 2048, 0), (24, 300, 3072, 0),
+    # 8 < m <= 16 on large matrices (more than 4096 rows): streaming kernel
+    # with one token tile (k % 1024 == 0), else the pipelined kernel
+    (9, 4097, 1024, 0), (16, 4200, 2048, 0), (12, 4100, 1536, 0),
+    # the pipelined kernel chosen automatically (k % 1024 != 0)
+    (24, 300, 1536, 0),
 ]
 
 

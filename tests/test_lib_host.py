@@ -203,8 +203,8 @@ def test_dispatch_and_workspace_plan(L):
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 1) == 0
     for m in (1, 8, 16):  # the full-K skinny kernel needs no workspace
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
-            if m > 8 and n > 4096:  # 8 < m <= 16 with > 256 row tiles: pipelined split-K
-                assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == (k // 512) * 4 * m * n
+            if m > 8 and (n > 4096 or n * k > 1 << 25):  # large matrices: streaming split-K (K chunks of 1024)
+                assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == (k // 1024) * 4 * m * n
             else:
                 assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0
     C = 0  # the workspace holds only the fp32 partials [splits, m, n]
@@ -212,15 +212,16 @@ def test_dispatch_and_workspace_plan(L):
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
             ws = L.nvfp4_w4a16_gemm_workspace_size(m, n, k)
             assert ws == 0 or ((ws - C) % (4 * m * n) == 0 and ws <= 64 * 4 * m * n + C)
-    # 16 < m <= 32, k % 128 == 0: K chunks of 512 (4 steps of 128)
-    assert L.nvfp4_w4a16_gemm_workspace_size(32, 4096, 4096) == C + 8 * 4 * 32 * 4096
-    assert L.nvfp4_w4a16_gemm_workspace_size(32, 14336, 4096) == C + 8 * 4 * 32 * 14336
-    assert L.nvfp4_w4a16_gemm_workspace_size(17, 4096, 14336) == C + 28 * 4 * 17 * 4096
-    # 32 < m <= 64, k % 1024 == 0: the streaming kernel, K chunks of 1024
+    # 16 < m <= 64, k % 1024 == 0: the streaming kernel, K chunks of 1024
+    assert L.nvfp4_w4a16_gemm_workspace_size(32, 4096, 4096) == C + 4 * 4 * 32 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(32, 14336, 4096) == C + 4 * 4 * 32 * 14336
+    assert L.nvfp4_w4a16_gemm_workspace_size(17, 4096, 14336) == C + 14 * 4 * 17 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 4096) == C + 4 * 4 * 48 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(48, 14336, 4096) == C + 4 * 4 * 48 * 14336
     assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 14336) == C + 14 * 4 * 48 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(33, 65, 1536) == C + 3 * 4 * 33 * 65  # k % 1024 != 0: chunks of 512
+    assert L.nvfp4_w4a16_gemm_workspace_size(17, 4096, 4608) == C + 9 * 4 * 17 * 4096  # pipelined, 9 chunks of 512
+    assert L.nvfp4_w4a16_gemm_workspace_size(12, 14336, 4608) == C + 9 * 4 * 12 * 14336  # pipelined, one token tile
     # explicit split K
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 2048, nv.PATH_SKINNY, 1) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 4) == C + 4 * 4 * 8 * 4096
