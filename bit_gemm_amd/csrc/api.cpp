@@ -104,7 +104,7 @@ int choose_path(int64_t m, int64_t n, int64_t k, int path) {
   if (m <= 48 && k % 128 == 0) return NVFP4_PATH_SKINNY;
   // 48 < m <= 64 with k % 1024 == 0: the streaming skinny kernel is faster
   // than the tiled kernel on every decoder shape (14336 x 4096 at m = 64:
-  // 27.1 against 31.7 us; 4096 x 14336: 28.5 against 31.4 us)
+  // 23.8 against 31.3 us; 4096 x 14336: 26.1 against 32.1 us)
   if (k % 1024 == 0) return NVFP4_PATH_SKINNY;
   if (k % 64 != 0 || n * k <= (int64_t(1) << 25)) return NVFP4_PATH_SKINNY;
   return NVFP4_PATH_TILED;
