@@ -693,7 +693,7 @@ __global__ __launch_bounds__(256) void k_skinny_pipe(const uint16_t* __restrict_
 }
 
 // Streaming split-K kernel (16 < m <= 64 on wide matrices): a workgroup
-// stages x[0:m, K chunk] in LDS once (plain loads, the pipelined kernel's
+// stages x[0:m, K chunk] in LDS once (LDS DMA, the pipelined kernel's
 // swizzled layout) and its 4 waves then stream `rows` weight rows through
 // it, 16 rows (one MFMA A tile) at a time, the next tile's codes and scales
 // in registers while the current one is multiplied.  With many rows per
@@ -772,26 +772,39 @@ __global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__
   const int g = lane >> 4, r16 = lane & 15;
   const int k0 = blockIdx.y * (NST * kStepK);
   const int rg0 = blockIdx.x * rows;
-  // x chunk: step s = 16 MT token rows x 256 bytes, piece q of row r at slot
-  // q ^ (r % 16); rows >= M repeat row M - 1 (their outputs are not stored)
-#pragma unroll
-  for (int s = 0; s < NST; ++s) {
-#pragma unroll
-    for (int i = 0; i < MT; ++i) {
-      const int pp = tid + 256 * i, r = pp >> 4, q = pp & 15;
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(x + (int64_t)min(r, M - 1) * K + k0 + kStepK * s + 8 * q);
-      *reinterpret_cast<u32x4_t*>(lds + s * 4096 * MT + 256 * r + 16 * (q ^ (r & 15))) = v;
-    }
-  }
-  __syncthreads();
   const int ntiles = (min(rows, N - rg0) + 15) / 16;
-  const float s_t = tensor_scale[0];
-  const int64_t mn = (int64_t)M * N;
   auto row_ptrs = [&](int t, const uint8_t*& cp, const uint8_t*& sp) {
     const int row = min(rg0 + 16 * t + r16, N - 1);
     cp = codes + (int64_t)row * (K / 2) + k0 / 2 + 16 * g;
     sp = scales + (int64_t)row * (K / 16) + k0 / 16 + 2 * g;
   };
+  // x chunk by LDS DMA, the pipelined kernel's layout: step s = 16 MT token
+  // rows x 256 bytes, piece q of row r at slot q ^ (r % 16); DMA instruction
+  // c (wave w issues c = w + 4 i) reads rows 4c .. 4c + 3 in whole cache
+  // lines.  Rows >= M repeat row M - 1 (their outputs are not stored).
+#pragma unroll
+  for (int s = 0; s < NST; ++s) {
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+      const int rr = 4 * (wave + 4 * i) + (lane >> 4);
+      copy16_to_lds(x + (int64_t)min(rr, M - 1) * K + k0 + kStepK * s + 8 * ((lane & 15) ^ (rr & 15)),
+                    lds + s * 4096 * MT + 1024 * (wave + 4 * i));
+    }
+  }
+  // then the first tile's weights (every wave issues them, clamped, so the
+  // count below is the same in every wave); waiting until only those are
+  // outstanding means this wave's copies have landed, and after the barrier
+  // every wave's have: the x latency overlaps the weights', and the first
+  // tile is still consumed step by step as its loads land
+  StrTile<NST> A, B;
+  const uint8_t *cp, *sp;
+  row_ptrs(min(wave, ntiles - 1), cp, sp);
+  str_load<0, NST>(A, cp, sp);
+  wait_vm<2 * NST>(A.cw[0], A.sb[0]);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+  const float s_t = tensor_scale[0];
+  const int64_t mn = (int64_t)M * N;
   auto finish = [&](int t, const f32x4_t* acc) {
     const int nbase = rg0 + 16 * t + 4 * g;
 #pragma unroll
@@ -818,12 +831,6 @@ __global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__
   // index is clamped: a redundant load of real data), so the code is
   // straight-line between the loop's uniform branches and the waits the
   // compiler counts let the next tile's loads stay in flight.
-  StrTile<NST> A, B;
-  const uint8_t *cp, *sp;
-  if (wave < ntiles) {
-    row_ptrs(wave, cp, sp);
-    str_load<0, NST>(A, cp, sp);
-  }
   for (int t = wave; t < ntiles; t += 8) {
     row_ptrs(min(t + 4, ntiles - 1), cp, sp);
     str_load<0, NST>(B, cp, sp);
