@@ -692,13 +692,13 @@ __global__ __launch_bounds__(256) void k_skinny_pipe(const uint16_t* __restrict_
   }
 }
 
-// Streaming split-K kernel (16 < m <= 64 on wide matrices): a workgroup
-// stages x[0:m, K chunk] in LDS once (LDS DMA, the pipelined kernel's
-// swizzled layout) and its 4 waves then stream `rows` weight rows through
-// it, 16 rows (one MFMA A tile) at a time, the next tile's codes and scales
-// in registers while the current one is multiplied.  With many rows per
-// workgroup the activations are read from L2 once per row group instead of
-// once per 64 rows.
+// Streaming split-K kernel (K % 1024 == 0: 16 < m <= 64, and 8 < m <= 16
+// on large matrices): a workgroup stages x[0:m, K chunk] in LDS once (LDS
+// DMA, the pipelined kernel's swizzled layout) and its 4 waves then stream
+// `rows` weight rows through it, 16 rows (one MFMA A tile) at a time, the
+// next tile's codes and scales in registers while the current one is
+// multiplied.  With many rows per workgroup the activations are read from
+// L2 once per row group instead of once per 64 rows.
 template <int NST>
 struct StrTile {
   u32x4_t cw[NST];   // codes of step s: 32 codes of row r16 at k = 32 g
