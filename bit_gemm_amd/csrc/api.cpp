@@ -90,7 +90,7 @@ int check_nk(int64_t n, int64_t k) {
 // MI355X (4096 x 4096, 14336 x 4096 and 4096 x 14336 weights, m = 1..256):
 // the skinny kernels win up to m = 64 on all three shapes, the tiled
 // kernels above.  Shapes the streaming skinny kernel does not take
-// (k % 1024 != 0) keep the tiled path for 48 < m <= 64 on large matrices;
+// (k % 512 != 0) keep the tiled path for 48 < m <= 64 on large matrices;
 // with k % 64 != 0 the tiled path has only its single-stage kernel, so the
 // skinny path keeps m <= 64 there.
 int choose_path(int64_t m, int64_t n, int64_t k, int path) {
@@ -102,10 +102,11 @@ int choose_path(int64_t m, int64_t n, int64_t k, int path) {
   // the tiled kernel up to m = 48 on every decoder shape (4096 x 4096,
   // 14336 x 4096, 4096 x 14336), and up to m = 64 on the smaller ones
   if (m <= 48 && k % 128 == 0) return NVFP4_PATH_SKINNY;
-  // 48 < m <= 64 with k % 1024 == 0: the streaming skinny kernel is faster
+  // 48 < m <= 64 with k % 512 == 0: the streaming skinny kernel is faster
   // than the tiled kernel on every decoder shape (14336 x 4096 at m = 64:
-  // 23.8 against 31.3 us; 4096 x 14336: 26.1 against 32.1 us)
-  if (k % 1024 == 0) return NVFP4_PATH_SKINNY;
+  // 23.9 against 31.4 us; 4096 x 14336: 26.0 against 31.8 us) and with
+  // 512-wide K chunks (14336 x 4608: 27.1 against 34.1 us)
+  if (k % 512 == 0) return NVFP4_PATH_SKINNY;
   if (k % 64 != 0 || n * k <= (int64_t(1) << 25)) return NVFP4_PATH_SKINNY;
   return NVFP4_PATH_TILED;
 }

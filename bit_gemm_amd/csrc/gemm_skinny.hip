@@ -7,25 +7,25 @@
 //
 // Kernels:
 //  * k_skinny_fk (2 < m <= 16, except 8 < m <= 16 on large matrices: more
-//    than 4096 rows or 2^25 weights, K % 512 == 0, which take the split-K
-//    kernels below): a workgroup owns 16 weight rows
-//    over the whole K and its waves split K; no workspace, one launch.  Loads
-//    of a group of K steps are in flight together and the next group is
-//    prefetched while the current one is consumed.
+//    than 4096 rows or 2^25 weights, K % 512 == 0, which take the streaming
+//    kernel below): a workgroup owns 16 weight rows over the whole K and its
+//    waves split K; no workspace, one launch.  Loads of a group of K steps
+//    are in flight together and the next group is prefetched while the
+//    current one is consumed.
 //  * k_skinny_dot (m <= 2): the same layout with VALU dot products.
-//  * k_skinny_pipe + k_reduce (K % 128 == 0 but K % 1024 != 0: 16 < m <= 64,
-//    and 8 < m <= 16 on large matrices):
-//    64 rows x one K chunk of 512 per workgroup, x staged in LDS by DMA
-//    (shared by the 4 waves), fp32 partials in the workspace, then a second
-//    kernel adds them in chunk order; k_skinny (other K) the same without
-//    the step pipelining.
-//  * k_skinny_str + k_reduce (K % 1024 == 0: 16 < m <= 64, and 8 < m <= 16
-//    on large matrices): one x chunk of
-//    1024 staged per workgroup, then hundreds of weight rows streamed
-//    through it 16 at a time (x read from L2 once per row group).  (A single
-//    launch in which the last workgroup of a tile adds the partials was
-//    measured slower here: the device-coherent stores and loads it needs
-//    cost more than the second launch.)
+//  * k_skinny_str + k_reduce (K % 512 == 0: 16 < m <= 64, and 8 < m <= 16
+//    on large matrices): one x chunk of 1024 (or 512) staged per workgroup,
+//    then hundreds of weight rows streamed through it 16 at a time (x read
+//    from L2 once per row group).  (A single launch in which the last
+//    workgroup of a tile adds the partials was measured slower here: the
+//    device-coherent stores and loads it needs cost more than the second
+//    launch.)
+//  * k_skinny_pipe + k_reduce (a split count forced by the caller, K % 128
+//    == 0): 64 rows x one K chunk of 4 to 16 steps of 128 per workgroup, x
+//    staged in LDS by DMA (shared by the 4 waves), fp32 partials in the
+//    workspace, then a second kernel adds them in chunk order; k_skinny
+//    (16 < m <= 64 with K % 512 != 0, and forced splits the pipelined
+//    kernel cannot take) the same without the step pipelining.
 // In both, val * sigma (<= 6 significant bits) is exact in bf16, products are
 // accumulated in fp32 by v_mfma_f32_16x16x32_bf16 (weights = A operand, 16
 // rows; tokens = B operand), and s_t is applied once to the fp32 sum.
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256) void k_skinny_pipe(const uint16_t* __restrict_
   }
 }
 
-// Streaming split-K kernel (K % 1024 == 0: 16 < m <= 64, and 8 < m <= 16
+// Streaming split-K kernel (K % 512 == 0: 16 < m <= 64, and 8 < m <= 16
 // on large matrices): a workgroup stages x[0:m, K chunk] in LDS once (LDS
 // DMA, the pipelined kernel's swizzled layout) and its 4 waves then stream
 // `rows` weight rows through it, 16 rows (one MFMA A tile) at a time, the
@@ -1100,21 +1100,24 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
     return p;
   }
   const int64_t tiles = (n + kRowsPerWg - 1) / kRowsPerWg;
-  if (forced_splits <= 0 && (mt >= 2 || pipe_small) && k % (8 * kStepK) == 0) {
+  if (forced_splits <= 0 && (mt >= 2 || pipe_small) && k % (4 * kStepK) == 0) {
     // 16 < m <= 64 (and the large-matrix 8 < m <= 16 above): the streaming
-    // kernel, K chunks of 1024 and row groups sized so that about 256
-    // workgroups run (one per CU).  Measured against the pipelined kernel:
+    // kernel, K chunks of 1024 (512 when k % 1024 != 0: against the
+    // pipelined kernel, 14336 x 4608 at m = 32 / 48: 20.1 / 24.0 against
+    // 24.6 / 30.3 us) and row groups sized so that about 256 workgroups
+    // run (one per CU).  Measured against the pipelined kernel:
     // 14336 x 4096 / 4096 x 14336 / 4096 x 4096 at m = 32: 17.5 / 19.3 /
     // 10.0 us against 21.6 / 23.4 / 10.7 us; at m = 48: 21.0 / 22.3 / 11.4
     // against 26.8 / 28.1 / 12.8 us (4096 x 4096 at m = 17: 9.6 against
     // 9.4 us, the one case where it is not faster).
-    const int64_t splits = k / (8 * kStepK);
+    const int64_t nst = k % (8 * kStepK) == 0 ? 8 : 4;
+    const int64_t splits = k / (nst * kStepK);
     int64_t groups = 256 / splits;
     if (groups < 1) groups = 1;
     const int64_t t16 = (n + 15) / 16;
     const int64_t per = (t16 + groups - 1) / groups;
     p.str_rows = (int)(16 * per);
-    p.kchunk = 8 * kStepK;
+    p.kchunk = (int)(nst * kStepK);
     p.splits = (int)splits;
     p.ws_bytes = p.splits > 1 ? (size_t)p.splits * (size_t)m * (size_t)n * sizeof(float) : 0;
     return p;

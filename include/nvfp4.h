@@ -210,15 +210,14 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  * measured on MI355X; nvfp4_w4a16_gemm_path tells which):
  *   m <= 16 -> memory-bound skinny kernel, one launch, a workgroup per 16
  *     weight rows over the whole K (except 8 < m <= 16 on large matrices,
- *     n > 4096 or n * k > 2^25, with k % 512 == 0: the split-K kernels
- *     below);
+ *     n > 4096 or n * k > 2^25, with k % 512 == 0: the streaming split-K
+ *     kernel below);
  *   16 < m <= 64 -> split-K skinny kernel plus a reduction kernel, when
- *     k % 1024 == 0, m <= 48 and k % 128 == 0, k % 64 != 0, or
- *     n * k <= 2^25; else the tiled kernel.  Within it: for k % 1024 == 0
- *     the streaming kernel (an x chunk of 1024 staged once per workgroup,
- *     then many 16-row weight tiles streamed through it); otherwise
- *     activations shared through LDS by 64 weight rows (chunks of 512,
- *     pipelined, when k % 128 == 0);
+ *     k % 512 == 0, m <= 48 and k % 128 == 0, k % 64 != 0, or
+ *     n * k <= 2^25; else the tiled kernel.  Within it: for k % 512 == 0
+ *     the streaming kernel (an x chunk of 1024, or 512, staged once per
+ *     workgroup, then many 16-row weight tiles streamed through it);
+ *     otherwise activations shared through LDS by 64 weight rows;
  *   m > 64 -> the tiled kernel;
  *   n >= 2^27 -> the tiled kernel at any m (the skinny kernels' grid would
  *     pass 2^32 work-items; forcing NVFP4_PATH_SKINNY there is an error).

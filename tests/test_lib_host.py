@@ -171,7 +171,8 @@ def test_dispatch_and_workspace_plan(L):
     # tiled kernel on the larger shapes
     assert P(17, 14336, 4096) == S and P(48, 14336, 4096) == S and P(64, 14336, 4096) == S
     assert P(17, 4096, 14336) == S and P(48, 4096, 14336) == S and P(64, 4096, 14336) == S
-    assert P(49, 14336, 4608) == T  # k % 1024 != 0 (the streaming kernel needs it): tiled above 48
+    assert P(49, 14336, 4608) == S  # k % 512 == 0: the streaming kernel with 512-wide K chunks
+    assert P(49, 14336, 4224) == T  # k % 512 != 0 (the streaming kernel needs it): tiled above 48
     assert P(48, 14336, 4160) == T  # k % 128 != 0, large: tiled
     assert P(48, 14336, 4112) == S and P(64, 4096, 4112) == S  # k % 64 != 0
     assert P(4096, 4096, 4096) == T
@@ -220,8 +221,9 @@ def test_dispatch_and_workspace_plan(L):
     assert L.nvfp4_w4a16_gemm_workspace_size(48, 14336, 4096) == C + 4 * 4 * 48 * 14336
     assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 14336) == C + 14 * 4 * 48 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(33, 65, 1536) == C + 3 * 4 * 33 * 65  # k % 1024 != 0: chunks of 512
-    assert L.nvfp4_w4a16_gemm_workspace_size(17, 4096, 4608) == C + 9 * 4 * 17 * 4096  # pipelined, 9 chunks of 512
-    assert L.nvfp4_w4a16_gemm_workspace_size(12, 14336, 4608) == C + 9 * 4 * 12 * 14336  # pipelined, one token tile
+    assert L.nvfp4_w4a16_gemm_workspace_size(17, 4096, 4608) == C + 9 * 4 * 17 * 4096  # streaming, 9 chunks of 512
+    assert L.nvfp4_w4a16_gemm_workspace_size(12, 14336, 4608) == C + 9 * 4 * 12 * 14336  # streaming, one token tile
+    assert L.nvfp4_w4a16_gemm_workspace_size(64, 14336, 4608) == C + 9 * 4 * 64 * 14336  # streaming above 48 too
     # explicit split K
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 2048, nv.PATH_SKINNY, 1) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 4) == C + 4 * 4 * 8 * 4096
