@@ -87,26 +87,26 @@ int check_nk(int64_t n, int64_t k) {
 
 // Path selection: the lower-latency kernel for the shape ([Recap] section 1
 // picks between its two GEMMs the same way), from latencies measured on
-// MI355X (4096 x 4096, 14336 x 4096 and 4096 x 14336 weights, m = 1..256):
-// the skinny kernels win up to m = 64 on all three shapes, the tiled
-// kernels above.  Shapes the streaming skinny kernel does not take
-// (k % 512 != 0) keep the tiled path for 48 < m <= 64 on large matrices;
-// with k % 64 != 0 the tiled path has only its single-stage kernel, so the
-// skinny path keeps m <= 64 there.
+// MI355X (4096 x 4096, 14336 x 4096 and 4096 x 14336 weights, m = 1..256,
+// and shapes with other k): the skinny kernels win up to m = 64 on all
+// three decoder shapes, the tiled kernels above.  Shapes the streaming
+// skinny kernel does not take (k % 512 != 0) keep the tiled path for
+// 16 < m <= 64 on large matrices; with k % 64 != 0 the tiled path has only
+// its single-stage kernel, so the skinny path keeps m <= 64 there.
 int choose_path(int64_t m, int64_t n, int64_t k, int path) {
   if (path != NVFP4_PATH_AUTO) return path;
   if (n >= ((int64_t)1 << 27)) return NVFP4_PATH_TILED;  // beyond the skinny kernels' grid
   if (m <= 16) return NVFP4_PATH_SKINNY;
   if (m > 64) return NVFP4_PATH_TILED;
-  // measured crossovers: the pipelined split-K skinny kernel is faster than
-  // the tiled kernel up to m = 48 on every decoder shape (4096 x 4096,
-  // 14336 x 4096, 4096 x 14336), and up to m = 64 on the smaller ones
-  if (m <= 48 && k % 128 == 0) return NVFP4_PATH_SKINNY;
-  // 48 < m <= 64 with k % 512 == 0: the streaming skinny kernel is faster
+  // 16 < m <= 64 with k % 512 == 0: the streaming skinny kernel is faster
   // than the tiled kernel on every decoder shape (14336 x 4096 at m = 64:
   // 23.9 against 31.4 us; 4096 x 14336: 26.0 against 31.8 us) and with
   // 512-wide K chunks (14336 x 4608: 27.1 against 34.1 us)
   if (k % 512 == 0) return NVFP4_PATH_SKINNY;
+  // other k: the unpipelined split-K kernel only on small matrices; on large
+  // ones the tiled kernel is faster from m = 17 (4096 x 11008 at m = 24 / 48:
+  // 22.9 / 25.3 against 30.7 / 35.9 us; 14336 x 4224 at m = 48: 32.4
+  // against 43.1 us; 4096 x 4224 keeps the skinny path: 15.4 against 19.3 us)
   if (k % 64 != 0 || n * k <= (int64_t(1) << 25)) return NVFP4_PATH_SKINNY;
   return NVFP4_PATH_TILED;
 }

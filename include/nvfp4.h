@@ -213,8 +213,8 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *     n > 4096 or n * k > 2^25, with k % 512 == 0: the streaming split-K
  *     kernel below);
  *   16 < m <= 64 -> split-K skinny kernel plus a reduction kernel, when
- *     k % 512 == 0, m <= 48 and k % 128 == 0, k % 64 != 0, or
- *     n * k <= 2^25; else the tiled kernel.  Within it: for k % 512 == 0
+ *     k % 512 == 0, k % 64 != 0, or n * k <= 2^25; else the tiled
+ *     kernel.  Within it: for k % 512 == 0
  *     the streaming kernel (an x chunk of 1024, or 512, staged once per
  *     workgroup, then many 16-row weight tiles streamed through it);
  *     otherwise activations shared through LDS by 64 weight rows;

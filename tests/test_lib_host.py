@@ -172,7 +172,9 @@ def test_dispatch_and_workspace_plan(L):
     assert P(17, 14336, 4096) == S and P(48, 14336, 4096) == S and P(64, 14336, 4096) == S
     assert P(17, 4096, 14336) == S and P(48, 4096, 14336) == S and P(64, 4096, 14336) == S
     assert P(49, 14336, 4608) == S  # k % 512 == 0: the streaming kernel with 512-wide K chunks
-    assert P(49, 14336, 4224) == T  # k % 512 != 0 (the streaming kernel needs it): tiled above 48
+    assert P(49, 14336, 4224) == T  # k % 512 != 0 (the streaming kernel needs it): tiled above 16
+    assert P(24, 4096, 11008) == T and P(48, 14336, 4224) == T  # large, k % 512 != 0
+    assert P(32, 4096, 4224) == S  # k % 512 != 0 but <= 2^25 weights: the split-K skinny kernel
     assert P(48, 14336, 4160) == T  # k % 128 != 0, large: tiled
     assert P(48, 14336, 4112) == S and P(64, 4096, 4112) == S  # k % 64 != 0
     assert P(4096, 4096, 4096) == T
