@@ -96,7 +96,16 @@ int check_nk(int64_t n, int64_t k) {
 int choose_path(int64_t m, int64_t n, int64_t k, int path) {
   if (path != NVFP4_PATH_AUTO) return path;
   if (n >= ((int64_t)1 << 27)) return NVFP4_PATH_TILED;  // beyond the skinny kernels' grid
-  if (m <= 16) return NVFP4_PATH_SKINNY;
+  if (m <= 16) {
+    // 8 < m <= 16 on more than 4096 rows when no split-K skinny kernel
+    // applies (k % 512 != 0): the full-K kernel's 16-token workgroups (one
+    // per CU) run in serial rounds, and the tiled kernel is faster
+    // (5120 x 13888 at m = 16: 34.6 against 44.2 us; 14336 x 4224 at m = 9:
+    // 25.7 against 31.7 us; 11008 x 4224 at m = 12: 23.4 against 24.4 us)
+    if (m > 8 && n > 4096 && k % 512 != 0 && k % 64 == 0 && n * k > ((int64_t)1 << 25))
+      return NVFP4_PATH_TILED;
+    return NVFP4_PATH_SKINNY;
+  }
   if (m > 64) return NVFP4_PATH_TILED;
   // 16 < m <= 64 with k % 512 == 0: the streaming skinny kernel is faster
   // than the tiled kernel on every decoder shape (14336 x 4096 at m = 64:

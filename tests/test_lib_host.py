@@ -175,6 +175,9 @@ def test_dispatch_and_workspace_plan(L):
     assert P(49, 14336, 4224) == T  # k % 512 != 0 (the streaming kernel needs it): tiled above 16
     assert P(24, 4096, 11008) == T and P(48, 14336, 4224) == T  # large, k % 512 != 0
     assert P(32, 4096, 4224) == S  # k % 512 != 0 but <= 2^25 weights: the split-K skinny kernel
+    # 8 < m <= 16, more than 4096 rows, k % 512 != 0: tiled; up to 8 tokens or 4096 rows: full-K skinny
+    assert P(12, 14336, 4224) == T and P(16, 5120, 13888) == T
+    assert P(8, 14336, 4224) == S and P(16, 4096, 11008) == S and P(16, 14336, 4096) == S
     assert P(48, 14336, 4160) == T  # k % 128 != 0, large: tiled
     assert P(48, 14336, 4112) == S and P(64, 4096, 4112) == S  # k % 64 != 0
     assert P(4096, 4096, 4096) == T
