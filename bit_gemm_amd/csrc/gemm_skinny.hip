@@ -7,13 +7,13 @@
 //
 // Kernels:
 //  * k_skinny_fk (2 < m <= 16, except 8 < m <= 16 on large matrices: more
-//    than 4096 rows or 2^25 weights, K % 512 == 0, which take the streaming
-//    kernel below): a workgroup owns 16 weight rows over the whole K and its
+//    than 4096 rows or 2^25 weights, K % 512 == 0, and 4 < m <= 8 there
+//    with K > 4096, which take the streaming kernel below): a workgroup owns 16 weight rows over the whole K and its
 //    waves split K; no workspace, one launch.  Loads of a group of K steps
 //    are in flight together and the next group is prefetched while the
 //    current one is consumed.
 //  * k_skinny_dot (m <= 2): the same layout with VALU dot products.
-//  * k_skinny_str + k_reduce (K % 512 == 0: 16 < m <= 64, and 8 < m <= 16
+//  * k_skinny_str + k_reduce (K % 512 == 0: 16 < m <= 64, and 4 < m <= 16
 //    on large matrices): one x chunk of 1024 (or 512) staged per workgroup,
 //    then hundreds of weight rows streamed through it 16 at a time (x read
 //    from L2 once per row group).  (A single launch in which the last
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(256) void k_skinny_pipe(const uint16_t* __restrict_
   }
 }
 
-// Streaming split-K kernel (K % 512 == 0: 16 < m <= 64, and 8 < m <= 16
+// Streaming split-K kernel (K % 512 == 0: 16 < m <= 64, and 4 < m <= 16
 // on large matrices): a workgroup stages x[0:m, K chunk] in LDS once (LDS
 // DMA, the pipelined kernel's swizzled layout) and its 4 waves then stream
 // `rows` weight rows through it, 16 rows (one MFMA A tile) at a time, the
@@ -1081,12 +1081,17 @@ SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   const int mt = (int)((m + 15) / 16);
   const int64_t ksteps = (k + kStepK - 1) / kStepK;
   // 8 < m <= 16 on large matrices (more 16-row workgroups than CUs, or more
-  // than 2^25 weights): the full-K kernel's 16-token build needs ~141 KiB of
-  // LDS per workgroup (one per CU), so its workgroups run in several serial
-  // rounds or few of them stream long rows; the split-K kernels are faster
-  // there (14336 x 4096 at m = 16: streaming 15.3, pipelined 17.4, full-K
-  // 20.6 us; 4096 x 14336 at m = 16: streaming 16.6, full-K 20.0 us).
-  const bool pipe_small = forced_splits <= 0 && m > 8 &&
+  // than 2^25 weights), and 4 < m <= 8 there when K needs more than one
+  // round of the full-K kernel (k > 4096): the full-K kernel's 16-token
+  // build needs ~141 KiB of LDS per workgroup (one per CU), so its
+  // workgroups run in several serial rounds or few of them stream long rows;
+  // the split-K kernels are faster there (14336 x 4096 at m = 16: streaming
+  // 15.3, pipelined 17.4, full-K 20.6 us; 4096 x 14336 at m = 16: streaming
+  // 16.6, full-K 20.0 us; 13824 x 5120 at m = 8: 16.1 against 28.9 us;
+  // 8192 x 28672 at m = 8: 39.6 against 47.4 us).  With one round (k <=
+  // 4096) the full-K kernel stays faster up to 8 tokens (14336 x 4096 at
+  // m = 5: 13.0 against 14.1 us); at 3-4 tokens the two are about even.
+  const bool pipe_small = forced_splits <= 0 && (m > 8 || (m > 4 && k > 4096)) &&
                           ((n + 15) / 16 > 256 || n * k > ((int64_t)1 << 25)) && k % 512 == 0;
   if (forced_splits <= 0 && mt == 1 && k > 0 && !pipe_small) {
     // full K per workgroup: one 512-wide slice per wave and round, up to 8

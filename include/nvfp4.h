@@ -210,8 +210,8 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  * measured on MI355X; nvfp4_w4a16_gemm_path tells which):
  *   m <= 16 -> memory-bound skinny kernel, one launch, a workgroup per 16
  *     weight rows over the whole K (except 8 < m <= 16 on large matrices,
- *     n > 4096 or n * k > 2^25, with k % 512 == 0: the streaming split-K
- *     kernel below; and 8 < m <= 16 with n > 4096, n * k > 2^25,
+ *     n > 4096 or n * k > 2^25, with k % 512 == 0, and 4 < m <= 8 there
+ *     with k > 4096: the streaming split-K kernel below; and 8 < m <= 16 with n > 4096, n * k > 2^25,
  *     k % 512 != 0 and k % 64 == 0: the tiled kernel);
  *   16 < m <= 64 -> split-K skinny kernel plus a reduction kernel, when
  *     k % 512 == 0, k % 64 != 0, or n * k <= 2^25; else the tiled

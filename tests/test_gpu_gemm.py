@@ -93,8 +93,8 @@ PIPE_CASES = [
     (33, 1001, 1024, 0), (48, 4000, 2048, 0), (64, 3000, 3072, 0), (40, 17, 1024, 0), (56, 5000, 4096, 0),
     (17, 1001, 1024, 0), (32, 4100, 2048, 0), (24, 300, 3072, 0),
     # 8 < m <= 16 on large matrices (more than 4096 rows): streaming kernel
-    # with one token tile, K chunks of 1024 or 512
-    (9, 4097, 1024, 0), (16, 4200, 2048, 0), (12, 4100, 1536, 0),
+    # with one token tile, K chunks of 1024 or 512; 4 < m <= 8 with k > 4096
+    (9, 4097, 1024, 0), (16, 4200, 2048, 0), (12, 4100, 1536, 0), (8, 4200, 5120, 0),
     # K chunks of 512 (k % 1024 == 512), two to four token tiles
     (24, 300, 1536, 0), (48, 1000, 2560, 0), (64, 700, 512, 0),
     # k % 512 != 0: the unpipelined split-K kernel

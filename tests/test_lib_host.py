@@ -178,6 +178,9 @@ def test_dispatch_and_workspace_plan(L):
     # 8 < m <= 16, more than 4096 rows, k % 512 != 0: tiled; up to 8 tokens or 4096 rows: full-K skinny
     assert P(12, 14336, 4224) == T and P(16, 5120, 13888) == T
     assert P(8, 14336, 4224) == S and P(16, 4096, 11008) == S and P(16, 14336, 4096) == S
+    # 4 < m <= 8 on large matrices with k > 4096: the streaming kernel (a workspace); k <= 4096: full-K (none)
+    assert L.nvfp4_w4a16_gemm_workspace_size(8, 13824, 5120) == 5 * 4 * 8 * 13824
+    assert L.nvfp4_w4a16_gemm_workspace_size(8, 14336, 4096) == 0 and L.nvfp4_w4a16_gemm_workspace_size(4, 13824, 5120) == 0
     assert P(48, 14336, 4160) == T  # k % 128 != 0, large: tiled
     assert P(48, 14336, 4112) == S and P(64, 4096, 4112) == S  # k % 64 != 0
     assert P(4096, 4096, 4096) == T
@@ -209,7 +212,7 @@ def test_dispatch_and_workspace_plan(L):
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 1) == 0
     for m in (1, 8, 16):  # the full-K skinny kernel needs no workspace
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
-            if m > 8 and (n > 4096 or n * k > 1 << 25):  # large matrices: streaming split-K (K chunks of 1024)
+            if (m > 8 or (m > 4 and k > 4096)) and (n > 4096 or n * k > 1 << 25):  # large: streaming split-K
                 assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == (k // 1024) * 4 * m * n
             else:
                 assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0
