@@ -67,6 +67,7 @@ SIGNATURES = {
     "nvfp4_w4a4_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
     "nvfp4_w4a4_gemm": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size, _c_p]),
     "nvfp4_selftest_cvt": (_c_int, [_c_p, _c_p]),
+    "nvfp4_stream_read": (_c_int, [_c_p, _c_size, _c_int, _c_int, _c_int, _c_p, _c_p]),
     "nvfp4_status_string": (ctypes.c_char_p, [_c_int]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
     "nvfp4_version": (_c_int, []),
@@ -109,13 +110,36 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _need_gpu(t: torch.Tensor, name: str, dtype: torch.dtype):
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None, device=None, min_numel: int = 0,
+          gpu: bool = True):
+    """Check a tensor argument before its pointer reaches the C ABI (which
+    cannot see buffer sizes): dtype, contiguity, exact shape or a minimum
+    element count, then GPU residence (and the device of the other
+    arguments).  Raises ValueError."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} must have at least {min_numel} elements, got {t.numel()}")
+    if not gpu:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other arguments on {device}")
+
+
+def _on_gpu(dev, *named):
+    """GPU residence (on device dev) of (tensor, name) pairs whose dtype and
+    shape were checked already; None entries are skipped."""
+    for t, name in named:
+        if t is not None:
+            _need(t, name, t.dtype, None, dev)
 
 
 @dataclass
@@ -132,15 +156,42 @@ class NVFP4Weight:
     def shape(self):
         return (self.codes.shape[0], self.codes.shape[1] * 2)
 
+    def check(self, device=None, need_amax: bool = False, gpu: bool = True):
+        """Raise ValueError unless codes, scales, mask and the scalars are
+        consistent tensors of one [n, k] matrix (k = 2 * codes.shape[1], a
+        multiple of 16) and, with gpu, all on the GPU; returns (n, k)."""
+        if not isinstance(self.codes, torch.Tensor) or self.codes.dim() != 2:
+            raise ValueError("codes must be a 2-D uint8 tensor [n, k/2]")
+        n, k = self.shape
+        if k % 16 != 0:
+            raise ValueError(f"codes imply k={k}, not a multiple of 16")
+        dev = self.codes.device if device is None else device
+        parts = [(self.codes, "codes", torch.uint8, (n, k // 2), 0),
+                 (self.scales, "scales", torch.uint8, (n, k // 16), 0),
+                 (self.tensor_scale, "tensor_scale", torch.float32, None, 1)]
+        if need_amax:
+            parts.append((self.amax, "amax", torch.float32, None, 1))
+        if self.m4_mask is not None:
+            parts.append((self.m4_mask, "m4_mask", torch.uint8, (n, k // 16), 0))
+        for on_gpu in (False, True) if gpu else (False,):  # every shape first, then residence
+            for t, name, dtype, shape, least in parts:
+                _need(t, name, dtype, shape, dev, min_numel=least, gpu=on_gpu)
+        return n, k
+
 
 def quantize_fos(w: torch.Tensor, amax: Optional[torch.Tensor] = None, with_mask: bool = True,
                  impl: int = IMPL_DEFAULT, out: Optional[NVFP4Weight] = None) -> NVFP4Weight:
     """FourOverSix NVFP4 quantization of a float32 [n, k] GPU matrix."""
-    _need_gpu(w, "w", torch.float32)
-    if w.dim() != 2:
-        raise ValueError("w must be 2-D")
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        raise ValueError("w must be a 2-D tensor")
+    _need(w, "w", torch.float32, gpu=False)
     n, k = w.shape
     dev = w.device
+    if out is not None:
+        if out.check(dev, need_amax=True, gpu=False) != (n, k):
+            raise ValueError(f"out holds a {out.shape} matrix, w is {(n, k)}")
+        out.check(dev, need_amax=True)
+    _on_gpu(dev, (w, "w"))
     if out is None:
         out = NVFP4Weight(
             codes=torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
@@ -150,7 +201,7 @@ def quantize_fos(w: torch.Tensor, amax: Optional[torch.Tensor] = None, with_mask
             m4_mask=torch.empty((n, k // 16), dtype=torch.uint8, device=dev) if with_mask else None,
         )
     if amax is not None:
-        _need_gpu(amax, "amax", torch.float32)
+        _need(amax, "amax", torch.float32, None, dev, min_numel=1)
     _check(lib().nvfp4_quantize_fos_ex(
         _ptr(w), n, k, _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale), _ptr(out.codes),
         _ptr(out.scales), _ptr(out.m4_mask), impl, _stream(dev)))
@@ -167,14 +218,13 @@ def quantize_fos_gptq(w: torch.Tensor, hinv_u: torch.Tensor, amax: Optional[torc
 
     ``hinv_u``: float32 [k, k] GPU matrix, the upper Cholesky factor of the
     inverse Hessian (only its upper triangle is read)."""
-    _need_gpu(w, "w", torch.float32)
-    _need_gpu(hinv_u, "hinv_u", torch.float32)
-    if w.dim() != 2:
-        raise ValueError("w must be 2-D")
+    if not isinstance(w, torch.Tensor) or w.dim() != 2:
+        raise ValueError("w must be a 2-D tensor")
+    _need(w, "w", torch.float32, gpu=False)
     n, k = w.shape
-    if tuple(hinv_u.shape) != (k, k):
-        raise ValueError(f"hinv_u must be [{k}, {k}], got {tuple(hinv_u.shape)}")
     dev = w.device
+    _need(hinv_u, "hinv_u", torch.float32, (k, k), gpu=False)
+    _on_gpu(dev, (w, "w"), (hinv_u, "hinv_u"))
     out = NVFP4Weight(
         codes=torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
         scales=torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
@@ -183,10 +233,11 @@ def quantize_fos_gptq(w: torch.Tensor, hinv_u: torch.Tensor, amax: Optional[torc
         m4_mask=torch.empty((n, k // 16), dtype=torch.uint8, device=dev) if with_mask else None,
     )
     if amax is not None:
-        _need_gpu(amax, "amax", torch.float32)
+        _need(amax, "amax", torch.float32, None, dev, min_numel=1)
     ws = gptq_workspace_size(n, k)
     if workspace is None:
         workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)  # its size: checked by the library
     _check(lib().nvfp4_quantize_fos_gptq(
         _ptr(w), n, k, _ptr(hinv_u), _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale), _ptr(out.codes),
         _ptr(out.scales), _ptr(out.m4_mask), _ptr(workspace), workspace.numel(), _stream(dev)))
@@ -195,8 +246,11 @@ def quantize_fos_gptq(w: torch.Tensor, hinv_u: torch.Tensor, amax: Optional[torc
 
 def tensor_amax(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """max |w| of a float32 GPU tensor, as a float32 [1] GPU tensor."""
-    _need_gpu(w, "w", torch.float32)
+    _need(w, "w", torch.float32, gpu=False)
     n, k = (w.shape[0], w.numel() // max(1, w.shape[0])) if w.dim() else (1, 1)
+    if out is not None:
+        _need(out, "out", torch.float32, None, min_numel=1, gpu=False)
+    _on_gpu(w.device, (w, "w"), (out, "out"))
     if out is None:
         out = torch.empty(1, dtype=torch.float32, device=w.device)
     _check(lib().nvfp4_tensor_amax(_ptr(w), n, k, _ptr(out), _stream(w.device)))
@@ -204,11 +258,16 @@ def tensor_amax(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Te
 
 
 def dequant(q: NVFP4Weight, dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    n, k = q.shape
+    n, k = q.check(gpu=False)
+    if dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"dtype must be float32 or bfloat16, got {dtype}")
     code = {torch.float32: F32, torch.bfloat16: BF16}[dtype]
+    dev = q.codes.device
     if out is None:
-        out = torch.empty((n, k), dtype=dtype, device=q.codes.device)
-    _need_gpu(out, "out", dtype)
+        out = torch.empty((n, k), dtype=dtype, device=dev)
+    _need(out, "out", dtype, (n, k), gpu=False)
+    q.check(dev)
+    _on_gpu(dev, (out, "out"))
     _check(lib().nvfp4_dequant(_ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), n, k, code,
                                _stream(q.codes.device)))
     return out
@@ -226,20 +285,26 @@ def w4a16_gemm(x: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.b
                out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                path: int = PATH_AUTO, split_k: int = 0, impl: int = IMPL_DEFAULT) -> torch.Tensor:
     """y[m, n] = x[m, k] @ W_hat[n, k]^T for bf16 x and NVFP4 weights."""
-    _need_gpu(x, "x", torch.bfloat16)
-    n, k = q.shape
-    if x.dim() != 2 or x.shape[1] != k:
-        raise ValueError(f"x must be [m, {k}], got {tuple(x.shape)}")
+    n, k = q.check(gpu=False)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}], got {tuple(getattr(x, 'shape', ()))}")
     m = x.shape[0]
+    dev = q.codes.device
+    _need(x, "x", torch.bfloat16, gpu=False)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
     code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
-    dev = x.device
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=dev)
-    _need_gpu(out, "out", out_dtype)
+    _need(out, "out", out_dtype, (m, n), gpu=False)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, gpu=False)
+    q.check(dev)
+    _on_gpu(dev, (x, "x"), (out, "out"), (workspace, "workspace"))
     need = workspace_size(m, n, k, path, split_k)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ws_bytes = 0 if workspace is None else workspace.numel()
     _check(lib().nvfp4_w4a16_gemm_ex(
         _ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), m, n, k, code,
         _ptr(workspace), ws_bytes, path, split_k, impl, _stream(dev)))
@@ -254,20 +319,27 @@ def w4a16_gemm_dx(dy: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = tor
                   out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """dx = dy @ W_hat for bf16 [m, n] dy: the input gradient of the linear
     layer y = x @ W_hat^T (quantization-aware training's backward pass)."""
-    _need_gpu(dy, "dy", torch.bfloat16)
-    if dy.dim() != 2:
-        raise ValueError("dy must be 2-D")
+    nw, k = q.check(gpu=False)
+    if not isinstance(dy, torch.Tensor) or dy.dim() != 2:
+        raise ValueError("dy must be a 2-D tensor")
     m, n = dy.shape
-    nw, k = q.shape
     if nw != n:
         raise ValueError(f"dy has n={n}, weights n={nw}")
+    dev = q.codes.device
+    _need(dy, "dy", torch.bfloat16, gpu=False)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
     code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
     if out is None:
-        out = torch.empty((m, k), dtype=out_dtype, device=dy.device)
-    _need_gpu(out, "out", out_dtype)
+        out = torch.empty((m, k), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, (m, k), gpu=False)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, gpu=False)
+    q.check(dev)
+    _on_gpu(dev, (dy, "dy"), (out, "out"), (workspace, "workspace"))
     need = gemm_dx_workspace_size(m, n, k)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dy.device)
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     _check(lib().nvfp4_w4a16_gemm_dx(_ptr(dy), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out),
                                      m, n, k, code, _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                      _stream(dy.device)))
@@ -289,11 +361,22 @@ class NVFP4Act:
 def quantize_act(x: torch.Tensor, amax: Optional[torch.Tensor] = None, with_blockscaled: bool = True,
                  out: Optional[NVFP4Act] = None) -> NVFP4Act:
     """NVFP4 quantization of bf16 [m, k] GPU activations (W4A4 input side)."""
-    _need_gpu(x, "x", torch.bfloat16)
-    if x.dim() != 2:
-        raise ValueError("x must be 2-D")
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor")
+    _need(x, "x", torch.bfloat16, gpu=False)
     m, k = x.shape
     dev = x.device
+    if out is not None:
+        parts = [(out.codes, "out.codes", torch.uint8, (m, k // 2), 0),
+                 (out.scales, "out.scales", torch.uint8, (m, k // 16), 0),
+                 (out.tensor_scale, "out.tensor_scale", torch.float32, None, 1),
+                 (out.amax, "out.amax", torch.float32, None, 1)]
+        if out.blockscaled is not None:
+            parts.append((out.blockscaled, "out.blockscaled", torch.bfloat16, (m, k), 0))
+        for on_gpu in (False, True):
+            for t, name, dtype, shape, least in parts:
+                _need(t, name, dtype, shape, dev, min_numel=least, gpu=on_gpu)
+    _on_gpu(dev, (x, "x"))
     out = out if out is not None else NVFP4Act(
         codes=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
         scales=torch.empty((m, k // 16), dtype=torch.uint8, device=dev),
@@ -302,7 +385,7 @@ def quantize_act(x: torch.Tensor, amax: Optional[torch.Tensor] = None, with_bloc
         blockscaled=torch.empty((m, k), dtype=torch.bfloat16, device=dev) if with_blockscaled else None,
     )
     if amax is not None:
-        _need_gpu(amax, "amax", torch.float32)
+        _need(amax, "amax", torch.float32, None, dev, min_numel=1)
     _check(lib().nvfp4_quantize_act(_ptr(x), m, k, _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale),
                                     _ptr(out.codes), _ptr(out.scales), _ptr(out.blockscaled), _stream(dev)))
     return out
@@ -315,24 +398,29 @@ def w4a4_workspace_size(m: int, n: int, k: int) -> int:
 def w4a4_gemm(x: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.bfloat16,
               out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """y = NVFP4(x) @ W_hat^T for bf16 [m, k] activations (W4A4)."""
-    _need_gpu(x, "x", torch.bfloat16)
+    n, kw = q.check(gpu=False)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor")
     m, k = x.shape
-    n, kw = q.shape
     if kw != k:
         raise ValueError(f"x has k={k}, weights k={kw}")
+    dev = q.codes.device
+    _need(x, "x", torch.bfloat16, gpu=False)
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
     code = {torch.float32: F32, torch.bfloat16: BF16}[out_dtype]
     if out is None:
-        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
-    _need_gpu(out, "out", out_dtype)
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, (m, n), gpu=False)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, gpu=False)
+    q.check(dev)
+    _on_gpu(dev, (x, "x"), (out, "out"), (workspace, "workspace"))
     need = w4a4_workspace_size(m, n, k)
     if workspace is None:
-        workspace = torch.empty(max(need, 256) + 256, dtype=torch.uint8, device=x.device)
-    ws = workspace
-    off = (-ws.data_ptr()) % 256  # the workspace must be 256-byte aligned
-    if off:
-        ws = ws[off:]
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
     _check(lib().nvfp4_w4a4_gemm(_ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), m, n, k,
-                                 code, _ptr(ws), ws.numel(), _stream(x.device)))
+                                 code, _ptr(workspace), workspace.numel(), _stream(dev)))
     return out
 
 
@@ -342,6 +430,24 @@ def selftest_cvt(device=None) -> list:
     buf = torch.zeros(8, dtype=torch.int32, device=dev)
     _check(lib().nvfp4_selftest_cvt(_ptr(buf), _stream(dev)))
     return [int(v) & 0xFFFFFFFF for v in buf.cpu().tolist()]
+
+
+def stream_read(buf: torch.Tensor, nbytes: Optional[int] = None, grid: int = 512, loads_in_flight: int = 8,
+                nontemporal: bool = True, sink: Optional[torch.Tensor] = None) -> None:
+    """Read the first `nbytes` (default: all) of a contiguous GPU tensor once
+    (the read-bandwidth ceiling measurement of nvfp4_stream_read)."""
+    if not isinstance(buf, torch.Tensor) or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous tensor")
+    total = buf.numel() * buf.element_size()
+    nbytes = total if nbytes is None else int(nbytes)
+    if nbytes < 0 or nbytes > total:
+        raise ValueError(f"nbytes={nbytes} outside the buffer ({total} bytes)")
+    if sink is None:
+        sink = torch.empty(64, dtype=torch.int32, device=buf.device)
+    _need(sink, "sink", torch.int32, None, min_numel=64, gpu=False)
+    _on_gpu(buf.device, (buf, "buf"), (sink, "sink"))
+    _check(lib().nvfp4_stream_read(_ptr(buf), nbytes, grid, loads_in_flight, 1 if nontemporal else 0, _ptr(sink),
+                                   _stream(buf.device)))
 
 
 def version() -> str:

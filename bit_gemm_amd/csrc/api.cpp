@@ -391,18 +391,21 @@ NVFP4_API int nvfp4_quantize_act(const void* x, int64_t m, int64_t k, const floa
 
 // W4A4 workspace: 256 bytes of scalars (amax, activation tensor scale, the
 // product of both tensor scales), the block-scaled bf16 activations, their
-// codes and scales, then the GEMM's own workspace; each piece 256-aligned.
+// codes and scales, then the GEMM's own workspace; each piece 256-aligned
+// from the first 256-byte boundary of the caller's (16-byte aligned)
+// buffer, whose size includes the 240 bytes that rounding may skip.
 static size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 static size_t w4a4_act_bytes(int64_t m, int64_t k) {
   const size_t e = (size_t)m * (size_t)k;
   return 256 + round256(2 * e) + round256(e / 2) + round256(e / 16);
 }
+constexpr size_t kW4a4Slack = 240;
 
 NVFP4_API size_t nvfp4_w4a4_gemm_workspace_size(int64_t m, int64_t n, int64_t k) {
   if (m <= 0 || n <= 0 || k <= 0 || k % 16 != 0 || m >= kMaxDim || n >= kMaxDim || k >= kMaxDim ||
       m > kMaxElems / k || m > kMaxElems / n)
     return 0;
-  return w4a4_act_bytes(m, k) + nvfp4_w4a16_gemm_workspace_size(m, n, k);
+  return kW4a4Slack + w4a4_act_bytes(m, k) + nvfp4_w4a16_gemm_workspace_size(m, n, k);
 }
 
 NVFP4_API int nvfp4_w4a4_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
@@ -424,12 +427,14 @@ NVFP4_API int nvfp4_w4a4_gemm(const void* x, const uint8_t* codes, const uint8_t
   if (k == 0) return nvfp4_w4a16_gemm(x, codes, scales, tensor_scale, y, m, n, k, out_dtype, nullptr, 0, stream);
   const size_t act = w4a4_act_bytes(m, k);
   const size_t gws = nvfp4_w4a16_gemm_workspace_size(m, n, k);
-  if (workspace_bytes < act + gws)
-    return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, act + gws);
+  if (workspace_bytes < kW4a4Slack + act + gws)
+    return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes,
+                kW4a4Slack + act + gws);
   if (!workspace) return fail(NVFP4_ERR_INVALID_VALUE, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  if (!aligned(workspace, 16)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 16-byte aligned");
   if ((st = check_device())) return st;
-  uint8_t* base = static_cast<uint8_t*>(workspace);
+  const uintptr_t wsa = reinterpret_cast<uintptr_t>(workspace);
+  uint8_t* base = static_cast<uint8_t*>(workspace) + (((wsa + 255) & ~(uintptr_t)255) - wsa);
   float* sc = reinterpret_cast<float*>(base);  // [0] amax, [1] s_t of x, [2] product of tensor scales
   const size_t e = (size_t)m * (size_t)k;
   uint16_t* xs = reinterpret_cast<uint16_t*>(base + 256);
@@ -441,6 +446,25 @@ NVFP4_API int nvfp4_w4a4_gemm(const void* x, const uint8_t* codes, const uint8_t
   // the bf16 MFMA GEMM of the block-scaled activations, scaled once by the
   // product of both tensor scales
   return nvfp4_w4a16_gemm(xs, codes, scales, sc + 2, y, m, n, k, out_dtype, base + act, gws, stream);
+}
+
+NVFP4_API int nvfp4_stream_read(const void* buf, size_t bytes, int grid, int loads_in_flight, int nontemporal,
+                                uint32_t* sink, void* stream) {
+  g_last_error.clear();
+  if (bytes == 0) return NVFP4_OK;
+  if (!buf || !sink) return fail(NVFP4_ERR_INVALID_VALUE, "buf and sink are required");
+  if (bytes % 16 != 0) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "bytes=%zu is not a multiple of 16", bytes);
+  if (bytes >= ((size_t)1 << 40)) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "bytes=%zu too large", bytes);
+  if (grid < 1 || grid > 65536) return fail(NVFP4_ERR_INVALID_VALUE, "grid %d (1 .. 65536)", grid);
+  if (loads_in_flight != 2 && loads_in_flight != 4 && loads_in_flight != 8 && loads_in_flight != 16)
+    return fail(NVFP4_ERR_INVALID_VALUE, "loads_in_flight %d (2, 4, 8 or 16)", loads_in_flight);
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(NVFP4_ERR_MISALIGNED, "buf must be 16-byte, sink 4-byte aligned");
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = nvfp4::launch_stream_read(buf, (int64_t)bytes, grid, loads_in_flight, nontemporal != 0, sink,
+                                           reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "stream_read launch");
+  return NVFP4_OK;
 }
 
 NVFP4_API int nvfp4_selftest_cvt(uint32_t* counters_out, void* stream) {

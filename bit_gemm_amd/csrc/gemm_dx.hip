@@ -34,20 +34,6 @@ constexpr int kTK = 128;        // weight columns (outputs) per workgroup
 constexpr int kTN = 64;         // weight rows (reduction) per step
 constexpr int kRow = kTN + 8;   // LDS row of 64 bf16 + 16 bytes of padding (bank spread, 16-byte aligned)
 
-// 8 codes of `d` (element i at bits 4i) times sigma, as 8 bf16 (exact).
-template <int J>
-__device__ __forceinline__ void decode2(uint32_t d, float sigma, float* v) {
-  const auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, J);  // byte J of d
-  v[2 * J] = p[0] * sigma;
-  v[2 * J + 1] = p[1] * sigma;
-}
-__device__ __forceinline__ void decode8(uint32_t d, float sigma, float* v) {
-  decode2<0>(d, sigma, v);
-  decode2<1>(d, sigma, v);
-  decode2<2>(d, sigma, v);
-  decode2<3>(d, sigma, v);
-}
-
 __device__ __forceinline__ uint32_t bf16_hi_exact(float f) { return __float_as_uint(f) >> 16; }
 
 struct DxLoads {
@@ -119,10 +105,10 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint16_t* __restrict__ dy
     // rows 2p and 2p + 1 of one block: 16 columns, each a bf16 pair (n, n + 1)
     float v0[16], v1[16];
     const float s0 = e4m3_decode(L.sc[0] & 0x7Fu), s1 = e4m3_decode(L.sc[1] & 0x7Fu);
-    decode8(L.code[0].x, s0, v0);
-    decode8(L.code[0].y, s0, v0 + 8);
-    decode8(L.code[1].x, s1, v1);
-    decode8(L.code[1].y, s1, v1 + 8);
+    dequant8_f32<kConvHw>(L.code[0].x, s0, v0);
+    dequant8_f32<kConvHw>(L.code[0].y, s0, v0 + 8);
+    dequant8_f32<kConvHw>(L.code[1].x, s1, v1);
+    dequant8_f32<kConvHw>(L.code[1].y, s1, v1 + 8);
 #pragma unroll
     for (int c = 0; c < 16; ++c)
       *reinterpret_cast<uint32_t*>(&bs[(16 * kb + c) * kRow + 2 * wp]) =

@@ -44,25 +44,7 @@ constexpr int kLdsBudget = 131072;
 
 template <int IMPL>
 __device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sigma) {
-  u32x4_t o;
-  if constexpr (IMPL == kConvHw) {
-    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
-    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
-    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
-    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
-    o[0] = pack_bf16_exact(v0[0] * sigma, v0[1] * sigma);
-    o[1] = pack_bf16_exact(v1[0] * sigma, v1[1] * sigma);
-    o[2] = pack_bf16_exact(v2[0] * sigma, v2[1] * sigma);
-    o[3] = pack_bf16_exact(v3[0] * sigma, v3[1] * sigma);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = e2m1_val_portable((d >> (8 * i)) & 0xFu) * sigma;
-      const float b = e2m1_val_portable((d >> (8 * i + 4)) & 0xFu) * sigma;
-      o[i] = pack_bf16_exact(a, b);
-    }
-  }
-  return __builtin_bit_cast(bf16x8_t, o);
+  return __builtin_bit_cast(bf16x8_t, dequant8_bf16<IMPL>(d, sigma));
 }
 
 __device__ __forceinline__ void store_out(void* y, int64_t idx, float v, int out_f32) {

@@ -39,25 +39,8 @@ constexpr int kFragBytes = 2 * 8 * 4 * 16 * 16;  // 16 KiB per operand
 
 template <int IMPL>
 __device__ __forceinline__ uint4 dequant8u(uint32_t d, float sigma) {
-  uint4 o;
-  if constexpr (IMPL == kConvHw) {
-    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
-    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
-    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
-    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
-    o.x = pack_bf16_exact(v0[0] * sigma, v0[1] * sigma);
-    o.y = pack_bf16_exact(v1[0] * sigma, v1[1] * sigma);
-    o.z = pack_bf16_exact(v2[0] * sigma, v2[1] * sigma);
-    o.w = pack_bf16_exact(v3[0] * sigma, v3[1] * sigma);
-  } else {
-    uint32_t t[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      t[i] = pack_bf16_exact(e2m1_val_portable((d >> (8 * i)) & 0xFu) * sigma,
-                             e2m1_val_portable((d >> (8 * i + 4)) & 0xFu) * sigma);
-    o = make_uint4(t[0], t[1], t[2], t[3]);
-  }
-  return o;
+  const u32x4_t o = dequant8_bf16<IMPL>(d, sigma);
+  return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
 

@@ -116,6 +116,43 @@ __device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
   return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
 }
 
+// 8 codes of `d` (code i in bits 4i..4i+3, the packed row order) times the
+// block scale sigma, as 8 fp32 values v[0..7] in k order.  The product has at
+// most 6 significant bits (2 of the E2M1 value, 4 of the E4M3 scale), so it
+// is exact in fp32 and in bf16.  kConvHw decodes each byte with gfx950's
+// FP4 -> fp32 conversion at unit scale (exact; checked on every code byte by
+// nvfp4_selftest_cvt), the portable form from the bit patterns.
+template <int IMPL>
+__device__ __forceinline__ void dequant8_f32(uint32_t d, float sigma, float* v) {
+  if constexpr (IMPL == kConvHw) {
+    const auto v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 0);
+    const auto v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 1);
+    const auto v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 2);
+    const auto v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d, 1.0f, 3);
+    v[0] = v0[0] * sigma;
+    v[1] = v0[1] * sigma;
+    v[2] = v1[0] * sigma;
+    v[3] = v1[1] * sigma;
+    v[4] = v2[0] * sigma;
+    v[5] = v2[1] * sigma;
+    v[6] = v3[0] * sigma;
+    v[7] = v3[1] * sigma;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = e2m1_val_portable((d >> (4 * i)) & 0xFu) * sigma;
+  }
+}
+
+// The same 8 values as bf16 in k order (an MFMA operand of 8 k): exact, so
+// packing keeps the high half of each fp32.
+template <int IMPL>
+__device__ __forceinline__ u32x4_t dequant8_bf16(uint32_t d, float sigma) {
+  float v[8];
+  dequant8_f32<IMPL>(d, sigma, v);
+  return u32x4_t{pack_bf16_exact(v[0], v[1]), pack_bf16_exact(v[2], v[3]), pack_bf16_exact(v[4], v[5]),
+                 pack_bf16_exact(v[6], v[7])};
+}
+
 // Streaming (non-temporal) accesses for data that one kernel reads or writes
 // exactly once: the weight matrix in the amax and quantization passes, the
 // dequantized output.  The hint lets the caches evict these lines first;

@@ -316,10 +316,12 @@ NVFP4_API int nvfp4_quantize_act(const void* x, int64_t m, int64_t k, const floa
  * scales applied once in the epilogue.  Same accuracy contract as
  * nvfp4_w4a16_gemm, against the W4A4 reference.
  *
- * Arguments as nvfp4_w4a16_gemm; workspace: device, 256-byte aligned, at
- * least nvfp4_w4a4_gemm_workspace_size(m, n, k) bytes (activation scalars,
- * block-scaled values, codes and scales, then the GEMM's workspace);
- * caller-owned scratch; contents on entry do not matter.
+ * Arguments as nvfp4_w4a16_gemm; workspace: device, 16-byte aligned like
+ * every other buffer, at least nvfp4_w4a4_gemm_workspace_size(m, n, k) bytes
+ * (activation scalars, block-scaled values, codes and scales, then the
+ * GEMM's workspace, laid out from the buffer's first 256-byte boundary; the
+ * size includes the bytes skipped to reach it); caller-owned scratch;
+ * contents on entry do not matter.
  */
 NVFP4_API size_t nvfp4_w4a4_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 NVFP4_API int nvfp4_w4a4_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
@@ -348,6 +350,28 @@ NVFP4_API int nvfp4_w4a4_gemm(const void* x, const uint8_t* codes, const uint8_t
  * Used by the tests to decide whether NVFP4_IMPL_HWCVT is exact.
  */
 NVFP4_API int nvfp4_selftest_cvt(uint32_t* counters_out, void* stream);
+
+/*
+ * nvfp4_stream_read - measurement helper: reads `bytes` of device memory
+ * once and computes nothing of the method.  Decode reads every weight from
+ * HBM once per token ([Notes08] section 01), so a W4A16 GEMM at small token
+ * counts is bounded by this GPU's read bandwidth; this kernel measures that
+ * ceiling at the size of a weight matrix, as the reference the GEMMs'
+ * throughput is reported against (beside the published 8 TB/s).
+ *
+ * buf: device, 16-byte aligned, `bytes` a multiple of 16 (0: no work);
+ * grid: workgroups of 256 threads (1 .. 65536); loads_in_flight: 16-byte
+ * loads per thread in flight (2, 4, 8 or 16); nontemporal != 0: streaming
+ * (non-temporal) loads; sink: device buffer of 64 uint32 that the kernel may
+ * write (only if the data folds to one fixed value: it keeps the loads from
+ * being removed).  Every load is in bounds.  Asynchronous on `stream`.
+ * Errors: NVFP4_ERR_INVALID_VALUE (null buf or sink, bad grid or
+ * loads_in_flight), NVFP4_ERR_UNSUPPORTED_SHAPE (bytes not a multiple of 16,
+ * or >= 2^40), NVFP4_ERR_MISALIGNED, NVFP4_ERR_UNSUPPORTED_DEVICE,
+ * NVFP4_ERR_HIP.
+ */
+NVFP4_API int nvfp4_stream_read(const void* buf, size_t bytes, int grid, int loads_in_flight, int nontemporal,
+                                uint32_t* sink, void* stream);
 
 NVFP4_API const char* nvfp4_status_string(int status);
 NVFP4_API const char* nvfp4_last_error(void);

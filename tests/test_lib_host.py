@@ -88,17 +88,29 @@ def test_w4a4_rejects_bad_arguments_on_host(L):
     assert qa(FAKE, 4, 32, None, FAKE, FAKE, FAKE, FAKE, ODD, None) == 3  # x_blockscaled
     e = 8 * 64
     act = 256 + 1024 + 256 + 256  # scalars, bf16 values, codes, scales (256-byte pieces)
-    assert L.nvfp4_w4a4_gemm_workspace_size(8, 32, 64) == act + L.nvfp4_w4a16_gemm_workspace_size(8, 32, 64)
+    slack = 240  # bytes a 16-byte aligned buffer may skip to its first 256-byte boundary
+    assert L.nvfp4_w4a4_gemm_workspace_size(8, 32, 64) == slack + act + L.nvfp4_w4a16_gemm_workspace_size(8, 32, 64)
     assert L.nvfp4_w4a4_gemm_workspace_size(0, 32, 64) == 0
     assert L.nvfp4_w4a4_gemm_workspace_size(8, 32, 24) == 0
     ws = L.nvfp4_w4a4_gemm_workspace_size(8, 32, 64)
     g = L.nvfp4_w4a4_gemm
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 0, FAKE, ws - 1, None) == 4
-    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 0, FAKE + 16, ws, None) == 3  # workspace alignment
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 0, ODD, ws, None) == 3  # workspace: 16-byte alignment
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 5, FAKE, ws, None) == 1
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 24, 0, FAKE, ws, None) == 2
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 64, 0, None, 0, None) == 0  # empty: no work
     assert e == 512
+
+
+def test_stream_read_rejects_bad_arguments_on_host(L):
+    r = L.nvfp4_stream_read
+    assert r(FAKE, 0, 512, 8, 1, FAKE, None) == 0  # nothing to read
+    assert r(None, 1024, 512, 8, 1, FAKE, None) == 1
+    assert r(FAKE, 1024, 512, 8, 1, None, None) == 1
+    assert r(FAKE, 1000, 512, 8, 1, FAKE, None) == 2  # not a multiple of 16
+    assert r(FAKE, 1024, 0, 8, 1, FAKE, None) == 1 and r(FAKE, 1024, 65537, 8, 1, FAKE, None) == 1
+    assert r(FAKE, 1024, 512, 3, 1, FAKE, None) == 1  # loads in flight: 2, 4, 8 or 16
+    assert r(ODD, 1024, 512, 8, 1, FAKE, None) == 3
 
 
 def test_gemm_dx_rejects_bad_arguments_on_host(L):
@@ -181,6 +193,11 @@ def test_dispatch_and_workspace_plan(L):
     # 4 < m <= 8 on large matrices with k > 4096: the streaming kernel (a workspace); k <= 4096: full-K (none)
     assert L.nvfp4_w4a16_gemm_workspace_size(8, 13824, 5120) == 5 * 4 * 8 * 13824
     assert L.nvfp4_w4a16_gemm_workspace_size(8, 14336, 4096) == 0 and L.nvfp4_w4a16_gemm_workspace_size(4, 13824, 5120) == 0
+    # the decoder's down projection (n = 4096, k = 14336: 2^25.8 weights) takes that route from m = 5
+    for m in (5, 6, 7, 8):
+        assert P(m, 4096, 14336) == S
+        assert L.nvfp4_w4a16_gemm_workspace_size(m, 4096, 14336) == 14 * 4 * m * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(4, 4096, 14336) == 0
     assert P(48, 14336, 4160) == T  # k % 128 != 0, large: tiled
     assert P(48, 14336, 4112) == S and P(64, 4096, 4112) == S  # k % 64 != 0
     assert P(4096, 4096, 4096) == T
@@ -237,3 +254,81 @@ def test_dispatch_and_workspace_plan(L):
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 4096, nv.PATH_SKINNY, 4) == C + 4 * 4 * 8 * 4096
     # a chunk larger than registers / LDS allow is split further (16 steps max)
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(8, 4096, 8192, nv.PATH_SKINNY, 2) == C + 4 * 4 * 8 * 4096
+
+
+# ---------------------------------------------------------------------------
+# The Python binding checks every tensor argument before a pointer reaches
+# the C ABI (which cannot see buffer sizes): shapes, dtypes and the packed
+# weight's internal consistency, then GPU residence.  These run on CPU
+# tensors: the shape and dtype checks come first, so each error below is the
+# one named, raised before any GPU call.
+# ---------------------------------------------------------------------------
+def _cpu_weight(n=32, k=64):
+    import torch
+
+    return nv.NVFP4Weight(codes=torch.zeros((n, k // 2), dtype=torch.uint8),
+                          scales=torch.zeros((n, k // 16), dtype=torch.uint8),
+                          tensor_scale=torch.ones(1, dtype=torch.float32),
+                          amax=torch.ones(1, dtype=torch.float32),
+                          m4_mask=torch.zeros((n, k // 16), dtype=torch.uint8))
+
+
+def test_binding_rejects_mismatched_weight_tensors():
+    import torch
+
+    q = _cpu_weight()
+    q.scales = torch.zeros((32, 3), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="scales must have shape"):
+        nv.dequant(q)
+    q = _cpu_weight()
+    q.m4_mask = torch.zeros((31, 4), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="m4_mask must have shape"):
+        q.check()
+    q = _cpu_weight()
+    q.tensor_scale = torch.ones(0, dtype=torch.float32)
+    with pytest.raises(ValueError, match="tensor_scale must have at least 1"):
+        nv.w4a16_gemm(torch.zeros((1, 64), dtype=torch.bfloat16), q)
+    q = _cpu_weight()
+    q.codes = torch.zeros((32, 12), dtype=torch.uint8)  # k = 24
+    with pytest.raises(ValueError, match="not a multiple of 16"):
+        q.check()
+    q = _cpu_weight()
+    q.scales = q.scales.to(torch.int32)
+    with pytest.raises(ValueError, match="scales must be torch.uint8"):
+        q.check()
+    with pytest.raises(ValueError, match="must be a GPU tensor"):  # consistent, but on the host
+        _cpu_weight().check()
+
+
+def test_binding_rejects_wrong_output_shapes():
+    import torch
+
+    q = _cpu_weight(32, 64)
+    x = torch.zeros((3, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match=r"out must have shape \(3, 32\)"):
+        nv.w4a16_gemm(x, q, out=torch.zeros((3, 31), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match=r"x must be \[m, 64\]"):
+        nv.w4a16_gemm(torch.zeros((3, 48), dtype=torch.bfloat16), q)
+    with pytest.raises(ValueError, match="out_dtype"):
+        nv.w4a16_gemm(x, q, out_dtype=torch.float16)
+    with pytest.raises(ValueError, match=r"out must have shape \(32, 64\)"):
+        nv.dequant(q, torch.float32, out=torch.zeros((32, 63), dtype=torch.float32))
+    with pytest.raises(ValueError, match=r"out must have shape \(3, 64\)"):
+        nv.w4a16_gemm_dx(torch.zeros((3, 32), dtype=torch.bfloat16), q,
+                         out=torch.zeros((3, 32), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="dy has n=31"):
+        nv.w4a16_gemm_dx(torch.zeros((3, 31), dtype=torch.bfloat16), q)
+    with pytest.raises(ValueError, match=r"out must have shape \(3, 32\)"):
+        nv.w4a4_gemm(x, q, out=torch.zeros((2, 32), dtype=torch.bfloat16))
+    w = torch.zeros((32, 64), dtype=torch.float32)
+    bad = _cpu_weight(16, 64)
+    with pytest.raises(ValueError, match="out holds a"):
+        nv.quantize_fos(w, out=bad)
+    with pytest.raises(ValueError, match=r"hinv_u must have shape \(64, 64\)"):
+        nv.quantize_fos_gptq(w, torch.zeros((64, 32), dtype=torch.float32))
+    act = nv.NVFP4Act(codes=torch.zeros((3, 31), dtype=torch.uint8), scales=torch.zeros((3, 4), dtype=torch.uint8),
+                      tensor_scale=torch.ones(1), amax=torch.ones(1), blockscaled=None)
+    with pytest.raises(ValueError, match=r"out.codes must have shape \(3, 32\)"):
+        nv.quantize_act(x, out=act)
+    with pytest.raises(ValueError, match="out must have at least 1"):
+        nv.tensor_amax(w, out=torch.zeros(0, dtype=torch.float32))
