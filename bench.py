@@ -1,24 +1,26 @@
 #!/usr/bin/env python
-"""Throughput of the NVFP4 FourOverSix quantizer + W4A16 GEMM hot path on one
-MI355X (gfx950).
+"""Throughput of the W4A16 NVFP4 GEMM (and the FourOverSix quantizer around
+it) on one MI355X (gfx950).
 
 Workload (single decode-shaped layer): W fp32 4096 x 4096 drawn from a
-Student-t (nu=5) scaled to std 0.02 with 0.1% outliers x20 (seed 2); bf16
-activations N(0, 1) of shape M x 4096 for M in {1, 8, 16, 32, 48}
-(seed 9000 + M).  Synthetic data stands in for the pages' real model weights.
+Student-t (nu=5) scaled to std 0.02 with 0.1% outliers x20 (seed 2),
+quantized with FourOverSix; bf16 activations N(0, 1) of shape M x 4096 for M
+in {1, 8, 16, 32, 48} (seed 9000 + M).  Synthetic data stands in for the
+pages' real model weights.
 
-One step = one pass of the whole hot path:
-  tensor amax -> FourOverSix quantization (codes, E4M3 scales, M=4 mask)
-  -> W4A16 GEMM at each M -> bf16 dequantization.
-Every step runs from a HIP graph (one graph per rotation slot) so the GPU is
-not starved by Python launch overhead.  Inputs rotate over enough copies that
-every kernel reads cold data from HBM (not the 256 MB last-level cache): 8
-fp32 sources (512 MiB) and 7 packed weight copies per rotation slot x 16
-slots; all copies hold the same quantized weights.
+The timed step (the metric): the five W4A16 GEMMs, M = 1, 8, 16, 32, 48,
+back to back, each reading its own cold copy of the packed weights from HBM
+(the copies total ~1 GiB, beyond the 256 MB last-level cache), replayed from
+HIP graphs.  value = 5 x packed-weight bytes (0.5625 B/weight) / step time.
 
-Output: one JSON line (rank 0) with the whole-step throughput in GB/s of
-algorithmic HBM bytes, per-kernel rooflines measured with HIP events over
-graph-batched launches, and the CPU oracle timed on this host.
+Beside it (not in value): the whole hot-path step (tensor amax ->
+FourOverSix quantization -> the five GEMMs -> bf16 dequant), per-kernel
+durations from HIP events over graph-batched launches, the HBM read ceiling
+of this GPU at the layer sizes (a read-only streaming kernel of the
+library), the decoder shapes, the 32-layer decoder, GPTQ, and the CPU oracle
+timed on this host.
+
+Output: one JSON line.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -67,7 +69,13 @@ def parse_args(argv=None):
                     help="only the GPTQ report (for rocprofv3 runs), then exit")
     ap.add_argument("--gptq-shape", default=None,
                     help="restrict the GPTQ report to one shape (w4096x4096, up_gate or down)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU oracle time per leg")
+    ap.add_argument("--no-cpu-configs", action="store_true",
+                    help="skip the oracle on the MLP set and the large-M shapes (per-matrix M=4 share, "
+                         "GPU == oracle)")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="also run the oracle on layers 0 and 31 of the 32-layer decoder in full (adds "
+                         "about a minute of host work)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the steps directly instead of from HIP graphs (for counter "
                          "collection); prints the step time only")
@@ -208,6 +216,12 @@ def main(argv=None):
     stream = torch.cuda.Stream()
     step_bytes = (bytes_amax(N, K) + bytes_fos(N, K) + sum(bytes_gemm(m, N, K) for m in M_LIST)
                   + bytes_dequant_bf16(N, K))
+    gemm_pass_weight_bytes = len(M_LIST) * bytes_gemm_weights(N, K)
+
+    def gemm_pass(v):
+        for j in range(len(M_LIST)):
+            op_gemm(v, j)
+
     if args.eager:
         with torch.cuda.stream(stream):
             for s in range(args.warmup):
@@ -219,33 +233,41 @@ def main(argv=None):
             torch.cuda.synchronize()
             t1 = time.perf_counter()
         ms = (t1 - t0) * 1e3 / args.steps
-        print(json.dumps({"metric": METRIC, "mode": "eager (profiling)", "value": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        print(json.dumps({"metric": METRIC, "mode": "eager hot-path steps (profiling)",
+                          "step_gbs": round(step_bytes / (ms * 1e-3) / 1e9, 1),
                           "unit": "GB/s", "ms_per_step": round(ms, 4), "steps": args.steps, "warmup": args.warmup}))
         return 0
-    graphs = []
     with torch.cuda.stream(stream):
         for v in range(ROT_SLOTS):  # eager warm-up of every path before capture
             step(v)
     torch.cuda.synchronize()
+    gemm_graphs, step_graphs = [], []
     for v in range(ROT_SLOTS):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=stream):
+            gemm_pass(v)
+        gemm_graphs.append(g)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
             step(v)
-        graphs.append(g)
+        step_graphs.append(g)
     torch.cuda.synchronize()
 
-    # ---------------- timed region: K whole steps ----------------------------
-    for s in range(args.warmup):
-        graphs[s % ROT_SLOTS].replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        graphs[(args.warmup + s) % ROT_SLOTS].replay()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    def timed_replays(graphs):
+        for s in range(args.warmup):
+            graphs[s % ROT_SLOTS].replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(args.steps):
+            graphs[(args.warmup + s) % ROT_SLOTS].replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
 
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    # ---------------- timed region: K steps of the five GEMMs ----------------
+    ms_per_step = timed_replays(gemm_graphs)
+    value = gemm_pass_weight_bytes / (ms_per_step * 1e-3) / 1e9
+    # the whole hot path (beside the metric)
+    ms_hot = timed_replays(step_graphs)
 
     # ---------------- per-kernel durations: HIP events over graph batches ----
     def time_op(fn, L):
@@ -275,6 +297,10 @@ def main(argv=None):
     def dequant_any(r):
         nv.dequant(packed(r % n_packed), torch.bfloat16, out=deq_out)
 
+    # HBM read ceiling at the sizes the GEMMs stream (read-only kernel of the library)
+    ceilings = read_ceilings(stream, time_op)
+    ceil_layer = ceilings[str(int(bytes_gemm_weights(N, K)))]
+
     L = args.kernel_reps
     kernels = {}
     kernels["amax"] = dict(us=time_op(lambda r: op_amax(r % ROT_SLOTS), L), bytes=bytes_amax(N, K), launches=2,
@@ -285,6 +311,7 @@ def main(argv=None):
         kernels[f"gemm_m{m}"] = dict(us=time_op(lambda r, j=j: gemm_any(r, j), n_packed), bytes=bytes_gemm(m, N, K),
                                      weight_bytes=bytes_gemm_weights(N, K),
                                      path=nv.gemm_path(m, N, K),
+                                     launches=2 if nv.workspace_size(m, N, K) > 0 else 1,
                                      flops=2 * m * N * K)
     kernels["dequant_bf16"] = dict(us=time_op(dequant_any, n_packed), bytes=bytes_dequant_bf16(N, K), launches=1)
     for name, kd in kernels.items():
@@ -293,30 +320,36 @@ def main(argv=None):
         if "weight_bytes" in kd:
             kd["weight_gbs"] = kd["weight_bytes"] / (kd["us"] * 1e-6) / 1e9
             kd["weight_frac_hbm"] = kd["weight_gbs"] / HBM_PEAK_GBS
+            kd["weight_frac_read_ceiling"] = kd["weight_gbs"] / ceil_layer["gbs"]
             kd["tflops"] = kd["flops"] / (kd["us"] * 1e-6) / 1e12
-    dominant = max(kernels, key=lambda k: kernels[k]["us"])
+    # roofline: the GEMM call of the metric that takes longest (two kernels,
+    # main + split-K reduction, when it needs a workspace)
+    dominant = max((f"gemm_m{m}" for m in M_LIST), key=lambda k: kernels[k]["us"])
     dk = kernels[dominant]
     traffic = read_traffic_summary(dominant)
-    # streaming ceiling on this GPU: torch's device copy of the 64 MiB fp32
-    # matrix (cold rotating sources and destinations), read + write bytes
     dsts = [torch.empty_like(src[0]) for _ in range(4)]
     copy_bytes = 2 * src[0].numel() * 4
     copy_us = time_op(lambda r: dsts[r % 4].copy_(src[r % ROT_SRC]), L)
     copy_gbs = copy_bytes / (copy_us * 1e-6) / 1e9
     del dsts
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(dk["gbs"], 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(dk["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
+    roofline = {"bound": "hbm", "kernel": dominant + (" (main kernel + split-K reduction)" if dk["launches"] == 2
+                                                      else ""),
+                "achieved": round(dk["gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dk["gbs"] / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_us": round(dk["us"], 3),
-                "stream_copy_gbs": round(copy_gbs, 1), "frac_of_stream_copy": round(dk["gbs"] / copy_gbs, 4)}
+                "read_ceiling_gbs_same_size": round(ceil_layer["gbs"], 1),
+                "frac_of_read_ceiling": round(dk["gbs"] / ceil_layer["gbs"], 4),
+                "device_copy_gbs_64MiB": round(copy_gbs, 1)}
 
-    gemm_w_bytes = sum(bytes_gemm_weights(N, K) for _ in M_LIST)
     gemm_us = sum(kernels[f"gemm_m{m}"]["us"] for m in M_LIST)
     gemm_summary = {
-        "weight_gbs_all_m": round(gemm_w_bytes / (gemm_us * 1e-6) / 1e9, 1),
-        "weight_frac_hbm_all_m": round(gemm_w_bytes / (gemm_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        "weight_gbs_all_m_events": round(gemm_pass_weight_bytes / (gemm_us * 1e-6) / 1e9, 1),
+        "weight_frac_hbm_all_m": round(value / HBM_PEAK_GBS, 4),
+        "weight_frac_read_ceiling_all_m": round(value / ceil_layer["gbs"], 4),
         "per_m": {m: {"us": round(kernels[f"gemm_m{m}"]["us"], 3),
                       "weight_gbs": round(kernels[f"gemm_m{m}"]["weight_gbs"], 1),
                       "frac_hbm": round(kernels[f"gemm_m{m}"]["weight_frac_hbm"], 4),
+                      "frac_read_ceiling": round(kernels[f"gemm_m{m}"]["weight_frac_read_ceiling"], 4),
                       "tflops": round(kernels[f"gemm_m{m}"]["tflops"], 2)} for m in M_LIST},
     }
     fos = kernels["fos_quantize"]
@@ -326,20 +359,27 @@ def main(argv=None):
         "with_amax_pass_gbs": round((bytes_fos(N, K) + bytes_amax(N, K)) / (quant_us * 1e-6) / 1e9, 1),
         "weights_per_s": round(N * K / (quant_us * 1e-6), 1),
         "m4_share": round(float(mask_all[0].to(torch.int64).sum().item()) / mask_all[0].numel(), 4),
+        "m4_share_pages_context": "40-43% of blocks (GPTQ on real weights, another GPU)",
     }
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "dtype_detail": "FP4 E2M1 weights x bf16 activations on bf16 MFMA, fp32 accumulate; fp32 quantizer",
+        "dtype_detail": "FP4 E2M1 weights (E4M3 block scales) x bf16 activations on bf16 MFMA / dot2, fp32 "
+                        "accumulate; fp32 quantizer",
         "data": "synthetic",
-        "config": {"workload": "single decode-shaped layer 4096x4096, Student-t(5) std 0.02 + 0.1% outliers x20, "
-                               "bf16 activations M in {1,8,16,32,48}; step = amax + FourOverSix quantize + "
-                               "5 W4A16 GEMMs + bf16 dequant",
-                   "n": N, "k": K, "m": M_LIST, "step_algorithmic_bytes": step_bytes},
+        "config": {"workload": "W4A16 GEMM on one decode-shaped layer 4096x4096 (Student-t(5) std 0.02 + 0.1% "
+                               "outliers x20, FourOverSix NVFP4), bf16 activations M in {1,8,16,32,48}; step = "
+                               "the five GEMMs, each on a cold copy of the packed weights; value = packed-weight "
+                               "bytes / step time",
+                   "n": N, "k": K, "m": M_LIST, "step_weight_bytes": gemm_pass_weight_bytes},
         "roofline": roofline,
+        "read_ceiling": ceilings,
         "gemm": gemm_summary,
+        "hot_path_step": {"what": "tensor amax + FourOverSix quantize + the five GEMMs + bf16 dequant",
+                          "ms": round(ms_hot, 4), "algorithmic_bytes": step_bytes,
+                          "gbs": round(step_bytes / (ms_hot * 1e-3) / 1e9, 1)},
         "quantizer": quant_summary,
         "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in kd.items()}
                     for k, kd in kernels.items()},
@@ -349,15 +389,55 @@ def main(argv=None):
     if args.dispatch_sweep:
         result["dispatch_sweep"] = dispatch_sweep(args, stream, time_op, src[0])
     if not args.no_shapes:
-        result["decoder_shapes"] = decoder_shapes(args, stream, time_op, src[0])
-        result["decoder_model_32_layers"] = decoder_model(args, stream, src[0])
+        result["decoder_shapes"] = decoder_shapes(args, stream, time_op, src[0], ceilings)
+        result["decoder_model_32_layers"] = decoder_model(args, stream, src[0], ceilings)
 
     if not args.no_gptq:
         result["gptq"] = gptq_report(args, src[0])
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], result["parity"] = cpu_baseline(args, w_host, xs, packed(1), step_bytes)
+        result["cpu_baseline"], result["parity"] = cpu_baseline(args, w_host, xs, packed(1))
     print(json.dumps(result), flush=True)
     return 0
+
+
+READ_SIZES = [("layer_4096x4096_packed", 9437184), ("mlp_matrix_packed", 33030144), ("1GiB", 1 << 30)]
+
+
+def read_ceilings(stream, time_op):
+    """The HBM read ceiling at each size: the fastest of a sweep of launch
+    shapes (256 .. 2048 workgroups of 256 threads, 4 or 8 16-byte loads per
+    thread in flight, plain or non-temporal loads) of the library's
+    read-only streaming kernel, each launch reading its own cold region of a
+    1.25 GiB buffer (beyond the 256 MB last-level cache)."""
+    import torch
+
+    import bit_gemm_amd as nv
+
+    total = 1280 << 20
+    buf = torch.empty(total, dtype=torch.uint8, device=stream.device)
+    buf.fill_(0x5A)
+    sink = torch.empty(64, dtype=torch.int32, device=stream.device)
+    out = {}
+    for name, size in READ_SIZES:
+        copies = total // size
+        L = min(100, max(4, copies))
+        views = [buf[(i % copies) * size:(i % copies) * size + size] for i in range(L)]
+        best = None
+        for grid in (256, 512, 1024, 2048):
+            for u in (4, 8):
+                for nt in (True, False):
+                    us = time_op(lambda r: nv.stream_read(views[r % L], grid=grid, loads_in_flight=u,
+                                                          nontemporal=nt, sink=sink), L)
+                    if best is None or us < best[0]:
+                        best = (us, grid, u, nt)
+        us, grid, u, nt = best
+        out[str(size)] = {"name": name, "bytes": size, "us": round(us, 3), "gbs": round(size / (us * 1e-6) / 1e9, 1),
+                          "frac_hbm": round(size / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                          "launch": {"grid": grid, "loads_in_flight": u, "nontemporal": nt}}
+        del views
+    del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix rate
@@ -368,7 +448,7 @@ LARGE_SHAPES = [("attn", 4096, 4096), ("up_gate", 14336, 4096)]
 LARGE_M = [64, 256, 1024, 4096]
 
 
-def decoder_shapes(args, stream, time_op, w_dev):
+def decoder_shapes(args, stream, time_op, w_dev, ceilings):
     """GEMM latency on the other decoder-layer shapes (reported beside the
     step, not part of it): the MLP matrices at decode token counts (weight
     GB/s against HBM) and the large-M prefill shapes (TFLOP/s against the
@@ -404,7 +484,9 @@ def decoder_shapes(args, stream, time_op, w_dev):
             y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
             us = time_op(lambda r: nv.w4a16_gemm(x, qs[r % count], out=y, workspace=ws), count)
             gbs = wb / (us * 1e-6) / 1e9
+            ceil = ceilings.get(str(int(wb)))
             res[m] = {"us": round(us, 3), "weight_gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                      "frac_read_ceiling": round(gbs / ceil["gbs"], 4) if ceil else None,
                       "path": "skinny" if nv.gemm_path(m, n, k) == nv.PATH_SKINNY else "tiled"}
         out["mlp"][f"{name}_n{n}_k{k}"] = res
         del qs, ws
@@ -620,7 +702,7 @@ def dispatch_sweep(args, stream, time_op, w_dev):
     return out
 
 
-def decoder_model(args, stream, w_dev):
+def decoder_model(args, stream, w_dev, ceilings):
     """The full synthetic 32-layer decoder (hidden 4096, MLP width 14336;
     per layer q, k, v, o 4096 x 4096, gate and up n = 14336, k = 4096, down
     n = 4096, k = 14336): one FourOverSix quantization pass over all 224
@@ -700,6 +782,7 @@ def decoder_model(args, stream, w_dev):
         gbs = out["packed_bytes"] / tg / 1e9
         out[f"gemm_pass_m{m}"] = {"us": round(tg * 1e6, 1), "weight_gbs": round(gbs, 1),
                                   "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                  "frac_read_ceiling_1GiB": round(gbs / ceilings[str(1 << 30)]["gbs"], 4),
                                   "us_per_layer": round(tg * 1e6 / layers, 2)}
     del packed
     torch.cuda.empty_cache()
@@ -717,85 +800,250 @@ def _cpu_model():
     return None
 
 
-def cpu_baseline(args, w_host, xs_dev, q_dev, step_bytes):
-    """The CPU oracle on the same workload (whole steps), timed on this host
-    on one thread and on all cores; its outputs are also compared with the
-    GPU's."""
+def _repeat(fn, seconds):
+    """Run fn until at least `seconds` have passed (at least once); returns
+    (runs, elapsed seconds)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            return reps, dt
+
+
+def cpu_baseline(args, w_host, xs_dev, q_dev):
+    """The CPU oracle (oracle/, as it stands) timed on this host beside the
+    GPU run, in the metric's unit: packed-weight GB/s of the W4A16 GEMM at
+    M = 1, 8, 16, 32, 48 on the single layer, each GEMM being the oracle's
+    float64 reference (exact dequantization, then a float64 product).  One
+    leg on one core (the process pinned to it with sched_setaffinity, BLAS /
+    torch / numpy on one thread), one on all cores of the affinity mask
+    (capped at 16, the GPU machine's CPU share): the dequantizations and the
+    quantizer on row chunks in a thread pool (blocks are independent once
+    the tensor amax is known; numpy releases the GIL), BLAS on every thread.
+    Also the quantizer, the MLP set (whole matrices: quantization time and
+    the M=4 share, GPU == oracle bit for bit), the large-M shapes on a row
+    sample, and the 32-layer decoder extrapolated from those rates (or run
+    on layers 0 and 31 with --cpu-full).  The oracle is a reported baseline,
+    not the optimisation target."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
     import torch
     from threadpoolctl import threadpool_limits
 
+    import bit_gemm_amd as nv
     import oracle
+    import synth
 
     xs = {m: x.cpu() for m, x in xs_dev.items()}
-    reps = 0
+    mask0 = os.sched_getaffinity(0)
+    ncores = max(1, min(16, len(mask0)))
     torch_threads = torch.get_num_threads()
+    wbytes = bytes_gemm_weights(N, K)
+
+    def chunks_of(n):
+        bounds = np.linspace(0, n, 4 * ncores + 1).astype(int)
+        return [(a, b) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
+
+    # ---- one core: the process pinned to a single CPU ----------------------
+    one_cpu = min(mask0)
+    os.sched_setaffinity(0, {one_cpu})
     torch.set_num_threads(1)
-    t0 = time.perf_counter()
-    with threadpool_limits(limits=1):
-        while True:
+    try:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
             r = oracle.quantize_fos(w_host)  # includes the amax pass
-            ys = {m: oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale) for m, x in xs.items()}
-            oracle.dequant(r.codes, r.scales, r.tensor_scale, "bf16")
-            reps += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds:
-                break
-    dt = time.perf_counter() - t0
-    one_core = {"value": round(step_bytes * reps / dt / 1e9, 3), "cores": 1, "steps": reps,
-                "seconds": round(dt, 1), "ms_per_step": round(dt * 1e3 / reps, 1)}
-    # All cores of this process's affinity mask (capped at 16, the GPU box's
-    # CPU share): blocks are independent once the tensor amax is known, so
-    # the oracle quantizer and dequant (also the float64 dequant inside each
-    # reference GEMM) run on row chunks in a thread pool (numpy releases the
-    # GIL in its array operations) and BLAS uses every thread for the
-    # float64 products.
-    ncores = max(1, min(16, len(os.sched_getaffinity(0))))
-    n = w_host.shape[0]
-    bounds = np.linspace(0, n, 4 * ncores + 1).astype(int)
-    chunks = [(a, b) for a, b in zip(bounds[:-1], bounds[1:]) if b > a]
-    reps_all = 0
+            tq1 = time.perf_counter() - t0
+
+            def gemms_one():
+                for x in xs.values():
+                    oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
+
+            reps1, dt1 = _repeat(gemms_one, args.cpu_seconds / 2)
+    finally:
+        os.sched_setaffinity(0, mask0)
+    one_core = {"value": round(len(xs) * wbytes * reps1 / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                "pinned_cpu": one_cpu, "gemm_passes": reps1, "seconds": round(dt1, 2),
+                "quantize_s": round(tq1, 2),
+                "quantize_weights_per_s": round(N * K / tq1, 1)}
+
+    # ---- all cores ----------------------------------------------------------
     torch.set_num_threads(ncores)
-    t0 = time.perf_counter()
     with threadpool_limits(limits=ncores), ThreadPoolExecutor(ncores) as ex:
-        while True:
-            amax = np.float32(max(ex.map(lambda ab: float(np.abs(w_host[ab[0]:ab[1]]).max()), chunks)))
-            parts = list(ex.map(lambda ab: oracle.quantize_fos(w_host[ab[0]:ab[1]], amax_in=amax), chunks))
-            codes = np.concatenate([q.codes for q in parts])
-            scales = np.concatenate([q.scales for q in parts])
-            s_t = parts[0].tensor_scale
-            for m, x in xs.items():  # oracle.gemm_ref's two steps, the dequant on row chunks
-                w64 = np.concatenate(list(ex.map(
-                    lambda ab: oracle.dequant_f64(codes[ab[0]:ab[1]], scales[ab[0]:ab[1]], s_t), chunks)))
-                np.asarray(x.float().numpy(), dtype=np.float64) @ w64.T
-            list(ex.map(lambda ab: oracle.dequant(codes[ab[0]:ab[1]], scales[ab[0]:ab[1]], s_t, "bf16"), chunks))
-            reps_all += 1
-            if time.perf_counter() - t0 >= args.cpu_seconds / 2:
-                break
-    dt_all = time.perf_counter() - t0
+        def quant_all(w):
+            ch = chunks_of(w.shape[0])
+            amax = np.float32(max(ex.map(lambda ab: float(np.abs(w[ab[0]:ab[1]]).max()), ch)))
+            parts = list(ex.map(lambda ab: oracle.quantize_fos(w[ab[0]:ab[1]], amax_in=amax), ch))
+            return (np.concatenate([q.codes for q in parts]), np.concatenate([q.scales for q in parts]),
+                    np.concatenate([q.m4_mask for q in parts]), parts[0].tensor_scale)
+
+        def gemm_all(x, codes, scales, s_t):  # oracle.gemm_ref's two steps, the dequant on row chunks
+            w64 = np.concatenate(list(ex.map(
+                lambda ab: oracle.dequant_f64(codes[ab[0]:ab[1]], scales[ab[0]:ab[1]], s_t), chunks_of(codes.shape[0]))))
+            return np.asarray(x.float().numpy(), dtype=np.float64) @ w64.T
+
+        def gemms_all():
+            for x in xs.values():
+                gemm_all(x, r.codes, r.scales, r.tensor_scale)
+
+        repsA, dtA = _repeat(gemms_all, args.cpu_seconds / 4)
+        qres = {}
+
+        def q_once():
+            qres["q"] = quant_all(w_host)
+
+        repsQ, dtQ = _repeat(q_once, args.cpu_seconds / 4)
+        all_ok = bool(np.array_equal(qres["q"][0], r.codes) and np.array_equal(qres["q"][1], r.scales))
+        quant = {"weights_per_s_all_cores": round(N * K * repsQ / dtQ, 1),
+                 "gbs_all_cores": round(N * K * (4 + 4.625) * repsQ / dtQ / 1e9, 3),
+                 "weights_per_s_one_core": one_core["quantize_weights_per_s"],
+                 "bytes_per_weight": "4 (amax pass) + 4.625 (read fp32, write codes, scales, mask)",
+                 "all_cores_matches_one_core": all_ok}
+
+        configs = {}
+        rates = {"gemm_gbs": {}, "quant_wps": []}
+        if not args.no_cpu_configs:
+            configs = cpu_configs(args, ex, quant_all, gemm_all, rates, q_dev.codes.device)
     torch.set_num_threads(torch_threads)
-    all_ok = bool(np.array_equal(codes, r.codes) and np.array_equal(scales, r.scales))
-    cpu = {"value": round(step_bytes * reps_all / dt_all / 1e9, 3), "unit": "GB/s", "cores": ncores,
-           "kind": "oracle",
-           "sample": f"{reps_all} whole steps of the same workload (4096x4096 quantize + 5 GEMMs + dequant), "
-                     f"{dt_all:.1f} s, {ncores} threads (quantize / dequant on row chunks, BLAS threads); "
-                     f"also {reps} steps on 1 thread in {dt:.1f} s",
-           "ms_per_step": round(dt_all * 1e3 / reps_all, 1), "one_core": one_core,
-           "cpu_model": _cpu_model(), "all_cores_matches_one_core": all_ok}
+
+    gemm_rate_all = len(xs) * wbytes * repsA / dtA / 1e9
+    # 32-layer decoder: extrapolated from the measured per-weight rates
+    shapes = synth.decoder_layer_shapes()
+    weights = 32 * sum(n * k for _, n, k in shapes)
+    packed_bytes = 32 * sum(bytes_gemm_weights(n, k) for _, n, k in shapes)
+    q_rate = quant["weights_per_s_all_cores"] if not rates["quant_wps"] else \
+        sum(rates["quant_wps"]) / len(rates["quant_wps"])
+    model = {"weights": weights, "quantize_s_extrapolated": round(weights / q_rate, 1),
+             "basis": "all-core oracle rates measured above (quantizer weights/s on the MLP matrices when "
+                      "they ran, else the single layer; GEMM packed-weight GB/s per M); every matrix of "
+                      "the decoder has the single layer's or an MLP matrix's shape"}
+    for m in (1, 48):
+        g = rates["gemm_gbs"].get(m)
+        if g:
+            model[f"gemm_pass_m{m}_s_extrapolated"] = round(packed_bytes / (g * 1e9), 2)
+    if args.cpu_full:
+        model["layers_0_31_measured"] = cpu_decoder_layers(args, quant_all, q_dev.codes.device)
+
+    cpu = {"value": round(gemm_rate_all, 4), "unit": "GB/s", "cores": ncores, "kind": "oracle",
+           "sample": f"{repsA} passes of the five float64 reference GEMMs (M = 1, 8, 16, 32, 48) on the "
+                     f"4096x4096 layer in {dtA:.1f} s on {ncores} threads, each GEMM dequantizing the packed "
+                     f"weights exactly; one-core leg: {reps1} passes in {dt1:.1f} s pinned to CPU {one_cpu}",
+           "one_core": one_core, "cpu_model": _cpu_model(), "quantizer": quant, "configs": configs,
+           "decoder_model_32_layers": model}
+
     # parity of what the GPU holds for this workload
     codes_ok = bool(np.array_equal(q_dev.codes.cpu().numpy(), r.codes))
     scales_ok = bool(np.array_equal(q_dev.scales.cpu().numpy(), r.scales))
     mask_ok = bool(np.array_equal(q_dev.m4_mask.cpu().numpy(), r.m4_mask))
-    import bit_gemm_amd as nv
-
     errs = {}
     for m, x in xs_dev.items():
+        ref = oracle.gemm_ref(xs[m], r.codes, r.scales, r.tensor_scale)
         y = nv.w4a16_gemm(x, q_dev).double().cpu().numpy()
-        errs[m] = float(np.linalg.norm(y - ys[m]) / np.linalg.norm(ys[m]))
+        errs[m] = float(np.linalg.norm(y - ref) / np.linalg.norm(ref))
     parity = {"quantize_bit_exact": codes_ok and scales_ok and mask_ok, "gemm_rel_err_max": max(errs.values()),
-              "gemm_rel_err_bound": 2e-3}
+              "gemm_rel_err_bound": 2e-3,
+              "mlp_set_bit_exact": all(c.get("gpu_equals_oracle", False) for c in configs.get("mlp_set", {}).values())
+              if configs.get("mlp_set") else None}
     return cpu, parity
+
+
+def cpu_configs(args, ex, quant_all, gemm_all, rates, dev):
+    """The oracle on the other workloads: the tiny layer in full; the MLP
+    set (up, gate, down at their seeds) quantized whole, with the M=4 share
+    of each matrix from the oracle and from the GPU (compared bit for bit),
+    and the float64 GEMM at M = 1, 4, 16, 48 on a 1024-row sample (rows are
+    independent once the matrix is quantized; the rate is per weight); the
+    large-M product at M = 64 ... 4096 on a 256-row sample of the 4096 x
+    4096 layer (seed 40)."""
+    import numpy as np
+    import torch
+
+    import bit_gemm_amd as nv
+    import oracle
+    import synth
+
+    out = {}
+    w, x = synth.tiny(0)
+    t0 = time.perf_counter()
+    q = oracle.quantize_fos(w)
+    oracle.gemm_ref(x, q.codes, q.scales, q.tensor_scale)
+    out["tiny_256x256_ms"] = round((time.perf_counter() - t0) * 1e3, 2)
+
+    mlp = {}
+    for name, n, k, seed in synth.MLP_SET["layers"]:
+        w = synth.student_t_weights(n, k, seed)
+        t0 = time.perf_counter()
+        codes, scales, mask, s_t = quant_all(w)
+        tq = time.perf_counter() - t0
+        rates["quant_wps"].append(n * k / tq)
+        g = nv.quantize_fos(torch.from_numpy(w).to(dev))
+        same = bool(np.array_equal(g.codes.cpu().numpy(), codes) and np.array_equal(g.scales.cpu().numpy(), scales)
+                    and np.array_equal(g.m4_mask.cpu().numpy(), mask))
+        share_gpu = float(g.m4_mask.to(torch.int64).sum().item()) / g.m4_mask.numel()
+        rows = 1024
+        gem = {}
+        for m in synth.MLP_SET["m"]:
+            xm = synth.activations(m, k, synth.activation_seed(m))
+            t0 = time.perf_counter()
+            gemm_all(xm, codes[:rows], scales[:rows], s_t)
+            dt = (time.perf_counter() - t0) * n / rows
+            gbs = bytes_gemm_weights(n, k) / dt / 1e9
+            rates["gemm_gbs"].setdefault(m, gbs)
+            gem[m] = {"s_extrapolated": round(dt, 3), "weight_gbs": round(gbs, 4)}
+        mlp[f"{name}_n{n}_k{k}_seed{seed}"] = {
+            "quantize_s": round(tq, 2), "quantize_weights_per_s": round(n * k / tq, 1),
+            "m4_share_oracle": round(float(mask.mean()), 4), "m4_share_gpu": round(share_gpu, 4),
+            "gpu_equals_oracle": same, "gemm_row_sample": rows, "gemm": gem}
+        del w, g
+        torch.cuda.empty_cache()
+    out["mlp_set"] = mlp
+    out["m4_share_pages_context"] = "40-43% of blocks, higher in MLP layers than in attention QKV (GPTQ on the " \
+                                    "real model's weights, another GPU); synthetic Student-t layers are not " \
+                                    "expected to match"
+    w = synth.student_t_weights(4096, 4096, 40)
+    n4, k4 = w.shape
+    codes, scales, _, s_t = quant_all(w)
+    rows = 256
+    lm = {}
+    for m in synth.LARGE_M["m"]:
+        xm = synth.activations(m, k4, synth.activation_seed(m))
+        t0 = time.perf_counter()
+        gemm_all(xm, codes[:rows], scales[:rows], s_t)
+        dt = (time.perf_counter() - t0) * n4 / rows
+        lm[m] = {"s_extrapolated": round(dt, 3), "tflops_fp64": round(2.0 * m * n4 * k4 / dt / 1e12, 4)}
+    out[f"large_m_{n4}x{k4}_seed40"] = {"row_sample": rows, "per_m": lm}
+    return out
+
+
+def cpu_decoder_layers(args, quant_all, dev):
+    """Layers 0 and 31 of the 32-layer decoder in full: each matrix drawn at
+    its seed, quantized by the oracle on all cores and by the GPU, compared
+    bit for bit, with its M=4 share."""
+    import numpy as np
+    import torch
+
+    import bit_gemm_amd as nv
+    import synth
+
+    res = {}
+    t_all = 0.0
+    for layer in (0, 31):
+        for j, (name, n, k) in enumerate(synth.decoder_layer_shapes()):
+            w = synth.student_t_weights(n, k, synth.decoder_weight_seed(layer, j))
+            t0 = time.perf_counter()
+            codes, scales, mask, _ = quant_all(w)
+            dt = time.perf_counter() - t0
+            t_all += dt
+            g = nv.quantize_fos(torch.from_numpy(w).to(dev))
+            same = bool(np.array_equal(g.codes.cpu().numpy(), codes) and np.array_equal(g.scales.cpu().numpy(), scales)
+                        and np.array_equal(g.m4_mask.cpu().numpy(), mask))
+            res[f"layer{layer}_{name}"] = {"quantize_s": round(dt, 2), "m4_share": round(float(mask.mean()), 4),
+                                           "gpu_equals_oracle": same}
+            del w, g
+    res["quantize_s_total"] = round(t_all, 2)
+    return res
 
 
 if __name__ == "__main__":

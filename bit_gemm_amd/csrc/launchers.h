@@ -93,4 +93,11 @@ hipError_t launch_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u
 
 hipError_t launch_selftest_cvt(uint32_t* counters, hipStream_t stream);
 
+// Read-only stream over `bytes` (a multiple of 16) of device memory:
+// `grid` workgroups of 256 threads, `loads_in_flight` (2, 4, 8 or 16)
+// 16-byte loads per thread in flight, non-temporal loads if `nontemporal`;
+// sink: 64 device words, written only for one data-dependent value.
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int grid, int loads_in_flight, int nontemporal,
+                              uint32_t* sink, hipStream_t stream);
+
 }  // namespace nvfp4
