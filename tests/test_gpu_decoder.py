@@ -8,7 +8,8 @@ n = 14336, k = 4096; down: n = 4096, k = 14336): the FourOverSix codes,
 scales, M=4 mask, amax and tensor scale bit-exact with the oracle over the
 whole matrix, and the W4A16 GEMM at the two token counts the decoder passes
 run (1 and 48, the launch configuration of those passes: automatic path)
-within the relative Frobenius bound of the float64 oracle.
+within the relative Frobenius bounds of the float64 oracle (bf16 and fp32
+output) and the per-element bound of tests/gemm_bounds.py.
 """
 
 import numpy as np
@@ -18,6 +19,7 @@ import torch
 import bit_gemm_amd as nv
 import oracle
 import synth
+from gemm_bounds import assert_gemm_elementwise
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +44,8 @@ def test_decoder_layer_matrix(layer, j):
     for m in (1, 48):
         x = synth.activations(m, k, synth.activation_seed(m))
         ref = np.asarray(x.float().numpy(), dtype=np.float64) @ w_hat.T
-        y = nv.w4a16_gemm(x.cuda(), q).double().cpu().numpy()
-        err = np.linalg.norm(y - ref) / np.linalg.norm(ref)
-        assert err <= 2e-3, (name, m, err)
+        for dt, tol in ((torch.bfloat16, 2e-3), (torch.float32, 1e-5)):
+            y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt).double().cpu().numpy()
+            err = np.linalg.norm(y - ref) / np.linalg.norm(ref)
+            assert err <= tol, (name, m, dt, err)
+            assert_gemm_elementwise(y, x, w_hat, ref, dt, f"layer {layer} {name} m={m} {dt}")
