@@ -68,6 +68,8 @@ SIGNATURES = {
     "nvfp4_w4a4_gemm": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p, _c_size, _c_p]),
     "nvfp4_selftest_cvt": (_c_int, [_c_p, _c_p]),
     "nvfp4_stream_read": (_c_int, [_c_p, _c_size, _c_int, _c_int, _c_int, _c_p, _c_p]),
+    "nvfp4_w4a16_gemm_noalloc": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_i64, _c_int, _c_p]),
+    "nvfp4_noalloc_scratch_bytes": (_c_size, []),
     "nvfp4_status_string": (ctypes.c_char_p, [_c_int]),
     "nvfp4_last_error": (ctypes.c_char_p, []),
     "nvfp4_version": (_c_int, []),
@@ -308,6 +310,27 @@ def w4a16_gemm(x: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.b
     _check(lib().nvfp4_w4a16_gemm_ex(
         _ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), m, n, k, code,
         _ptr(workspace), ws_bytes, path, split_k, impl, _stream(dev)))
+    return out
+
+
+def w4a16_gemm_noalloc(x: torch.Tensor, q: NVFP4Weight, out: torch.Tensor) -> torch.Tensor:
+    """nvfp4_w4a16_gemm_noalloc: the W4A16 GEMM into a caller-provided
+    output (bf16 or fp32 [m, n]) without a workspace and without allocating
+    (split-K partials go to the library's fixed per-GPU scratch)."""
+    n, k = q.check(gpu=False)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}], got {tuple(getattr(x, 'shape', ()))}")
+    m = x.shape[0]
+    if not isinstance(out, torch.Tensor) or out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out must be a float32 or bfloat16 tensor")
+    dev = q.codes.device
+    _need(x, "x", torch.bfloat16, gpu=False)
+    _need(out, "out", out.dtype, (m, n), gpu=False)
+    q.check(dev)
+    _on_gpu(dev, (x, "x"), (out, "out"))
+    code = F32 if out.dtype == torch.float32 else BF16
+    _check(lib().nvfp4_w4a16_gemm_noalloc(_ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out),
+                                          m, n, k, code, _stream(dev)))
     return out
 
 

@@ -122,6 +122,15 @@ int choose_path(int64_t m, int64_t n, int64_t k, int path) {
 
 }  // namespace
 
+namespace nvfp4 {
+// Error reporting and the device check for entry points defined in other
+// sources (the no-allocation GEMM in noalloc.hip).
+void clear_error() { g_last_error.clear(); }
+int set_error(int status, const char* msg) { return fail(status, "%s", msg); }
+int set_hip_error(hipError_t e, const char* where) { return hip_fail(e, where); }
+int device_ok() { return check_device(); }
+}  // namespace nvfp4
+
 extern "C" {
 
 NVFP4_API int nvfp4_version(void) { return 100; }  // 0.1.0

@@ -91,6 +91,13 @@ hipError_t launch_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u
                        uint8_t* codes, uint8_t* scales, uint8_t* m4_mask, void* workspace,
                        int impl, hipStream_t stream);
 
+// Thread-local error text and status codes of the C ABI (api.cpp), for
+// entry points defined in other sources.
+void clear_error();
+int set_error(int status, const char* msg);
+int set_hip_error(hipError_t e, const char* where);
+int device_ok();  // NVFP4_OK if the current device is gfx950, else the error status
+
 hipError_t launch_selftest_cvt(uint32_t* counters, hipStream_t stream);
 
 // Read-only stream over `bytes` (a multiple of 16) of device memory:

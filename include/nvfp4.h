@@ -251,6 +251,28 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
                                   size_t workspace_bytes, int path, int split_k, int impl,
                                   void* stream);
 
+/*
+ * nvfp4_w4a16_gemm_noalloc - nvfp4_w4a16_gemm without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results (the same kernels: bit-identical to
+ * nvfp4_w4a16_gemm) and errors otherwise.
+ *
+ * When the plan splits K, its fp32 partial sums go to a fixed per-GPU
+ * device array of nvfp4_noalloc_scratch_bytes() bytes (32 MiB) that the
+ * library holds on each GPU it runs on until the process ends; its address
+ * is looked up once per device on the first call made there.  A shape whose
+ * plan needs more (nvfp4_w4a16_gemm_workspace_size(m, n, k) larger than
+ * that) is rejected with NVFP4_ERR_WORKSPACE_TOO_SMALL before any launch.
+ * The call allocates nothing.  All calls on one GPU share the array: calls
+ * that overlap on one GPU (other streams, other threads) race; serialize
+ * them.  The array's contents on entry do not matter.
+ */
+NVFP4_API int nvfp4_w4a16_gemm_noalloc(const void* x, const uint8_t* codes, const uint8_t* scales,
+                                       const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                                       int out_dtype, void* stream);
+NVFP4_API size_t nvfp4_noalloc_scratch_bytes(void);
+
 /* The path NVFP4_PATH_AUTO picks for (m, n, k): NVFP4_PATH_SKINNY or
  * NVFP4_PATH_TILED. */
 NVFP4_API int nvfp4_w4a16_gemm_path(int64_t m, int64_t n, int64_t k);

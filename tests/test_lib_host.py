@@ -113,6 +113,20 @@ def test_stream_read_rejects_bad_arguments_on_host(L):
     assert r(ODD, 1024, 512, 8, 1, FAKE, None) == 3
 
 
+def test_noalloc_gemm_rejects_on_host(L):
+    g = L.nvfp4_w4a16_gemm_noalloc
+    assert L.nvfp4_noalloc_scratch_bytes() == 32 << 20
+    # a plan whose split-K partials exceed the fixed scratch: rejected before any HIP call
+    assert L.nvfp4_w4a16_gemm_workspace_size(64, 14336, 14336) > L.nvfp4_noalloc_scratch_bytes()
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 64, 14336, 14336, 0, None) == 4
+    assert "no-allocation" in L.nvfp4_last_error().decode()
+    # invalid arguments: the GEMM's own validation
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 24, 0, None) == 2
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 32, 64, 7, None) == 1
+    assert g(FAKE, FAKE, FAKE, FAKE, ODD, 8, 32, 64, 0, None) == 3
+    assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 32, 64, 0, None) == 0  # empty: nothing to do
+
+
 def test_gemm_dx_rejects_bad_arguments_on_host(L):
     g = L.nvfp4_w4a16_gemm_dx
     assert g(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 8, 24, 0, None, 0, None) == 2  # k % 16
