@@ -6,6 +6,14 @@
 // the weights from HBM ("SOAR Weekly Champion Notes 08 ...", section "01").
 //
 // Kernels:
+//  * k_skinny_pk (4 < m <= 16, k % 512 == 0, k <= 4096): a persistent form
+//    of the full-K layout below; a workgroup per CU walks its 16-row tiles
+//    with the activations in LDS once and the next two tiles' weights in
+//    flight.  No workspace, one launch.
+//  * k_skinny_fx (16 < m <= 64 with at most one 16-row tile per CU, k <=
+//    4096): a workgroup per tile over the whole K, each wave streaming its
+//    K slice and the activations of each step through a private LDS double
+//    buffer.  No workspace, one launch.
 //  * k_skinny_fk (2 < m <= 16, except 8 < m <= 16 on large matrices: more
 //    than 4096 rows or 2^25 weights, K % 512 == 0, and 4 < m <= 8 there
 //    with K > 4096, which take the streaming kernel below): a workgroup owns 16 weight rows over the whole K and its
@@ -41,6 +49,7 @@ constexpr int kRowsPerWg = 16 * kWaves;
 constexpr int kStepK = 128;     // K per step (4 MFMAs of K=32)
 constexpr int kMaxSteps = 16;   // K steps per chunk held in registers
 constexpr int kLdsBudget = 131072;
+constexpr int kFxMaxTiles = 256;  // the single-launch 16 < m <= 64 kernel: at most one 16-row tile per CU
 
 template <int IMPL>
 __device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sigma) {
@@ -375,6 +384,339 @@ __global__ __launch_bounds__(512) void k_skinny_dot(const uint16_t* __restrict__
     float t = red[m * 16 + r16];
     for (int w = 1; w < nwaves; ++w) t += red[(w * MR + m) * 16 + r16];
     store_out(y, (int64_t)m * N + row, t * s_t, out_f32);
+  }
+}
+
+// Persistent full-K kernel (m <= 16, k = W * ROUNDS * 512 for W <= 8 waves
+// and ROUNDS in {1, 2, 4}): the full-K layout above, but a workgroup walks
+// several 16-row tiles (tiles blockIdx.x, + gridDim.x, ...) and keeps the
+// activations in LDS for all of them.  Wave w owns the K slices r W + w
+// (r < ROUNDS) of every tile; at the start it copies x[0:MR, its slices]
+// into its own LDS region with the LDS DMA (one instruction per token row
+// and slice: 512 contiguous bf16, whole cache lines; token rows >= m repeat
+// row m - 1, whose outputs are not stored), so the activations cross L2 ->
+// CU once per workgroup instead of once per tile, and no load of x stands
+// in front of the weight loads.  Per tile a lane loads, per slice, the 8
+// scale bytes and four 16-byte code pieces of its quarter (the full-K
+// kernel's layout); the next two tiles' loads are in flight while a tile is
+// consumed, and step s waits only until its own loads have landed
+// (inline-asm loads with counted waits; loads return in issue order).  The
+// W partial tiles are added in wave order through LDS (two buffers by tile
+// parity) after a bare barrier (a workgroup fence would also wait for the
+// next tile's loads); one wave per tile, in turn, adds and stores.  MR <= 2
+// uses VALU dot products, larger MR the 16x16x32 MFMA.
+// VALU dot products for one or two tokens with the hardware FP4 decode; the
+// portable decode's dot form needs more registers than the in-flight loads
+// leave, so it takes the MFMA form (token rows >= m repeat row m - 1).
+constexpr bool pk_dot_path(int mr, int impl) { return mr <= 2 && impl == kConvHw; }
+
+template <int ROUNDS>
+struct PkTile {
+  u32x4_t cw[ROUNDS][kSpw];  // codes: slice r, step s (32 codes of row r16 at k = 128 g + 32 s)
+  u32x2_t sw[ROUNDS];        // the 8 scale bytes of the lane's quarter of slice r
+};
+
+constexpr int kPkLoadsPerSlice = 1 + kSpw;  // scales, then the four code pieces
+constexpr int kPkAhead = 2;                  // tiles whose loads are in flight while one is consumed
+constexpr int kPkRow = kWaveK + 8;          // LDS row of one token and slice (bf16), 16-byte pad
+
+template <int R, int ROUNDS>
+__device__ __forceinline__ void pk_issue(PkTile<ROUNDS>& T, const uint8_t* const* cp, const uint8_t* const* sp) {
+  load_b64_async<0>(T.sw[R], sp[R]);
+  load_b128_async<0>(T.cw[R][0], cp[R]);
+  load_b128_async<16>(T.cw[R][1], cp[R]);
+  load_b128_async<32>(T.cw[R][2], cp[R]);
+  load_b128_async<48>(T.cw[R][3], cp[R]);
+  if constexpr (R + 1 < ROUNDS) pk_issue<R + 1, ROUNDS>(T, cp, sp);
+}
+
+// Slice R, step S of a tile (MFMA), then the following steps.  AFTER = loads
+// issued after this tile's (the next tile's).
+template <int R, int S, int MR, int IMPL, int ROUNDS, int AFTER>
+__device__ __forceinline__ void pk_mfma(PkTile<ROUNDS>& T, const uint16_t* xw, int g, int rb, f32x4_t& acc) {
+  wait_vm_b64<(kSpw - 1 - S) + kPkLoadsPerSlice * (ROUNDS - 1 - R) + AFTER>(T.cw[R][S], T.sw[R]);
+  const uint32_t s2 = (T.sw[R][S >> 1] >> (16 * (S & 1))) & 0xFFFFu;
+  const float sg0 = scale_at<IMPL, 0>(s2), sg1 = scale_at<IMPL, 1>(s2);
+  bf16x8_t a[4];
+  a[0] = dequant8<IMPL>(T.cw[R][S][0], sg0);
+  a[1] = dequant8<IMPL>(T.cw[R][S][1], sg0);
+  a[2] = dequant8<IMPL>(T.cw[R][S][2], sg1);
+  a[3] = dequant8<IMPL>(T.cw[R][S][3], sg1);
+  const uint16_t* xb = xw + (R * MR + rb) * kPkRow + g * kQuarter + 32 * S;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(xb + 8 * j);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
+  }
+  if constexpr (S + 1 < kSpw)
+    pk_mfma<R, S + 1, MR, IMPL, ROUNDS, AFTER>(T, xw, g, rb, acc);
+  else if constexpr (R + 1 < ROUNDS)
+    pk_mfma<R + 1, 0, MR, IMPL, ROUNDS, AFTER>(T, xw, g, rb, acc);
+}
+
+// The same for the dot kernel: per token, the two 16-code blocks of the
+// step summed in fp32 and scaled by their sigma.
+template <int R, int S, int MR, int IMPL, int ROUNDS, int AFTER>
+__device__ __forceinline__ void pk_dot(PkTile<ROUNDS>& T, const uint16_t* xw, int g, float (&acc)[MR]) {
+  wait_vm_b64<(kSpw - 1 - S) + kPkLoadsPerSlice * (ROUNDS - 1 - R) + AFTER>(T.cw[R][S], T.sw[R]);
+  const uint32_t s2 = (T.sw[R][S >> 1] >> (16 * (S & 1))) & 0xFFFFu;
+  const float sg0 = scale_at<IMPL, 0>(s2), sg1 = scale_at<IMPL, 1>(s2);
+#pragma unroll
+  for (int m = 0; m < MR; ++m) {
+    const uint16_t* xb = xw + (R * MR + m) * kPkRow + g * kQuarter + 32 * S;
+    const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(xb);
+    const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(xb + 8);
+    const u32x4_t x2 = *reinterpret_cast<const u32x4_t*>(xb + 16);
+    const u32x4_t x3 = *reinterpret_cast<const u32x4_t*>(xb + 24);
+    const float b0 = dot8<IMPL>(T.cw[R][S][1], x1, dot8<IMPL>(T.cw[R][S][0], x0, 0.0f));
+    const float b1 = dot8<IMPL>(T.cw[R][S][3], x3, dot8<IMPL>(T.cw[R][S][2], x2, 0.0f));
+    acc[m] += sg0 * b0;
+    acc[m] += sg1 * b1;
+  }
+  if constexpr (S + 1 < kSpw)
+    pk_dot<R, S + 1, MR, IMPL, ROUNDS, AFTER>(T, xw, g, acc);
+  else if constexpr (R + 1 < ROUNDS)
+    pk_dot<R + 1, 0, MR, IMPL, ROUNDS, AFTER>(T, xw, g, acc);
+}
+
+template <int MR, int IMPL, int ROUNDS>
+__global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ x,
+                                                   const uint8_t* __restrict__ codes,
+                                                   const uint8_t* __restrict__ scales,
+                                                   const float* __restrict__ tensor_scale,
+                                                   void* __restrict__ y, int M, int N, int K, int out_f32) {
+  constexpr bool kDot = pk_dot_path(MR, IMPL);
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int g = lane >> 4, r16 = lane & 15;
+  uint16_t* xw = reinterpret_cast<uint16_t*>(lds) + wave * (ROUNDS * MR * kPkRow);
+  uint8_t* red = lds + (size_t)W * ROUNDS * MR * kPkRow * 2;  // [2][W] partial tiles
+  const float s_t = tensor_scale[0];
+
+  // activations of this wave's slices, once (LDS DMA: lane l -> bf16 8l .. 8l + 7)
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r)
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      copy16_to_lds(x + (int64_t)min(m, M - 1) * K + (r * W + wave) * kWaveK + 8 * lane,
+                    reinterpret_cast<uint8_t*>(xw + (r * MR + m) * kPkRow));
+
+  const int ntiles = (N + 15) / 16;
+  const int cnt = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // tiles of this workgroup
+  int64_t slice_c[ROUNDS], slice_s[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    slice_c[r] = (int64_t)(r * W + wave) * (kWaveK / 2) + 16 * (kSpw * g);
+    slice_s[r] = (int64_t)(r * W + wave) * (kWaveK / 16) + 8 * g;
+  }
+  // loads of this workgroup's tile i; past the last tile every lane reads
+  // the first bytes of the buffers instead (in bounds, one cache line per
+  // instruction, never used), so the count of loads in flight stays fixed
+  auto issue = [&](PkTile<ROUNDS>& T, int i) __attribute__((always_inline)) {
+    const bool real = i < cnt;
+    const int t = (int)blockIdx.x + i * (int)gridDim.x;
+    const int64_t row = real ? min(16 * t + r16, N - 1) : 0;
+    const uint8_t* cp[ROUNDS];
+    const uint8_t* sp[ROUNDS];
+#pragma unroll
+    for (int r = 0; r < ROUNDS; ++r) {
+      cp[r] = real ? codes + row * (K / 2) + slice_c[r] : codes;
+      sp[r] = real ? scales + row * (K / 16) + slice_s[r] : scales;
+    }
+    pk_issue<0, ROUNDS>(T, cp, sp);
+  };
+  auto finish = [&](int i, auto& acc) __attribute__((always_inline)) {  // add the W partial tiles of tile i and store it
+    const int par = i & 1;
+    const int t = (int)blockIdx.x + i * (int)gridDim.x;
+    if constexpr (kDot) {
+      float* rf = reinterpret_cast<float*>(red) + (size_t)par * W * MR * 16;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) {  // lane groups g = 0..3 of a row: ((g0 + g1) + (g2 + g3))
+        acc[m] += __shfl_xor(acc[m], 16, 64);
+        acc[m] += __shfl_xor(acc[m], 32, 64);
+      }
+      if (g == 0) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) rf[(wave * MR + m) * 16 + r16] = acc[m];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (wave == i % W && lane < MR * 16) {
+        const int m = lane >> 4, row = 16 * t + (lane & 15);
+        float v = rf[lane];
+        for (int w = 1; w < W; ++w) v += rf[w * MR * 16 + lane];
+        if (m < M && row < N) store_out(y, (int64_t)m * N + row, v * s_t, out_f32);
+      }
+    } else {
+      f32x4_t* rf = reinterpret_cast<f32x4_t*>(red) + (size_t)par * W * 64;
+      rf[wave * 64 + lane] = acc;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (wave == i % W) {  // lane holds D[n = 4 g + e][m = r16]
+        f32x4_t v = rf[lane];
+        for (int w = 1; w < W; ++w) {
+          const f32x4_t u = rf[w * 64 + lane];
+          v[0] += u[0];
+          v[1] += u[1];
+          v[2] += u[2];
+          v[3] += u[3];
+        }
+        const int nb = 16 * t + 4 * g;
+        if (r16 < M) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (nb + e < N) store_out(y, (int64_t)r16 * N + nb + e, v[e] * s_t, out_f32);
+        }
+      }
+    }
+  };
+  auto consume = [&](PkTile<ROUNDS>& T, int i) __attribute__((always_inline)) {
+    if constexpr (kDot) {
+      float acc[MR];
+#pragma unroll
+      for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
+      pk_dot<0, 0, MR, IMPL, ROUNDS, kPkAhead * kPkLoadsPerSlice * ROUNDS>(T, xw, g, acc);
+      finish(i, acc);
+    } else {
+      f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pk_mfma<0, 0, MR, IMPL, ROUNDS, kPkAhead * kPkLoadsPerSlice * ROUNDS>(T, xw, g, min(r16, MR - 1), acc);
+      finish(i, acc);
+    }
+  };
+  // three register sets: while tile i is consumed the loads of tiles i + 1
+  // and i + 2 are in flight
+  PkTile<ROUNDS> A, B, C;
+  issue(A, 0);
+  issue(B, 1);
+  for (int i = 0; i < cnt; i += 3) {
+    issue(C, i + 2);
+    consume(A, i);
+    if (i + 1 >= cnt) break;
+    issue(A, i + 3);
+    consume(B, i + 1);
+    if (i + 2 >= cnt) break;
+    issue(B, i + 4);
+    consume(C, i + 2);
+  }
+  wait_vm_all();  // the last (unused) loads land before the wave ends
+}
+
+// Single-launch full-K kernel for 16 < m <= 64 on matrices with about one
+// 16-row tile per CU (k = W * NSTEP * 128): a workgroup owns one tile of 16
+// weight rows over the whole K, so no fp32 partial planes and no second
+// launch; its W waves split K into slices of NSTEP steps of 128.  The
+// activations (up to 64 x k) do not fit in LDS, so each wave streams its
+// slice: per step a lane loads its row's 32 codes at k = 128 s + 32 g (the
+// four lanes of a row read 64 contiguous bytes) and their two scale bytes,
+// and the wave copies the step's activations (16 MT token rows x 256 bytes,
+// whole cache lines; piece q of row r at slot q ^ (r % 16), so the B
+// fragment reads of 16 rows hit 16 bank groups) into one of its two private
+// LDS buffers with the LDS DMA.  Step s + 1's loads are in flight while
+// step s is dequantized and multiplied; step s waits (counted, inline-asm
+// loads) only for its own loads, and a buffer is refilled only after the
+// step that read it.  No barrier until the W partial tiles are added in wave
+// order through LDS.  Token rows >= m repeat row m - 1 (outputs not stored).
+template <int MT>
+__device__ __forceinline__ void fx_issue(u32x4_t& cw, uint32_t& sb, const uint8_t* cp, const uint8_t* sp,
+                                         const uint16_t* const* xsrc, uint8_t* buf, int s) {
+  load_b128_async<0>(cw, cp + 64 * s);
+  load_u16_async<0>(sb, sp + 8 * s);
+#pragma unroll
+  for (int c = 0; c < 4 * MT; ++c) copy16_to_lds(xsrc[c] + kStepK * s, buf + 1024 * c);
+  asm volatile("" ::: "memory");
+}
+
+constexpr int fx_loads_per_step(int mt) { return 2 + 4 * mt; }
+
+// Step S of NSTEP (register set S % 2, LDS buffer S % 2), then the rest.
+template <int S, int NSTEP, int MT, int IMPL>
+__device__ __forceinline__ void fx_steps(u32x4_t (&cw)[2], uint32_t (&sb)[2], const uint8_t* cp, const uint8_t* sp,
+                                         const uint16_t* const* xsrc, uint8_t* xbuf, int g, int c16,
+                                         f32x4_t (&acc)[MT]) {
+  constexpr int cur = S & 1;
+  wait_vm<(S + 1 < NSTEP) ? fx_loads_per_step(MT) : 0>(cw[cur], sb[cur]);
+  const float sg0 = scale_at<IMPL, 0>(sb[cur]), sg1 = scale_at<IMPL, 1>(sb[cur]);
+  bf16x8_t a[4];
+  a[0] = dequant8<IMPL>(cw[cur][0], sg0);
+  a[1] = dequant8<IMPL>(cw[cur][1], sg0);
+  a[2] = dequant8<IMPL>(cw[cur][2], sg1);
+  a[3] = dequant8<IMPL>(cw[cur][3], sg1);
+  const uint8_t* buf = xbuf + cur * (4096 * MT);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const u32x4_t b = *reinterpret_cast<const u32x4_t*>(buf + 256 * (16 * mt + c16) + 16 * ((4 * g + j) ^ c16));
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, b), acc[mt], 0, 0, 0);
+    }
+  if constexpr (S + 2 < NSTEP) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this buffer's reads are done before it is refilled
+    fx_issue<MT>(cw[cur], sb[cur], cp, sp, xsrc, xbuf + cur * (4096 * MT), S + 2);
+  }
+  if constexpr (S + 1 < NSTEP) fx_steps<S + 1, NSTEP, MT, IMPL>(cw, sb, cp, sp, xsrc, xbuf, g, c16, acc);
+}
+
+template <int MT, int IMPL, int NSTEP>
+__global__ __launch_bounds__(512) void k_skinny_fx(const uint16_t* __restrict__ x,
+                                                   const uint8_t* __restrict__ codes,
+                                                   const uint8_t* __restrict__ scales,
+                                                   const float* __restrict__ tensor_scale,
+                                                   void* __restrict__ y, int M, int N, int K, int out_f32) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  uint8_t* xbuf = lds + (size_t)wave * 2 * 4096 * MT;            // [2][16 MT rows][256 bytes]
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + (size_t)W * 2 * 4096 * MT);  // [W][MT][64]
+  const float s_t = tensor_scale[0];
+  const int n0 = blockIdx.x * 16;
+  const int k0 = wave * NSTEP * kStepK;
+  const int row = min(n0 + c16, N - 1);  // rows past n read row n - 1 (real data); outputs dropped
+  const uint8_t* cp = codes + (int64_t)row * (K / 2) + k0 / 2 + 16 * g;
+  const uint8_t* sp = scales + (int64_t)row * (K / 16) + k0 / 16 + 2 * g;
+  // DMA instruction c of a step: token rows 4c .. 4c + 3, lane l -> row
+  // 4c + l / 16, piece (l % 16) ^ (row % 16)
+  const uint16_t* xsrc[4 * MT];
+#pragma unroll
+  for (int c = 0; c < 4 * MT; ++c) {
+    const int rr = 4 * c + (lane >> 4);
+    xsrc[c] = x + (int64_t)min(rr, M - 1) * K + k0 + 8 * ((lane & 15) ^ (rr & 15));
+  }
+  u32x4_t cw[2];
+  uint32_t sb[2];
+  fx_issue<MT>(cw[0], sb[0], cp, sp, xsrc, xbuf, 0);
+  if constexpr (NSTEP > 1) fx_issue<MT>(cw[1], sb[1], cp, sp, xsrc, xbuf + 4096 * MT, 1);
+  f32x4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  fx_steps<0, NSTEP, MT, IMPL>(cw, sb, cp, sp, xsrc, xbuf, g, c16, acc);
+
+  // the W partial tiles, added in wave order; lane holds D[n = 4 g + e][m = 16 mt + c16]
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  for (int i = threadIdx.x; i < MT * 64; i += blockDim.x) {
+    f32x4_t v = red[i];
+    for (int w = 1; w < W; ++w) {
+      const f32x4_t u = red[w * MT * 64 + i];
+      v[0] += u[0];
+      v[1] += u[1];
+      v[2] += u[2];
+      v[3] += u[3];
+    }
+    const int mt = i >> 6, l = i & 63;
+    const int m = 16 * mt + (l & 15), nb = n0 + 4 * (l >> 4);
+    if (m >= M) continue;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (nb + e < N) store_out(y, (int64_t)m * N + nb + e, v[e] * s_t, out_f32);
   }
 }
 
@@ -911,6 +1253,73 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
   }
 }
 
+// LDS bytes of the persistent full-K kernel: the activation slices of W
+// waves plus two buffers of W partial tiles.
+size_t pk_lds_bytes(int mr, int w, int rounds, bool dot) {
+  const size_t part = dot ? (size_t)mr * 16 * sizeof(float) : 64 * sizeof(f32x4_t);
+  return (size_t)w * rounds * mr * kPkRow * 2 + 2 * (size_t)w * part;
+}
+
+template <int MR, int IMPL, int ROUNDS>
+hipError_t launch_pk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
+                     const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+  const size_t lds = pk_lds_bytes(MR, p.waves, ROUNDS, pk_dot_path(MR, IMPL));
+  hipError_t e = set_lds_limit<k_skinny_pk<MR, IMPL, ROUNDS>>(lds);
+  if (e != hipSuccess) return e;
+  // persistent: at most as many workgroups as can be resident at once
+  // (per device, kernel and block shape; a host query, no allocation)
+  static std::atomic<int> resident[64][9];
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int per_cu = (dev >= 0 && dev < 64) ? resident[dev][p.waves].load(std::memory_order_relaxed) : 0;
+  if (per_cu <= 0) {
+    int cus = 0, blocks = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, k_skinny_pk<MR, IMPL, ROUNDS>, 64 * p.waves, lds);
+    if (e != hipSuccess) return e;
+    per_cu = cus;  // one workgroup per CU (measured faster than filling every resident slot)
+    (void)blocks;
+    if (dev >= 0 && dev < 64) resident[dev][p.waves].store(per_cu, std::memory_order_relaxed);
+  }
+  const int tiles = (N + 15) / 16;
+  const dim3 grid((unsigned)(tiles < per_cu ? tiles : per_cu));  // per_cu: workgroups resident at once
+  hipLaunchKernelGGL((k_skinny_pk<MR, IMPL, ROUNDS>), grid, dim3(64 * p.waves), lds, stream, x, codes, scales, ts, y,
+                     M, N, K, out_f32);
+  return hipGetLastError();
+}
+
+template <int MR, int IMPL>
+hipError_t launch_pk_r(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
+                       const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+  if (p.pk_rounds != 1) return hipErrorInvalidValue;  // the planner takes one slice per wave only
+  return launch_pk<MR, IMPL, 1>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+}
+
+size_t fx_lds_bytes(int mt, int w) { return (size_t)w * mt * (2 * 4096 + 1024); }
+
+template <int MT, int IMPL, int NSTEP>
+hipError_t launch_fx(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
+                     const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+  const size_t lds = fx_lds_bytes(MT, p.waves);
+  hipError_t e = set_lds_limit<k_skinny_fx<MT, IMPL, NSTEP>>(lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_skinny_fx<MT, IMPL, NSTEP>), dim3((unsigned)((N + 15) / 16)), dim3(64 * p.waves), lds, stream,
+                     x, codes, scales, ts, y, M, N, K, out_f32);
+  return hipGetLastError();
+}
+
+template <int MT, int IMPL>
+hipError_t launch_fx_n(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
+                       const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+  switch (p.fx_steps) {
+    case 4: return launch_fx<MT, IMPL, 4>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+    case 8: return launch_fx<MT, IMPL, 8>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <auto Kernel>
 hipError_t launch_fk_kernel(dim3 grid, int waves, size_t lds, hipStream_t stream,
                             const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
@@ -983,6 +1392,13 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
                      const uint8_t* codes, const uint8_t* scales, const float* ts, void* y,
                      float* ws, int M, int N, int K, int out_f32) {
   if constexpr (MT == 1) {
+    if (p.splits == 0 && p.pk_rounds > 0) {  // persistent full-K kernel
+      if constexpr (K32) {  // the planner takes it for 4 < m <= 16
+        if (M <= 8) return launch_pk_r<8, IMPL>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+        return launch_pk_r<16, IMPL>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+      }
+      return hipErrorInvalidValue;
+    }
     if (p.splits == 0) {  // full-K kernel (one token tile only)
       const int mr = M <= 1 ? 1 : (M <= 2 ? 2 : (M <= 4 ? 4 : (M <= 8 ? 8 : 16)));
       switch (mr) {
@@ -993,6 +1409,10 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
         default: return launch_fk<16, IMPL, K32>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
       }
     }
+  }
+  if (p.fx_steps > 0) {
+    if constexpr (K32 && MT >= 2) return launch_fx_n<MT, IMPL>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+    return hipErrorInvalidValue;
   }
   if (p.str_rows > 0) {
     if constexpr (K32) {
@@ -1058,7 +1478,81 @@ hipError_t launch_split_reduce(const float* ws, const float* tensor_scale, void*
   return hipGetLastError();
 }
 
+namespace {
+// The persistent full-K kernel's shape for (m, k): W waves x `rounds` K
+// slices of 512 covering k exactly (W <= 8, rounds in {1, 2, 4}, fewest
+// rounds first), with the activations and partial tiles within the LDS
+// budget.  False when there is none.
+bool pk_shape(int64_t m, int64_t k, int* waves, int* rounds) {
+  // measured against the full-K and streaming kernels on 4096 x 4096 and
+  // 14336 x 4096 (one 512-wide K slice per wave): faster for 4 < m <= 16
+  // (14336 x 4096 at m = 8 / 16: 12.3 / 13.2 against 13.6 / 14.6 us;
+  // 4096 x 4096: 5.75 / 6.53 against 5.97 / 6.75 us), even or slower for
+  // m <= 4; with several slices per wave (k > 4096: 4096 x 14336) slower
+  if (m <= 4 || m > 16 || k < kWaveK || k % kWaveK != 0) return false;
+  const int64_t slices = k / kWaveK;
+  if (slices > 8) return false;
+  const int mr = m <= 8 ? 8 : 16;
+  if (pk_lds_bytes(mr, (int)slices, 1, false) > (size_t)159 * 1024) return false;
+  *waves = (int)slices;
+  *rounds = 1;
+  return true;
+}
+}  // namespace
+
+namespace {
+// The single-launch full-K kernel's shape for 16 < m <= 64: W waves (8
+// down to 4) x NSTEP in {4, 8} steps of 128 covering k exactly, within
+// the LDS budget.  Taken where it measured faster than the streaming
+// split-K kernel and its reduction: at most one 16-row tile per CU (a
+// second round of workgroups re-streams the activations: 4100 x 4096 at
+// m = 32 12.6 against 10.9 us), k <= 4096 (4096 x 8192 at m = 32: 13.6
+// against 12.9 us), and m <= 48 unless k <= 2048 (4096 x 4096 at m = 64:
+// 12.1 against 11.9 us).  Measured gains: 4096 x 4096 at m = 17 / 32 / 48
+// 9.06 / 9.40 / 10.61 -> 7.76 / 8.35 / 9.79 us; 4096 x 2048 at m = 17 / 48
+// / 64 8.0 / 9.0 / 9.9 -> 5.4 / 6.4 / 7.7 us.
+bool fx_shape(int64_t m, int64_t n, int64_t k, int* waves, int* nsteps) {
+  if (m <= 16 || m > 64 || k < kStepK || k % kStepK != 0 || k > 4096) return false;
+  if (m > 48 && k > 2048) return false;
+  if ((n + 15) / 16 > kFxMaxTiles) return false;
+  const int mt = (int)((m + 15) / 16);
+  const int64_t steps = k / kStepK;
+  for (int w = 8; w >= 4; --w) {
+    if (steps % w != 0) continue;
+    const int64_t ns = steps / w;
+    if (ns != 4 && ns != 8) continue;
+    if (fx_lds_bytes(mt, w) > (size_t)159 * 1024) continue;
+    *waves = w;
+    *nsteps = (int)ns;
+    return true;
+  }
+  return false;
+}
+}  // namespace
+
+SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits);
+
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
+  int w = 0, r = 0;
+  if (forced_splits <= 0 && fx_shape(m, n, k, &w, &r)) {
+    SkinnyPlan p{};
+    p.splits = 1;
+    p.waves = w;
+    p.fx_steps = r;
+    return p;
+  }
+  if (forced_splits <= 0 && pk_shape(m, k, &w, &r)) {
+    SkinnyPlan p{};
+    p.splits = 0;
+    p.waves = w;
+    p.pk_rounds = r;
+    p.steps_per_wave = kSpw;
+    return p;
+  }
+  return plan_skinny_base(m, n, k, forced_splits);
+}
+
+SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits) {
   SkinnyPlan p{};
   const int mt = (int)((m + 15) / 16);
   const int64_t ksteps = (k + kStepK - 1) / kStepK;

@@ -182,6 +182,13 @@ __device__ __forceinline__ void load_b128_async(u32x4_t& d, const uint8_t* p) {
   asm volatile("global_load_dwordx4 %0, %1, off offset:%2" : "=v"(d) : "v"(p), "i"(OFF) : "memory");
 #endif
 }
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2_t;
+template <int OFF>
+__device__ __forceinline__ void load_b64_async(u32x2_t& d, const uint8_t* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("global_load_dwordx2 %0, %1, off offset:%2" : "=v"(d) : "v"(p), "i"(OFF) : "memory");
+#endif
+}
 template <int OFF>
 __device__ __forceinline__ void load_u16_async(uint32_t& d, const uint8_t* p) {
 #if defined(__HIP_DEVICE_COMPILE__)
@@ -212,6 +219,14 @@ template <int V>
 __device__ __forceinline__ void wait_vm4(u32x4_t& a, u32x4_t& b, uint32_t& c, uint32_t& e) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt vmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(e) : "n"(V > 63 ? 63 : V) : "memory");
+#endif
+}
+
+// Same, binding a 16-byte and an 8-byte loaded value.
+template <int V>
+__device__ __forceinline__ void wait_vm_b64(u32x4_t& a, u32x2_t& b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%2)" : "+v"(a), "+v"(b) : "n"(V > 63 ? 63 : V) : "memory");
 #endif
 }
 

@@ -204,18 +204,24 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  *            aligned (may be NULL when that size is 0).  Scratch: its
  *            contents on entry do not matter.  Calls that may run
  *            concurrently must use distinct workspaces.  The full-K
- *            kernel (m <= 16, see below) needs none (size 0); it holds fp32
+ *            kernels (see below) need none (size 0); it holds fp32
  *            partial sums [splits, m, n] whenever a path splits K.
  * Dispatch (the lower-latency kernel for the shape, [Recap] section 1, as
  * measured on MI355X; nvfp4_w4a16_gemm_path tells which):
- *   m <= 16 -> memory-bound skinny kernel, one launch, a workgroup per 16
- *     weight rows over the whole K (except 8 < m <= 16 on large matrices,
- *     n > 4096 or n * k > 2^25, with k % 512 == 0, and 4 < m <= 8 there
- *     with k > 4096: the streaming split-K kernel below; and 8 < m <= 16 with n > 4096, n * k > 2^25,
+ *   m <= 16 -> memory-bound skinny kernel, one launch, no workspace: for
+ *     4 < m <= 16 with k % 512 == 0 and k <= 4096 a persistent kernel (a
+ *     workgroup per CU walks 16-row tiles with the activations in LDS
+ *     once); otherwise a workgroup per 16 weight rows over the whole K
+ *     (except 8 < m <= 16 on large matrices, n > 4096 or n * k > 2^25,
+ *     with k % 512 == 0, and 4 < m <= 8 there with k > 4096: the streaming
+ *     split-K kernel below; and 8 < m <= 16 with n > 4096, n * k > 2^25,
  *     k % 512 != 0 and k % 64 == 0: the tiled kernel);
- *   16 < m <= 64 -> split-K skinny kernel plus a reduction kernel, when
- *     k % 512 == 0, k % 64 != 0, or n * k <= 2^25; else the tiled
- *     kernel.  Within it: for k % 512 == 0
+ *   16 < m <= 64 -> with at most 256 tiles of 16 rows, k <= 4096 (and
+ *     m <= 48 unless k <= 2048) and k a multiple of 128 that 4 to 8 waves
+ *     of 4 or 8 steps of 128 cover: one launch, a workgroup per 16
+ *     rows over the whole K, no workspace; otherwise the split-K skinny
+ *     kernel plus a reduction kernel, when k % 512 == 0, k % 64 != 0, or
+ *     n * k <= 2^25; else the tiled kernel.  Within it: for k % 512 == 0
  *     the streaming kernel (an x chunk of 1024, or 512, staged once per
  *     workgroup, then many 16-row weight tiles streamed through it);
  *     otherwise activations shared through LDS by 64 weight rows;

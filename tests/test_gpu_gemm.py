@@ -28,6 +28,16 @@ def _rel(y, ref):
     return np.linalg.norm(y - ref) / (den if den > 0 else 1.0)
 
 
+def _tol(dt, ref):
+    """The Frobenius bar; for bf16 output never below 1.05x the error of the
+    exact result rounded once to bf16 (on a small output, such as 6 x 17,
+    that rounding alone can exceed 2e-3)."""
+    if dt != torch.bfloat16:
+        return TOL[dt]
+    floor = _rel(torch.from_numpy(ref).float().bfloat16().double().numpy(), ref)
+    return max(TOL[dt], 1.05 * floor)
+
+
 def _quant(w):
     wd = torch.from_numpy(np.ascontiguousarray(w)).cuda()
     q = nv.quantize_fos(wd)
@@ -92,7 +102,9 @@ PIPE_CASES = [
     (20, 100, 2048, 1), (1, 300, 2048, 4), (7, 64, 2048, 2), (16, 333, 2048, 1), (64, 64, 512, 0),
     (33, 65, 1536, 3), (45, 190, 2048, 2), (48, 4000, 128, 0),
     # the streaming kernel (16 < m <= 64, k % 1024 == 0): ragged row groups
-    # and tiles, one K chunk, several chunks, one to four token tiles
+    # and tiles, one K chunk, several chunks, one to four token tiles (those
+    # with at most 256 row tiles and k of 2048 to 4096 take the single-launch
+    # full-K kernel instead)
     (33, 1001, 1024, 0), (48, 4000, 2048, 0), (64, 3000, 3072, 0), (40, 17, 1024, 0), (56, 5000, 4096, 0),
     (17, 1001, 1024, 0), (32, 4100, 2048, 0), (24, 300, 3072, 0),
     # 8 < m <= 16 on large matrices (more than 4096 rows): streaming kernel
@@ -121,6 +133,41 @@ def test_pipe_kernel_configs(impl):
             torch.cuda.synchronize()
             e = _rel(y, ref)
             assert e <= TOL[dt], (m, n, k, split, dt, e)
+
+
+# The two full-K kernels that need no workspace.  Persistent kernel (4 < m
+# <= 16, k % 512 == 0, k <= 4096): a workgroup per CU walks 16-row tiles,
+# 8 or 16 token rows in LDS, one to eight 512-wide K slices, fewer tiles
+# than CUs, a few tiles per CU, ragged n.  Single-launch kernel (16 < m <=
+# 64, at most 256 tiles): 2 to 4 token tiles, 4 to 8 waves of 4 or 8 K
+# steps of 128, ragged n and m.
+FULL_K_CASES = [
+    (5, 4096, 4096), (8, 14336, 4096), (9, 1001, 512), (16, 14336, 4096), (12, 20000, 2048), (7, 300, 1536),
+    (6, 17, 3584),
+    (17, 4096, 4096), (48, 4000, 4096), (64, 1001, 2048), (33, 4096, 2048), (20, 333, 3584), (40, 100, 2560),
+    (32, 4096, 3072), (49, 64, 2048),
+]
+
+
+@pytest.mark.parametrize("impl", [nv.IMPL_PORTABLE, nv.IMPL_HWCVT])
+def test_full_k_kernel_configs(impl):
+    lib = nv.lib()
+    for i, (m, n, k) in enumerate(FULL_K_CASES):
+        print("full-K case", m, n, k, "impl", impl, flush=True)
+        assert lib.nvfp4_w4a16_gemm_path(m, n, k) == nv.PATH_SKINNY
+        assert lib.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0, (m, n, k)
+        w = synth.student_t_weights(n, k, seed=1500 + i)
+        q, r = _quant(w)
+        x = synth.activations(m, k, seed=1600 + i)
+        w_hat = oracle.dequant_f64(r.codes, r.scales, r.tensor_scale)
+        ref = np.asarray(x.float().numpy(), dtype=np.float64) @ w_hat.T
+        for dt in (torch.bfloat16, torch.float32):
+            y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt, impl=impl)
+            torch.cuda.synchronize()
+            yd = y.double().cpu().numpy()
+            e = _rel(yd, ref)
+            assert e <= _tol(dt, ref), (m, n, k, dt, e)
+            assert_gemm_elementwise(yd, x, w_hat, ref, dt, f"full-K m={m} n={n} k={k} {dt}")
 
 
 @pytest.mark.parametrize("path", [nv.PATH_SKINNY, nv.PATH_TILED])

@@ -241,22 +241,34 @@ def test_dispatch_and_workspace_plan(L):
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(256, 4096, 4096, T, 3) == 3 * 4 * 256 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 5) == 2 * 4 * 100 * 256
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 1) == 0
-    for m in (1, 8, 16):  # the full-K skinny kernel needs no workspace
+    for m in (1, 8, 16):  # the full-K skinny kernels need no workspace
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
-            if (m > 8 or (m > 4 and k > 4096)) and (n > 4096 or n * k > 1 << 25):  # large: streaming split-K
+            if (m > 8 or (m > 4 and k > 4096)) and (n > 4096 or n * k > 1 << 25) and k > 4096:  # streaming split-K
                 assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == (k // 1024) * 4 * m * n
-            else:
+            else:  # full K: one workgroup per 16 rows, or the persistent kernel (4 < m, k % 512 == 0, k <= 4096)
                 assert L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0
+    # 4 < m <= 16, k % 512 == 0, k <= 4096: the persistent full-K kernel on any n
+    for m in (5, 8, 9, 16):
+        for (n, k) in ((14336, 4096), (4096, 4096), (1001, 512), (65536, 2048)):
+            assert P(m, n, k) == S and L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0
     C = 0  # the workspace holds only the fp32 partials [splits, m, n]
     for m in (17, 48):
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
             ws = L.nvfp4_w4a16_gemm_workspace_size(m, n, k)
             assert ws == 0 or ((ws - C) % (4 * m * n) == 0 and ws <= 64 * 4 * m * n + C)
-    # 16 < m <= 64, k % 1024 == 0: the streaming kernel, K chunks of 1024
-    assert L.nvfp4_w4a16_gemm_workspace_size(32, 4096, 4096) == C + 4 * 4 * 32 * 4096
+    # 16 < m <= 64 with at most 256 tiles of 16 rows, k <= 4096 a multiple of
+    # 128 that 4..8 waves of 4 or 8 steps of 128 cover (m <= 48 unless
+    # k <= 2048): the single-launch full-K kernel, no workspace
+    for (m, n, k) in ((17, 4096, 4096), (32, 4096, 4096), (48, 4096, 4096), (64, 4096, 2048), (32, 1001, 3072),
+                      (48, 4000, 2560), (20, 4096, 3584), (64, 17, 2048)):
+        assert P(m, n, k) == S and L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0, (m, n, k)
+    # more than 256 tiles, k > 4096, m > 48 with k > 2048, or k not so covered:
+    # the streaming split-K kernel, K chunks of 1024
+    assert L.nvfp4_w4a16_gemm_workspace_size(32, 4112, 4096) == C + 4 * 4 * 32 * 4112  # 257 tiles
+    assert L.nvfp4_w4a16_gemm_workspace_size(64, 4096, 4096) == C + 4 * 4 * 64 * 4096
+    assert L.nvfp4_w4a16_gemm_workspace_size(33, 1001, 3072) > 0  # 3 token tiles x 6 waves exceed LDS; 4 waves: 6 steps
     assert L.nvfp4_w4a16_gemm_workspace_size(32, 14336, 4096) == C + 4 * 4 * 32 * 14336
     assert L.nvfp4_w4a16_gemm_workspace_size(17, 4096, 14336) == C + 14 * 4 * 17 * 4096
-    assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 4096) == C + 4 * 4 * 48 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(48, 14336, 4096) == C + 4 * 4 * 48 * 14336
     assert L.nvfp4_w4a16_gemm_workspace_size(48, 4096, 14336) == C + 14 * 4 * 48 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(33, 65, 1536) == C + 3 * 4 * 33 * 65  # k % 1024 != 0: chunks of 512

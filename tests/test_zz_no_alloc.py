@@ -29,8 +29,9 @@ def _noalloc(x, q, out):
 
 def test_noalloc_matches_workspace_entry_point():
     # (m, n, k, seed): both split K (the streaming kernel, then the reduction
-    # reading the scratch); the second is smaller than the first
-    cases = [(48, 4096, 4096, 2), (17, 1000, 2048, 3)]
+    # reading the scratch): more than 256 row tiles, then k > 4096, where the
+    # single-launch full-K kernel does not apply; the second is smaller
+    cases = [(48, 14336, 4096, 2), (17, 1000, 4608, 3)]
     scratch = nv.lib().nvfp4_noalloc_scratch_bytes()
     for m, n, k, seed in cases:
         need = nv.workspace_size(m, n, k)
