@@ -395,8 +395,9 @@ __global__ __launch_bounds__(512) void k_skinny_dot(const uint16_t* __restrict__
 // into its own LDS region with the LDS DMA (one instruction per token row
 // and slice: 512 contiguous bf16, whole cache lines; token rows >= m repeat
 // row m - 1, whose outputs are not stored), so the activations cross L2 ->
-// CU once per workgroup instead of once per tile, and no load of x stands
-// in front of the weight loads.  Per tile a lane loads, per slice, the 8
+// CU once per workgroup instead of once per tile.  (Requesting the first
+// tile's weights before the copies measured slower: 4096 x 4096 at m = 8,
+// 6.3 against 5.9 us.)  Per tile a lane loads, per slice, the 8
 // scale bytes and four 16-byte code pieces of its quarter (the full-K
 // kernel's layout); the next two tiles' loads are in flight while a tile is
 // consumed, and step s waits only until its own loads have landed
@@ -496,12 +497,15 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
   const float s_t = tensor_scale[0];
 
   // activations of this wave's slices, once (LDS DMA: lane l -> bf16 8l .. 8l + 7)
+  auto copy_x = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int r = 0; r < ROUNDS; ++r)
+    for (int r = 0; r < ROUNDS; ++r)
 #pragma unroll
-    for (int m = 0; m < MR; ++m)
-      copy16_to_lds(x + (int64_t)min(m, M - 1) * K + (r * W + wave) * kWaveK + 8 * lane,
-                    reinterpret_cast<uint8_t*>(xw + (r * MR + m) * kPkRow));
+      for (int m = 0; m < MR; ++m)
+        copy16_to_lds(x + (int64_t)min(m, M - 1) * K + (r * W + wave) * kWaveK + 8 * lane,
+                      reinterpret_cast<uint8_t*>(xw + (r * MR + m) * kPkRow));
+    asm volatile("" ::: "memory");
+  };
 
   const int ntiles = (N + 15) / 16;
   const int cnt = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // tiles of this workgroup
@@ -590,6 +594,7 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
   // three register sets: while tile i is consumed the loads of tiles i + 1
   // and i + 2 are in flight
   PkTile<ROUNDS> A, B, C;
+  copy_x();
   issue(A, 0);
   issue(B, 1);
   for (int i = 0; i < cnt; i += 3) {
@@ -610,41 +615,55 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
 // weight rows over the whole K, so no fp32 partial planes and no second
 // launch; its W waves split K into slices of NSTEP steps of 128.  The
 // activations (up to 64 x k) do not fit in LDS, so each wave streams its
-// slice: per step a lane loads its row's 32 codes at k = 128 s + 32 g (the
-// four lanes of a row read 64 contiguous bytes) and their two scale bytes,
-// and the wave copies the step's activations (16 MT token rows x 256 bytes,
+// slice: per step a lane's row has 32 codes at k = 128 s + 32 g (the four
+// lanes of a row read 64 contiguous bytes) and their two scale bytes, and
+// the wave copies the step's activations (16 MT token rows x 256 bytes,
 // whole cache lines; piece q of row r at slot q ^ (r % 16), so the B
 // fragment reads of 16 rows hit 16 bank groups) into one of its two private
-// LDS buffers with the LDS DMA.  Step s + 1's loads are in flight while
-// step s is dequantized and multiplied; step s waits (counted, inline-asm
-// loads) only for its own loads, and a buffer is refilled only after the
-// step that read it.  No barrier until the W partial tiles are added in wave
-// order through LDS.  Token rows >= m repeat row m - 1 (outputs not stored).
+// LDS buffers with the LDS DMA.
+// Issue order: the activations of steps 0 and 1, then the codes and scales
+// of every step (a wave's whole weight slice is in flight at once, so the
+// weights cross HBM while the activations stream from L2), then step s + 2's
+// activations once step s has read its buffer.  Loads complete in issue
+// order, so step s waits (counted, inline-asm loads) for what it needs and
+// no more: for s < 2 its weights, after that its activations (measured on
+// 4096 x 4096, m = 32 / 48: 8.3 / 9.8 -> 7.8 / 9.0 us against the order
+// step by step).  Token rows >= m repeat row m - 1 (outputs not stored).
+// No barrier until the W partial tiles are added in wave order through LDS.
 template <int MT>
-__device__ __forceinline__ void fx_issue(u32x4_t& cw, uint32_t& sb, const uint8_t* cp, const uint8_t* sp,
-                                         const uint16_t* const* xsrc, uint8_t* buf, int s) {
-  load_b128_async<0>(cw, cp + 64 * s);
-  load_u16_async<0>(sb, sp + 8 * s);
+__device__ __forceinline__ void fx_issue_x(const uint16_t* const* xsrc, uint8_t* buf, int s) {
 #pragma unroll
   for (int c = 0; c < 4 * MT; ++c) copy16_to_lds(xsrc[c] + kStepK * s, buf + 1024 * c);
   asm volatile("" ::: "memory");
 }
 
-constexpr int fx_loads_per_step(int mt) { return 2 + 4 * mt; }
+// Loads still allowed in flight when step S starts (see the issue order).
+template <int S, int NSTEP, int MT>
+constexpr int fx_wait_count() {
+  constexpr int kx = 4 * MT;  // copies per step
+  if constexpr (S < 2) {
+    // after step S's weights: the later steps' weights, and the activation
+    // copies issued after steps 0 .. S - 1 (step j issues step j + 2)
+    constexpr int later_x = (S < NSTEP - 2 ? S : (NSTEP - 2 > 0 ? NSTEP - 2 : 0));
+    return 2 * (NSTEP - 1 - S) + kx * later_x;
+  } else {
+    // after step S's activations: step S + 1's, if issued
+    return S + 1 < NSTEP ? kx : 0;
+  }
+}
 
-// Step S of NSTEP (register set S % 2, LDS buffer S % 2), then the rest.
+// Step S of NSTEP (LDS buffer S % 2), then the rest.
 template <int S, int NSTEP, int MT, int IMPL>
-__device__ __forceinline__ void fx_steps(u32x4_t (&cw)[2], uint32_t (&sb)[2], const uint8_t* cp, const uint8_t* sp,
-                                         const uint16_t* const* xsrc, uint8_t* xbuf, int g, int c16,
-                                         f32x4_t (&acc)[MT]) {
+__device__ __forceinline__ void fx_steps(u32x4_t (&cw)[NSTEP], uint32_t (&sb)[NSTEP], const uint16_t* const* xsrc,
+                                         uint8_t* xbuf, int g, int c16, f32x4_t (&acc)[MT]) {
   constexpr int cur = S & 1;
-  wait_vm<(S + 1 < NSTEP) ? fx_loads_per_step(MT) : 0>(cw[cur], sb[cur]);
-  const float sg0 = scale_at<IMPL, 0>(sb[cur]), sg1 = scale_at<IMPL, 1>(sb[cur]);
+  wait_vm<fx_wait_count<S, NSTEP, MT>()>(cw[S], sb[S]);
+  const float sg0 = scale_at<IMPL, 0>(sb[S]), sg1 = scale_at<IMPL, 1>(sb[S]);
   bf16x8_t a[4];
-  a[0] = dequant8<IMPL>(cw[cur][0], sg0);
-  a[1] = dequant8<IMPL>(cw[cur][1], sg0);
-  a[2] = dequant8<IMPL>(cw[cur][2], sg1);
-  a[3] = dequant8<IMPL>(cw[cur][3], sg1);
+  a[0] = dequant8<IMPL>(cw[S][0], sg0);
+  a[1] = dequant8<IMPL>(cw[S][1], sg0);
+  a[2] = dequant8<IMPL>(cw[S][2], sg1);
+  a[3] = dequant8<IMPL>(cw[S][3], sg1);
   const uint8_t* buf = xbuf + cur * (4096 * MT);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
@@ -655,9 +674,9 @@ __device__ __forceinline__ void fx_steps(u32x4_t (&cw)[2], uint32_t (&sb)[2], co
     }
   if constexpr (S + 2 < NSTEP) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this buffer's reads are done before it is refilled
-    fx_issue<MT>(cw[cur], sb[cur], cp, sp, xsrc, xbuf + cur * (4096 * MT), S + 2);
+    fx_issue_x<MT>(xsrc, xbuf + cur * (4096 * MT), S + 2);
   }
-  if constexpr (S + 1 < NSTEP) fx_steps<S + 1, NSTEP, MT, IMPL>(cw, sb, cp, sp, xsrc, xbuf, g, c16, acc);
+  if constexpr (S + 1 < NSTEP) fx_steps<S + 1, NSTEP, MT, IMPL>(cw, sb, xsrc, xbuf, g, c16, acc);
 }
 
 template <int MT, int IMPL, int NSTEP>
@@ -687,14 +706,21 @@ __global__ __launch_bounds__(512) void k_skinny_fx(const uint16_t* __restrict__ 
     const int rr = 4 * c + (lane >> 4);
     xsrc[c] = x + (int64_t)min(rr, M - 1) * K + k0 + 8 * ((lane & 15) ^ (rr & 15));
   }
-  u32x4_t cw[2];
-  uint32_t sb[2];
-  fx_issue<MT>(cw[0], sb[0], cp, sp, xsrc, xbuf, 0);
-  if constexpr (NSTEP > 1) fx_issue<MT>(cw[1], sb[1], cp, sp, xsrc, xbuf + 4096 * MT, 1);
+  static_assert(NSTEP >= 2, "two activation buffers per wave");
+  fx_issue_x<MT>(xsrc, xbuf, 0);
+  fx_issue_x<MT>(xsrc, xbuf + 4096 * MT, 1);
+  u32x4_t cw[NSTEP];
+  uint32_t sb[NSTEP];
+#pragma unroll
+  for (int t = 0; t < NSTEP; ++t) {
+    load_b128_async<0>(cw[t], cp + 64 * t);
+    load_u16_async<0>(sb[t], sp + 8 * t);
+  }
+  asm volatile("" ::: "memory");
   f32x4_t acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  fx_steps<0, NSTEP, MT, IMPL>(cw, sb, cp, sp, xsrc, xbuf, g, c16, acc);
+  fx_steps<0, NSTEP, MT, IMPL>(cw, sb, xsrc, xbuf, g, c16, acc);
 
   // the W partial tiles, added in wave order; lane holds D[n = 4 g + e][m = 16 mt + c16]
 #pragma unroll
