@@ -10,10 +10,10 @@
 //    of the full-K layout below; a workgroup per CU walks its 16-row tiles
 //    with the activations in LDS once and the next two tiles' weights in
 //    flight.  No workspace, one launch.
-//  * k_skinny_fx (16 < m <= 64 with at most one 16-row tile per CU, k <=
-//    4096): a workgroup per tile over the whole K, each wave streaming its
-//    K slice and the activations of each step through a private LDS double
-//    buffer.  No workspace, one launch.
+//  * k_skinny_fx (16 < m <= 64, k <= 4096, at most 256 workgroups of one
+//    to four 16-row tiles): a workgroup per group of tiles over the whole
+//    K, each wave streaming its K slice and the activations of each step
+//    through a private LDS double buffer.  No workspace, one launch.
 //  * k_skinny_fk (2 < m <= 16, except 8 < m <= 16 on large matrices: more
 //    than 4096 rows or 2^25 weights, K % 512 == 0, and 4 < m <= 8 there
 //    with K > 4096, which take the streaming kernel below): a workgroup owns 16 weight rows over the whole K and its
@@ -49,7 +49,7 @@ constexpr int kRowsPerWg = 16 * kWaves;
 constexpr int kStepK = 128;     // K per step (4 MFMAs of K=32)
 constexpr int kMaxSteps = 16;   // K steps per chunk held in registers
 constexpr int kLdsBudget = 131072;
-constexpr int kFxMaxTiles = 256;  // the single-launch 16 < m <= 64 kernel: at most one 16-row tile per CU
+constexpr int kFxMaxTiles = 256;  // the single-launch 16 < m <= 64 kernel: at most one workgroup per CU
 
 template <int IMPL>
 __device__ __forceinline__ bf16x8_t dequant8(uint32_t d, float sigma) {
@@ -610,10 +610,11 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
   wait_vm_all();  // the last (unused) loads land before the wave ends
 }
 
-// Single-launch full-K kernel for 16 < m <= 64 on matrices with about one
-// 16-row tile per CU (k = W * NSTEP * 128): a workgroup owns one tile of 16
-// weight rows over the whole K, so no fp32 partial planes and no second
-// launch; its W waves split K into slices of NSTEP steps of 128.  The
+// Single-launch full-K kernel for 16 < m <= 64 on matrices of up to 1024
+// 16-row tiles (k = W * NSTEP * 128): a workgroup owns T (1 .. 4) tiles of
+// 16 weight rows over the whole K, so no fp32 partial planes and no second
+// launch; its W waves split K into slices of NSTEP steps of 128, and each
+// activation fragment a wave reads feeds all T tiles.  The
 // activations (up to 64 x k) do not fit in LDS, so each wave streams its
 // slice: per step a lane's row has 32 codes at k = 128 s + 32 g (the four
 // lanes of a row read 64 contiguous bytes) and their two scale bytes, and
@@ -637,67 +638,102 @@ __device__ __forceinline__ void fx_issue_x(const uint16_t* const* xsrc, uint8_t*
   asm volatile("" ::: "memory");
 }
 
-// Loads still allowed in flight when step S starts (see the issue order).
-template <int S, int NSTEP, int MT>
-constexpr int fx_wait_count() {
-  constexpr int kx = 4 * MT;  // copies per step
-  if constexpr (S < 2) {
-    // after step S's weights: the later steps' weights, and the activation
-    // copies issued after steps 0 .. S - 1 (step j issues step j + 2)
-    constexpr int later_x = (S < NSTEP - 2 ? S : (NSTEP - 2 > 0 ? NSTEP - 2 : 0));
-    return 2 * (NSTEP - 1 - S) + kx * later_x;
-  } else {
-    // after step S's activations: step S + 1's, if issued
-    return S + 1 < NSTEP ? kx : 0;
+// Loads still allowed in flight when step S starts.  Issue order: the
+// activation copies of steps 0 and 1 (kx loads each), the weights of steps
+// 0 .. P - 1 (kw loads each: codes and scales of T tiles); after step j,
+// the copies of step j + 2 and the weights of step j + P.  Step S needs its
+// copies and its weights; loads complete in issue order.
+template <int NSTEP, int MT, int T, int P>
+constexpr int fx_wait_count(int S) {
+  const int kx = 4 * MT, kw = 2 * T;
+  int end_x[64] = {}, end_w[64] = {};
+  int pos = 0;
+  for (int t = 0; t < 2 && t < NSTEP; ++t) end_x[t] = (pos += kx);
+  for (int t = 0; t < P && t < NSTEP; ++t) end_w[t] = (pos += kw);
+  for (int j = 0; j < S; ++j) {
+    if (j + 2 < NSTEP) end_x[j + 2] = (pos += kx);
+    if (j + P < NSTEP) end_w[j + P] = (pos += kw);
   }
+  return pos - (end_x[S] > end_w[S] ? end_x[S] : end_w[S]);
 }
 
-// Step S of NSTEP (LDS buffer S % 2), then the rest.
-template <int S, int NSTEP, int MT, int IMPL>
-__device__ __forceinline__ void fx_steps(u32x4_t (&cw)[NSTEP], uint32_t (&sb)[NSTEP], const uint16_t* const* xsrc,
-                                         uint8_t* xbuf, int g, int c16, f32x4_t (&acc)[MT]) {
-  constexpr int cur = S & 1;
-  wait_vm<fx_wait_count<S, NSTEP, MT>()>(cw[S], sb[S]);
-  const float sg0 = scale_at<IMPL, 0>(sb[S]), sg1 = scale_at<IMPL, 1>(sb[S]);
-  bf16x8_t a[4];
-  a[0] = dequant8<IMPL>(cw[S][0], sg0);
-  a[1] = dequant8<IMPL>(cw[S][1], sg0);
-  a[2] = dequant8<IMPL>(cw[S][2], sg1);
-  a[3] = dequant8<IMPL>(cw[S][3], sg1);
+template <int T>
+__device__ __forceinline__ void fx_issue_w(u32x4_t (&cw)[T], uint32_t (&sb)[T], const uint8_t* const* cp,
+                                           const uint8_t* const* sp, int s) {
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    load_b128_async<0>(cw[t], cp[t] + 64 * s);
+    load_u16_async<0>(sb[t], sp[t] + 8 * s);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// Step S of NSTEP (LDS buffer S % 2, weight registers S % P), then the
+// rest: each B fragment read from LDS feeds the MFMAs of all T row tiles.
+template <int S, int NSTEP, int MT, int IMPL, int T, int P>
+__device__ __forceinline__ void fx_steps(u32x4_t (&cw)[P][T], uint32_t (&sb)[P][T], const uint8_t* const* cp,
+                                         const uint8_t* const* sp, const uint16_t* const* xsrc, uint8_t* xbuf, int g,
+                                         int c16, f32x4_t (&acc)[T][MT]) {
+  constexpr int cur = S & 1, slot = S % P;
+  wait_vm<fx_wait_count<NSTEP, MT, T, P>(S)>(cw[slot][0], sb[slot][0]);
+#pragma unroll
+  for (int t = 1; t < T; ++t) bind_loaded(cw[slot][t], sb[slot][t]);  // landed with the wait above
+  bf16x8_t a[T][4];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const float sg0 = scale_at<IMPL, 0>(sb[slot][t]), sg1 = scale_at<IMPL, 1>(sb[slot][t]);
+    a[t][0] = dequant8<IMPL>(cw[slot][t][0], sg0);
+    a[t][1] = dequant8<IMPL>(cw[slot][t][1], sg0);
+    a[t][2] = dequant8<IMPL>(cw[slot][t][2], sg1);
+    a[t][3] = dequant8<IMPL>(cw[slot][t][3], sg1);
+  }
   const uint8_t* buf = xbuf + cur * (4096 * MT);
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const u32x4_t b = *reinterpret_cast<const u32x4_t*>(buf + 256 * (16 * mt + c16) + 16 * ((4 * g + j) ^ c16));
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], __builtin_bit_cast(bf16x8_t, b), acc[mt], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[t][j], __builtin_bit_cast(bf16x8_t, b), acc[t][mt], 0, 0, 0);
     }
   if constexpr (S + 2 < NSTEP) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // this buffer's reads are done before it is refilled
     fx_issue_x<MT>(xsrc, xbuf + cur * (4096 * MT), S + 2);
   }
-  if constexpr (S + 1 < NSTEP) fx_steps<S + 1, NSTEP, MT, IMPL>(cw, sb, xsrc, xbuf, g, c16, acc);
+  if constexpr (S + P < NSTEP) fx_issue_w<T>(cw[slot], sb[slot], cp, sp, S + P);
+  if constexpr (S + 1 < NSTEP) fx_steps<S + 1, NSTEP, MT, IMPL, T, P>(cw, sb, cp, sp, xsrc, xbuf, g, c16, acc);
 }
 
-template <int MT, int IMPL, int NSTEP>
-__global__ __launch_bounds__(512) void k_skinny_fx(const uint16_t* __restrict__ x,
-                                                   const uint8_t* __restrict__ codes,
-                                                   const uint8_t* __restrict__ scales,
-                                                   const float* __restrict__ tensor_scale,
-                                                   void* __restrict__ y, int M, int N, int K, int out_f32) {
+// Weight steps in flight: all of a wave's slice for one tile per
+// workgroup; fewer with more tiles, so the loaded words stay in registers.
+constexpr int fx_weight_ahead(int nstep, int t) { return t == 1 ? nstep : (16 / t < nstep ? 16 / t : nstep); }
+
+template <int MT, int IMPL, int NSTEP, int T>
+__global__ __launch_bounds__(T == 1 ? 512 : 256) void k_skinny_fx(const uint16_t* __restrict__ x,
+                                                                  const uint8_t* __restrict__ codes,
+                                                                  const uint8_t* __restrict__ scales,
+                                                                  const float* __restrict__ tensor_scale,
+                                                                  void* __restrict__ y, int M, int N, int K,
+                                                                  int out_f32) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   uint8_t* xbuf = lds + (size_t)wave * 2 * 4096 * MT;            // [2][16 MT rows][256 bytes]
-  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + (size_t)W * 2 * 4096 * MT);  // [W][MT][64]
+  f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + (size_t)W * 2 * 4096 * MT);  // [W][T][MT][64]
   const float s_t = tensor_scale[0];
-  const int n0 = blockIdx.x * 16;
+  const int n0 = blockIdx.x * 16 * T;
   const int k0 = wave * NSTEP * kStepK;
-  const int row = min(n0 + c16, N - 1);  // rows past n read row n - 1 (real data); outputs dropped
-  const uint8_t* cp = codes + (int64_t)row * (K / 2) + k0 / 2 + 16 * g;
-  const uint8_t* sp = scales + (int64_t)row * (K / 16) + k0 / 16 + 2 * g;
+  const uint8_t* cp[T];
+  const uint8_t* sp[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    const int row = min(n0 + 16 * t + c16, N - 1);  // rows past n read row n - 1 (real data); outputs dropped
+    cp[t] = codes + (int64_t)row * (K / 2) + k0 / 2 + 16 * g;
+    sp[t] = scales + (int64_t)row * (K / 16) + k0 / 16 + 2 * g;
+  }
   // DMA instruction c of a step: token rows 4c .. 4c + 3, lane l -> row
   // 4c + l / 16, piece (l % 16) ^ (row % 16)
   const uint16_t* xsrc[4 * MT];
@@ -707,38 +743,39 @@ __global__ __launch_bounds__(512) void k_skinny_fx(const uint16_t* __restrict__ 
     xsrc[c] = x + (int64_t)min(rr, M - 1) * K + k0 + 8 * ((lane & 15) ^ (rr & 15));
   }
   static_assert(NSTEP >= 2, "two activation buffers per wave");
+  constexpr int P = fx_weight_ahead(NSTEP, T);
   fx_issue_x<MT>(xsrc, xbuf, 0);
   fx_issue_x<MT>(xsrc, xbuf + 4096 * MT, 1);
-  u32x4_t cw[NSTEP];
-  uint32_t sb[NSTEP];
+  u32x4_t cw[P][T];
+  uint32_t sb[P][T];
 #pragma unroll
-  for (int t = 0; t < NSTEP; ++t) {
-    load_b128_async<0>(cw[t], cp + 64 * t);
-    load_u16_async<0>(sb[t], sp + 8 * t);
-  }
-  asm volatile("" ::: "memory");
-  f32x4_t acc[MT];
+  for (int s = 0; s < P; ++s) fx_issue_w<T>(cw[s], sb[s], cp, sp, s);
+  f32x4_t acc[T][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  fx_steps<0, NSTEP, MT, IMPL>(cw, sb, xsrc, xbuf, g, c16, acc);
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  fx_steps<0, NSTEP, MT, IMPL, T, P>(cw, sb, cp, sp, xsrc, xbuf, g, c16, acc);
 
   // the W partial tiles, added in wave order; lane holds D[n = 4 g + e][m = 16 mt + c16]
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) red[(wave * MT + mt) * 64 + lane] = acc[mt];
+  for (int t = 0; t < T; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[((wave * T + t) * MT + mt) * 64 + lane] = acc[t][mt];
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  for (int i = threadIdx.x; i < MT * 64; i += blockDim.x) {
+  for (int i = threadIdx.x; i < T * MT * 64; i += blockDim.x) {
     f32x4_t v = red[i];
     for (int w = 1; w < W; ++w) {
-      const f32x4_t u = red[w * MT * 64 + i];
+      const f32x4_t u = red[w * T * MT * 64 + i];
       v[0] += u[0];
       v[1] += u[1];
       v[2] += u[2];
       v[3] += u[3];
     }
-    const int mt = i >> 6, l = i & 63;
-    const int m = 16 * mt + (l & 15), nb = n0 + 4 * (l >> 4);
+    const int t = i / (MT * 64), mt = (i >> 6) % MT, l = i & 63;
+    const int m = 16 * mt + (l & 15), nb = n0 + 16 * t + 4 * (l >> 4);
     if (m >= M) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -1323,25 +1360,37 @@ hipError_t launch_pk_r(const SkinnyPlan& p, hipStream_t stream, const uint16_t* 
   return launch_pk<MR, IMPL, 1>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
 }
 
-size_t fx_lds_bytes(int mt, int w) { return (size_t)w * mt * (2 * 4096 + 1024); }
+size_t fx_lds_bytes(int mt, int w, int t) { return (size_t)w * mt * (2 * 4096 + 1024 * t); }
 
-template <int MT, int IMPL, int NSTEP>
+template <int MT, int IMPL, int NSTEP, int T>
 hipError_t launch_fx(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
                      const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
-  const size_t lds = fx_lds_bytes(MT, p.waves);
-  hipError_t e = set_lds_limit<k_skinny_fx<MT, IMPL, NSTEP>>(lds);
+  const size_t lds = fx_lds_bytes(MT, p.waves, T);
+  hipError_t e = set_lds_limit<k_skinny_fx<MT, IMPL, NSTEP, T>>(lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_skinny_fx<MT, IMPL, NSTEP>), dim3((unsigned)((N + 15) / 16)), dim3(64 * p.waves), lds, stream,
-                     x, codes, scales, ts, y, M, N, K, out_f32);
+  hipLaunchKernelGGL((k_skinny_fx<MT, IMPL, NSTEP, T>), dim3((unsigned)((N + 16 * T - 1) / (16 * T))),
+                     dim3(64 * p.waves), lds, stream, x, codes, scales, ts, y, M, N, K, out_f32);
   return hipGetLastError();
+}
+
+template <int MT, int IMPL, int T>
+hipError_t launch_fx_s(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
+                       const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+  switch (p.fx_steps) {
+    case 4: return launch_fx<MT, IMPL, 4, T>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+    case 8: return launch_fx<MT, IMPL, 8, T>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <int MT, int IMPL>
 hipError_t launch_fx_n(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
                        const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
-  switch (p.fx_steps) {
-    case 4: return launch_fx<MT, IMPL, 4>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
-    case 8: return launch_fx<MT, IMPL, 8>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+  switch (p.fx_tiles) {
+    case 1: return launch_fx_s<MT, IMPL, 1>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+    case 2: return launch_fx_s<MT, IMPL, 2>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+    case 3: return launch_fx_s<MT, IMPL, 3>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
+    case 4: return launch_fx_s<MT, IMPL, 4>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1537,19 +1586,40 @@ namespace {
 // 12.1 against 11.9 us).  Measured gains: 4096 x 4096 at m = 17 / 32 / 48
 // 9.06 / 9.40 / 10.61 -> 7.76 / 8.35 / 9.79 us; 4096 x 2048 at m = 17 / 48
 // / 64 8.0 / 9.0 / 9.9 -> 5.4 / 6.4 / 7.7 us.
-bool fx_shape(int64_t m, int64_t n, int64_t k, int* waves, int* nsteps) {
+bool fx_shape(int64_t m, int64_t n, int64_t k, int* waves, int* nsteps, int* tiles) {
   if (m <= 16 || m > 64 || k < kStepK || k % kStepK != 0 || k > 4096) return false;
   if (m > 48 && k > 2048) return false;
-  if ((n + 15) / 16 > kFxMaxTiles) return false;
   const int mt = (int)((m + 15) / 16);
   const int64_t steps = k / kStepK;
+  const int64_t ntiles = (n + 15) / 16;
+  if (ntiles > kFxMaxTiles) {
+    // T = 2 .. 4 row tiles per workgroup, so that at most 256 workgroups
+    // share the activation stream (4 waves of 512-wide K slices).  Measured
+    // against the streaming split-K kernel at m = 17 / 32 / 48: 8192 x 4096
+    // 12.2 / 13.2 / 15.6 -> 10.6 / 10.9 / 12.6 us (T = 2); 12288 x 4096
+    // 14.8 / 15.2 / 18.0 -> 13.9 / 14.7 / 16.8 us (T = 3); 14336 x 2048
+    // 11.8 / 12.7 / 14.9 -> 9.9 / 10.3 / 12.2 us (T = 4); with T = 4 and
+    // k = 4096 (14336 x 4096) even or slower (16.5 / 17.6 / 20.0 against
+    // 17.0 / 17.0 / 20.1 us), so not taken there.
+    const int64_t t = (ntiles + kFxMaxTiles - 1) / kFxMaxTiles;
+    if (t > 4 || (t == 4 && k > 2048)) return false;
+    if ((ntiles + t - 1) / t < 192) return false;  // keep at least 3/4 of the CUs busy
+    const int64_t ns = steps / 4;
+    if (steps % 4 != 0 || (ns != 4 && ns != 8)) return false;
+    if (fx_lds_bytes(mt, 4, (int)t) > (size_t)159 * 1024) return false;
+    *waves = 4;
+    *nsteps = (int)ns;
+    *tiles = (int)t;
+    return true;
+  }
   for (int w = 8; w >= 4; --w) {
     if (steps % w != 0) continue;
     const int64_t ns = steps / w;
     if (ns != 4 && ns != 8) continue;
-    if (fx_lds_bytes(mt, w) > (size_t)159 * 1024) continue;
+    if (fx_lds_bytes(mt, w, 1) > (size_t)159 * 1024) continue;
     *waves = w;
     *nsteps = (int)ns;
+    *tiles = 1;
     return true;
   }
   return false;
@@ -1559,12 +1629,13 @@ bool fx_shape(int64_t m, int64_t n, int64_t k, int* waves, int* nsteps) {
 SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits);
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
-  int w = 0, r = 0;
-  if (forced_splits <= 0 && fx_shape(m, n, k, &w, &r)) {
+  int w = 0, r = 0, t = 0;
+  if (forced_splits <= 0 && fx_shape(m, n, k, &w, &r, &t)) {
     SkinnyPlan p{};
     p.splits = 1;
     p.waves = w;
     p.fx_steps = r;
+    p.fx_tiles = t;
     return p;
   }
   if (forced_splits <= 0 && pk_shape(m, k, &w, &r)) {

@@ -35,6 +35,7 @@ struct SkinnyPlan {
   int str_rows;   // > 0: streaming kernel with row groups of str_rows rows
   int pk_rounds;  // > 0 (with splits == 0): persistent full-K kernel, `waves` waves x pk_rounds K slices of 512
   int fx_steps;   // > 0: single-launch full-K kernel, `waves` waves x fx_steps K steps of 128 (16 < m <= 64)
+  int fx_tiles;   // with fx_steps: 16-row weight tiles per workgroup (1 .. 4)
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits);
 hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* scales,

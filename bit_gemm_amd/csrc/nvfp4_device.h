@@ -230,6 +230,14 @@ __device__ __forceinline__ void wait_vm_b64(u32x4_t& a, u32x2_t& b) {
 #endif
 }
 
+// After a counted wait that also covers them: marks a 16-byte and a 4-byte
+// loaded value as written here, so no use moves above it.
+__device__ __forceinline__ void bind_loaded(u32x4_t& c, uint32_t& s) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(c), "+v"(s));
+#endif
+}
+
 // Wait until every vector-memory operation of this wave has completed.
 __device__ __forceinline__ void wait_vm_all() {
 #if defined(__HIP_DEVICE_COMPILE__)

@@ -34,7 +34,7 @@ def test_checker_flags_early_reads():
     ("gemm_skinny.hip", r"k_skinny_pipe", 20),  # MT 1..4 x chunk lengths x 2 conversion implementations
     ("gemm_skinny.hip", r"k_skinny_str", 16),    # streaming kernel: MT 1..4 x chunk lengths x 2 conversion implementations
     ("gemm_skinny.hip", r"k_skinny_pk", 4),      # persistent full-K kernel: 8 or 16 token rows x 2 implementations
-    ("gemm_skinny.hip", r"k_skinny_fx", 12),     # single-launch full-K kernel: MT 2..4 x 4 or 8 steps x 2 implementations
+    ("gemm_skinny.hip", r"k_skinny_fx", 48),     # single-launch full-K kernel: MT 2..4 x 4 or 8 steps x 1..4 tiles x 2 implementations
     ("gemm_tiled.hip", r"k_lmr", 2),             # weights-in-registers large-M kernel, 2 implementations
 ])
 def test_counted_waits_cover_every_use(tmp_path, source, pattern, minimum):

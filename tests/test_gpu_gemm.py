@@ -139,13 +139,15 @@ def test_pipe_kernel_configs(impl):
 # <= 16, k % 512 == 0, k <= 4096): a workgroup per CU walks 16-row tiles,
 # 8 or 16 token rows in LDS, one to eight 512-wide K slices, fewer tiles
 # than CUs, a few tiles per CU, ragged n.  Single-launch kernel (16 < m <=
-# 64, at most 256 tiles): 2 to 4 token tiles, 4 to 8 waves of 4 or 8 K
-# steps of 128, ragged n and m.
+# 64, at most 256 workgroups of 1 to 4 row tiles): 2 to 4 token tiles, 4
+# to 8 waves of 4 or 8 K steps of 128, ragged n and m.
 FULL_K_CASES = [
     (5, 4096, 4096), (8, 14336, 4096), (9, 1001, 512), (16, 14336, 4096), (12, 20000, 2048), (7, 300, 1536),
     (6, 17, 3584),
     (17, 4096, 4096), (48, 4000, 4096), (64, 1001, 2048), (33, 4096, 2048), (20, 333, 3584), (40, 100, 2560),
     (32, 4096, 3072), (49, 64, 2048),
+    # two to four row tiles per workgroup (more than 256 tiles), ragged n
+    (17, 8192, 4096), (48, 12000, 4096), (33, 14336, 2048), (25, 7777, 2048),
 ]
 
 

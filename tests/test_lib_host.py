@@ -262,8 +262,13 @@ def test_dispatch_and_workspace_plan(L):
     for (m, n, k) in ((17, 4096, 4096), (32, 4096, 4096), (48, 4096, 4096), (64, 4096, 2048), (32, 1001, 3072),
                       (48, 4000, 2560), (20, 4096, 3584), (64, 17, 2048)):
         assert P(m, n, k) == S and L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0, (m, n, k)
-    # more than 256 tiles, k > 4096, m > 48 with k > 2048, or k not so covered:
-    # the streaming split-K kernel, K chunks of 1024
+    # more than 256 tiles: 2 to 4 tiles per workgroup when that keeps 192 to
+    # 256 workgroups (4 tiles only for k <= 2048)
+    for (m, n, k) in ((17, 8192, 4096), (48, 12288, 4096), (48, 14336, 2048), (25, 7777, 2048)):
+        assert P(m, n, k) == S and L.nvfp4_w4a16_gemm_workspace_size(m, n, k) == 0, (m, n, k)
+    # more than 256 tiles otherwise, k > 4096, m > 48 with k > 2048, or k not
+    # so covered: the streaming split-K kernel, K chunks of 1024
+    assert L.nvfp4_w4a16_gemm_workspace_size(17, 4097, 4096) == C + 4 * 4 * 17 * 4097  # 129 workgroups of 2 tiles: too few
     assert L.nvfp4_w4a16_gemm_workspace_size(32, 4112, 4096) == C + 4 * 4 * 32 * 4112  # 257 tiles
     assert L.nvfp4_w4a16_gemm_workspace_size(64, 4096, 4096) == C + 4 * 4 * 64 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(33, 1001, 3072) > 0  # 3 token tiles x 6 waves exceed LDS; 4 waves: 6 steps
