@@ -456,9 +456,9 @@ def read_ceilings(stream, time_op):
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X published dense bf16 matrix rate
 # decoder layer shapes (n, k)
-MLP_SHAPES = [("up_gate", 14336, 4096), ("down", 4096, 14336)]
+MLP_SHAPES = [("up_gate", 14336, 4096, 30), ("down", 4096, 14336, 32)]  # (name, n, k, weight seed)
 MLP_M = [1, 4, 16, 48]
-LARGE_SHAPES = [("attn", 4096, 4096), ("up_gate", 14336, 4096)]
+LARGE_SHAPES = [("attn", 4096, 4096, 40), ("up_gate", 14336, 4096, 41)]
 LARGE_M = [64, 256, 1024, 4096]
 
 
@@ -468,29 +468,29 @@ def decoder_shapes(args, stream, time_op, w_dev, ceilings):
     GB/s against HBM) and the large-M prefill shapes (TFLOP/s against the
     bf16 MFMA peak).  Each launch reads its own packed copy (>= 1 GiB of
     copies per shape for the decode counts) so weights come from HBM.  The
-    weights are the single layer's Student-t matrix tiled to each shape
-    (latency does not depend on the values; drawing 58.7 M Student-t values
-    on the host would take longer than the whole run)."""
+    weights are drawn on the GPU from the configs' distribution with their
+    seeds (synth.student_t_weights_device: not the host draw's values, which
+    would take ~15 s per MLP matrix to make)."""
     import torch
 
     import bit_gemm_amd as nv
     import synth
 
     dev = torch.device("cuda:0")
-    out = {"mlp": {}, "large_m": {}, "weights": "the 4096 x 4096 Student-t layer tiled to each shape"}
+    out = {"mlp": {}, "large_m": {}, "weights": "each shape's own Student-t draw on the GPU (config seeds)"}
 
-    def copies(n, k, count):
-        w = w_dev.repeat((n + N - 1) // N, (k + K - 1) // K)[:n, :k].contiguous()
+    def copies(n, k, count, seed):
+        w = synth.student_t_weights_device(n, k, seed, dev)
         q = nv.quantize_fos(w)
         del w
         codes = q.codes.unsqueeze(0).repeat(count, 1, 1)
         scales = q.scales.unsqueeze(0).repeat(count, 1, 1)
         return [nv.NVFP4Weight(codes[i], scales[i], q.tensor_scale, q.amax, None) for i in range(count)]
 
-    for name, n, k in MLP_SHAPES:
+    for name, n, k, seed in MLP_SHAPES:
         wb = bytes_gemm_weights(n, k)
         count = max(8, int((1 << 30) // wb))
-        qs = copies(n, k, count)
+        qs = copies(n, k, count, seed)
         ws = torch.empty(max(16, max(nv.workspace_size(m, n, k) for m in MLP_M)), dtype=torch.uint8, device=dev)
         res = {}
         for m in MLP_M:
@@ -513,8 +513,8 @@ def decoder_shapes(args, stream, time_op, w_dev, ceilings):
     out["qat_input_grad"] = {"note": "dx = dy @ W_hat on the packed weights (the backward GEMM of "
                                      "quantization-aware training); tflops against the bf16 MFMA peak",
                              "shapes": {}}
-    for name, n, k in LARGE_SHAPES:
-        qs = copies(n, k, 4)
+    for name, n, k, seed in LARGE_SHAPES:
+        qs = copies(n, k, 4, seed)
         ws = torch.empty(max(16, max(nv.workspace_size(m, n, k) for m in LARGE_M)), dtype=torch.uint8, device=dev)
         ws4 = torch.empty(max(nv.w4a4_workspace_size(m, n, k) for m in LARGE_M), dtype=torch.uint8, device=dev)
         res, res4, resd = {}, {}, {}
@@ -653,8 +653,8 @@ def profile_large_m(w_dev):
 
     dev = torch.device("cuda:0")
     runs = []
-    for name, n, k in LARGE_SHAPES:
-        w = w_dev.repeat((n + N - 1) // N, (k + K - 1) // K)[:n, :k].contiguous()
+    for name, n, k, seed in LARGE_SHAPES:
+        w = synth.student_t_weights_device(n, k, seed, dev)
         q = nv.quantize_fos(w)
         del w
         for m in PROFILE_M:
@@ -722,9 +722,12 @@ def decoder_model(args, stream, w_dev, ceilings):
     n = 4096, k = 14336): one FourOverSix quantization pass over all 224
     fp32 matrices (31.1 GB, amax pass + quantizer per matrix), and one
     sequential pass of the 224 W4A16 GEMMs at M = 1 and at M = 48 over the
-    4.38 GB of packed weights, each pass replayed from one HIP graph.  The
-    fp32 weights are the single layer's Student-t matrix tiled to each
-    shape (timing does not depend on the values)."""
+    4.38 GB of packed weights, each pass replayed from one HIP graph.  Each
+    of the 224 fp32 matrices is its own draw, made on the GPU with a
+    generator seeded per layer and matrix (the single layer's distribution;
+    drawing 7.8 G values on the host would take minutes); the M=4 share of
+    every matrix comes from the GPU quantizer's mask, summarised per matrix
+    kind beside the pages' 40-43 %."""
     import torch
 
     import bit_gemm_amd as nv
@@ -739,11 +742,12 @@ def decoder_model(args, stream, w_dev, ceilings):
     flat = torch.empty(total, dtype=torch.float32, device=dev)
     views, off = [], 0
     for li in range(layers):
-        for _, n, k in shapes:
+        for j, (_, n, k) in enumerate(shapes):
             v = flat[off:off + n * k].view(n, k)
-            v.copy_(w_dev.repeat((n + N - 1) // N, (k + K - 1) // K)[:n, :k])
+            v.copy_(synth.student_t_weights_device(n, k, synth.decoder_weight_seed(li, j), dev))
             views.append(v)
             off += n * k
+    torch.cuda.synchronize()
     packed = [nv.NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
                              torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
                              torch.empty(1, dtype=torch.float32, device=dev),
@@ -772,13 +776,28 @@ def decoder_model(args, stream, w_dev, ceilings):
             nv.quantize_fos(v, out=q)
 
     tq = replay_time(quant_pass)
+    # M=4 share per matrix (the last replay's masks: the same weights each time)
+    shares = [float(q.m4_mask.float().mean()) for q in packed]
+    by_kind = {}
+    for i, (name, _, _) in enumerate(shapes * layers):
+        by_kind.setdefault(name, []).append(shares[i])
+    m4 = {name: {"mean": round(sum(v) / len(v), 4), "min": round(min(v), 4), "max": round(max(v), 4)}
+          for name, v in by_kind.items()}
+    attn = [x for nm in ("q", "k", "v", "o") for x in by_kind[nm]]
+    mlp = [x for nm in ("gate", "up", "down") for x in by_kind[nm]]
     wsum = float(total)
     out = {"layers": layers, "weights": int(total), "fp32_bytes": int(4 * total),
            "packed_bytes": int(sum(bytes_gemm_weights(n, k) for _, n, k in shapes) * layers),
            "quantize_pass_ms": round(tq * 1e3, 3),
            "quantize_weights_per_s": round(wsum / tq, 1),
            "quantize_gbs_with_amax_pass": round(wsum * (4 + 4.625) / tq / 1e9, 1),
-           "quantize_gbs_single_read": round(wsum * 4.625 / tq / 1e9, 1)}
+           "quantize_gbs_single_read": round(wsum * 4.625 / tq / 1e9, 1),
+           "weights_source": "per-layer, per-matrix draws on the GPU (seed 5000 + 8 layer + matrix)",
+           "m4_share_per_matrix_kind": m4,
+           "m4_share_attention_mean": round(sum(attn) / len(attn), 4),
+           "m4_share_mlp_mean": round(sum(mlp) / len(mlp), 4),
+           "m4_share_pages_context": "40-43 % of blocks, higher in MLP than in attention QKV (real weights, "
+                                     "GPTQ; another GPU): synthetic Student-t layers are not expected to match"}
     del flat, views
     torch.cuda.empty_cache()
     for m in (1, 48):

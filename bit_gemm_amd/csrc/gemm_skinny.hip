@@ -497,15 +497,12 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
   const float s_t = tensor_scale[0];
 
   // activations of this wave's slices, once (LDS DMA: lane l -> bf16 8l .. 8l + 7)
-  auto copy_x = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < ROUNDS; ++r)
+  for (int r = 0; r < ROUNDS; ++r)
 #pragma unroll
-      for (int m = 0; m < MR; ++m)
-        copy16_to_lds(x + (int64_t)min(m, M - 1) * K + (r * W + wave) * kWaveK + 8 * lane,
-                      reinterpret_cast<uint8_t*>(xw + (r * MR + m) * kPkRow));
-    asm volatile("" ::: "memory");
-  };
+    for (int m = 0; m < MR; ++m)
+      copy16_to_lds(x + (int64_t)min(m, M - 1) * K + (r * W + wave) * kWaveK + 8 * lane,
+                    reinterpret_cast<uint8_t*>(xw + (r * MR + m) * kPkRow));
 
   const int ntiles = (N + 15) / 16;
   const int cnt = (ntiles - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;  // tiles of this workgroup
@@ -594,7 +591,6 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
   // three register sets: while tile i is consumed the loads of tiles i + 1
   // and i + 2 are in flight
   PkTile<ROUNDS> A, B, C;
-  copy_x();
   issue(A, 0);
   issue(B, 1);
   for (int i = 0; i < cnt; i += 3) {

@@ -42,6 +42,27 @@ def student_t_weights(n: int, k: int, seed: int, rng=None) -> np.ndarray:
     return w.astype(np.float32)
 
 
+def student_t_weights_device(n: int, k: int, seed: int, device) -> torch.Tensor:
+    """fp32 [n, k] on `device`, drawn there from the same distribution as
+    student_t_weights (Student-t, nu = 5, as z / sqrt(chi2_5 / 5) from six
+    normal draws; std 0.02; round(0.001 n k) distinct positions x 20) with
+    a torch generator seeded by `seed` -- not the same values as the numpy
+    draw.  For whole-model timing runs, where drawing billions of values on
+    the host would take minutes."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    z = torch.randn((n, k), generator=g, device=device, dtype=torch.float32)
+    chi2 = torch.zeros((n, k), device=device, dtype=torch.float32)
+    for _ in range(5):
+        chi2.addcmul_(e := torch.randn((n, k), generator=g, device=device, dtype=torch.float32), e)
+    w = z.div_(chi2.div_(5.0).sqrt_()).mul_(0.02 / float(np.sqrt(5.0 / 3.0)))
+    n_out = int(round(0.001 * n * k))
+    if n_out:
+        idx = torch.randperm(n * k, generator=g, device=device)[:n_out]
+        w.view(-1)[idx] *= 20.0
+    return w
+
+
 def activations(m: int, k: int, seed: int) -> torch.Tensor:
     """bf16 [m, k] CPU tensor of N(0, 1) draws."""
     rng = np.random.default_rng(seed)
