@@ -74,9 +74,12 @@ def _fixed_scales(pre: FosResult):
     return sigma, r
 
 
-def gptq_fos(w, u, amax_in=None, dtype=np.float32) -> FosResult:
+def gptq_fos(w, u, amax_in=None, dtype=np.float32, return_updated=False):
     """C10.  ``dtype=np.float64`` runs the column loop in float64 (for the
-    cross-check against the explicit inverse-Hessian form; not the contract)."""
+    cross-check against the explicit inverse-Hessian form; not the contract).
+    ``return_updated=True`` also returns the weights after the loop (every
+    column j holding w_j as it stood when it was quantized), for the pin
+    that re-evaluates the fp32 steps in exact arithmetic."""
     w = np.ascontiguousarray(w, dtype=F32)
     n, k = w.shape
     u = np.asarray(u)
@@ -102,7 +105,8 @@ def gptq_fos(w, u, amax_in=None, dtype=np.float32) -> FosResult:
         if j + 1 < k:
             wk[:, j + 1:] = wk[:, j + 1:] - e[:, None] * uk[j, j + 1:][None, :]
     codes = code[:, 0::2] | (code[:, 1::2] << 4)
-    return FosResult(codes.astype(np.uint8), pre.scales, pre.m4_mask, s_t, pre.amax)
+    res = FosResult(codes.astype(np.uint8), pre.scales, pre.m4_mask, s_t, pre.amax)
+    return (res, wk) if return_updated else res
 
 
 def gptq_fos_obs(w, hinv, amax_in=None) -> np.ndarray:
