@@ -570,10 +570,13 @@ GPTQ_SHAPES = [("w4096x4096", 4096, 4096), ("up_gate", 14336, 4096), ("down", 40
 
 
 def gptq_report(args, w_dev):
-    """GPTQ inside fixed FourOverSix scales on the decoder shapes: U (upper
-    Cholesky factor of the damped inverse Hessian) from seeded synthetic
-    calibration activations (2k x k, N(0,1) x per-channel U(1,2)), computed
-    with torch.linalg in float64 outside the timed region; then the average
+    """GPTQ inside fixed FourOverSix scales on the decoder shapes: the damped
+    Hessian H = 2 X^T X + 0.01 mean(diag) I from seeded synthetic calibration
+    activations (2k x k, N(0,1) x per-channel U(1,2), as bf16) by the
+    library's nvfp4_gptq_hessian (timed: HIP events, TFLOP/s of the full
+    2 s k^2 product against the bf16 MFMA peak), then U (upper Cholesky factor
+    of H^-1) by torch.linalg in float64 outside the timed region (a standard
+    factorization the caller supplies); then the average
     duration of whole calls (amax and quantizer kernels, then one kernel per
     64 columns) with HIP events on the call's stream.  The 4096 x 4096 layer
     is the bench's own matrix; the MLP shapes tile it (the time does not
@@ -591,12 +594,30 @@ def gptq_report(args, w_dev):
     stream = torch.cuda.current_stream(dev)
     factors = {}
 
+    hessians = {}
+
     def factor(k):
         if k not in factors:
-            x = torch.from_numpy(synth.calibration_activations(2 * k, k, GPTQ_CALIB_SEED)).to(dev)
-            h = 2.0 * (x.T @ x)
-            del x
-            h += 0.01 * torch.mean(torch.diag(h)) * torch.eye(k, dtype=torch.float64, device=dev)
+            x = torch.from_numpy(synth.calibration_activations(2 * k, k, GPTQ_CALIB_SEED)).to(torch.bfloat16).to(dev)
+            hws = torch.empty(nv.gptq_hessian_workspace_size(2 * k, k), dtype=torch.uint8, device=dev)
+            h32 = torch.empty((k, k), dtype=torch.float32, device=dev)
+            nv.gptq_hessian(x, 0.01, out=h32, workspace=hws)
+            torch.cuda.synchronize()
+            reps = 5
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                nv.gptq_hessian(x, 0.01, out=h32, workspace=hws)
+            ev1.record(stream)
+            ev1.synchronize()
+            ms = ev0.elapsed_time(ev1) / reps
+            tf = 2.0 * (2 * k) * k * k / (ms * 1e-3) / 1e12
+            hessians[k] = {"calibration_samples": 2 * k, "ms": round(ms, 4), "tflops_full_product": round(tf, 1),
+                           "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                           "note": "tiles on and above the diagonal only: the executed MFMA work is about half"}
+            del x, hws
+            h = h32.to(torch.float64)
+            del h32
             hinv = torch.cholesky_inverse(torch.linalg.cholesky(h))
             del h
             factors[k] = torch.linalg.cholesky(hinv, upper=True).to(torch.float32).contiguous()
@@ -637,6 +658,7 @@ def gptq_report(args, w_dev):
             "code_bytes_changed_vs_rtn": round(moved, 4)}
         del w, ws, q, rtn
         torch.cuda.empty_cache()
+    out["hessian"] = {f"k{k}": v for k, v in hessians.items()}
     return out
 
 

@@ -52,6 +52,8 @@ SIGNATURES = {
     "nvfp4_quantize_fos_gptq_workspace_size": (_c_size, [_c_i64, _c_i64]),
     "nvfp4_quantize_fos_gptq": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                          _c_size, _c_p]),
+    "nvfp4_gptq_hessian_workspace_size": (_c_size, [_c_i64, _c_i64]),
+    "nvfp4_gptq_hessian": (_c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_size, _c_p]),
     "nvfp4_tensor_amax": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
     "nvfp4_dequant": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p]),
     "nvfp4_w4a16_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
@@ -243,6 +245,34 @@ def quantize_fos_gptq(w: torch.Tensor, hinv_u: torch.Tensor, amax: Optional[torc
     _check(lib().nvfp4_quantize_fos_gptq(
         _ptr(w), n, k, _ptr(hinv_u), _ptr(amax), _ptr(out.amax), _ptr(out.tensor_scale), _ptr(out.codes),
         _ptr(out.scales), _ptr(out.m4_mask), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
+def gptq_hessian_workspace_size(s: int, k: int) -> int:
+    return int(lib().nvfp4_gptq_hessian_workspace_size(s, k))
+
+
+def gptq_hessian(x: torch.Tensor, damp: float = 0.01, out: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """H = 2 X^T X + damp * mean(diag(2 X^T X)) * I, float32 [k, k], from
+    bf16 calibration activations x [s, k] on the GPU (the Hessian whose
+    inverse's upper Cholesky factor quantize_fos_gptq takes)."""
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError("x must be a 2-D tensor")
+    _need(x, "x", torch.bfloat16, gpu=False)
+    s, k = x.shape
+    dev = x.device
+    if out is not None:
+        _need(out, "out", torch.float32, (k, k), gpu=False)
+    _on_gpu(dev, (x, "x"), (out, "out"))
+    if out is None:
+        out = torch.empty((k, k), dtype=torch.float32, device=dev)
+    ws = gptq_hessian_workspace_size(s, k)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)  # its size: checked by the library
+    _check(lib().nvfp4_gptq_hessian(_ptr(x), s, k, float(damp), _ptr(out), _ptr(workspace), workspace.numel(),
+                                    _stream(dev)))
     return out
 
 

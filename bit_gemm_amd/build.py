@@ -22,7 +22,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnvfp4.so")
-SOURCES = ["quantize.hip", "dequant.hip", "gemm_skinny.hip", "gemm_tiled.hip", "gptq.hip", "act_quant.hip", "gemm_dx.hip", "selftest.hip", "stream.hip", "noalloc.hip",
+SOURCES = ["quantize.hip", "dequant.hip", "gemm_skinny.hip", "gemm_tiled.hip", "gptq.hip", "act_quant.hip", "gemm_dx.hip", "selftest.hip", "stream.hip", "noalloc.hip", "hessian.hip",
            "api.cpp"]
 
 

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -35,6 +36,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;  // each dimension < 2^31
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
+constexpr int64_t kMaxHessianK = 65536;  // H is k x k fp32: 16 GiB at the limit
 
 // Per-device cache of the gfx950 check: 0 unknown, 1 ok, 2 unsupported.
 std::atomic<int> g_dev_ok[64];
@@ -210,6 +212,37 @@ NVFP4_API int nvfp4_quantize_fos_gptq(const float* w, int64_t n, int64_t k, cons
   hipError_t e = nvfp4::launch_gptq(w, n, k, hinv_u, amax_in, amax_out, tensor_scale, codes, scales,
                                     m4_mask, workspace, ci, reinterpret_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "gptq launch");
+  return NVFP4_OK;
+}
+
+NVFP4_API size_t nvfp4_gptq_hessian_workspace_size(int64_t s, int64_t k) {
+  if (s < 0 || k < 0 || k > kMaxHessianK || s >= kMaxDim || (k > 0 && s > kMaxElems / k)) return 0;
+  return nvfp4::hessian_workspace_bytes(s, k);
+}
+
+NVFP4_API int nvfp4_gptq_hessian(const void* x, int64_t s, int64_t k, float damp, float* h, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (s < 0 || k < 0) return fail(NVFP4_ERR_INVALID_VALUE, "negative dimension (s=%lld, k=%lld)", (long long)s, (long long)k);
+  if (k > kMaxHessianK || s >= kMaxDim || (k > 0 && s > kMaxElems / k))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "s=%lld, k=%lld: too large (k <= %lld)", (long long)s, (long long)k,
+                (long long)kMaxHessianK);
+  if (!(damp >= 0.0f) || !std::isfinite(damp)) return fail(NVFP4_ERR_INVALID_VALUE, "damp must be finite and >= 0");
+  if (k == 0) return NVFP4_OK;
+  if (!h || (s > 0 && !x)) return fail(NVFP4_ERR_INVALID_VALUE, "x and h are required");
+  if (!aligned(h, 4) || (x && !aligned(x, 2))) return fail(NVFP4_ERR_MISALIGNED, "x must be 2-byte and h 4-byte aligned");
+  const size_t need = nvfp4::hessian_workspace_bytes(s, k);
+  if (need > 0) {
+    if (workspace_bytes < need)
+      return fail(NVFP4_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu required", workspace_bytes, need);
+    if (!workspace) return fail(NVFP4_ERR_INVALID_VALUE, "workspace is NULL");
+    if (!aligned(workspace, 16)) return fail(NVFP4_ERR_MISALIGNED, "workspace must be 16-byte aligned");
+  }
+  int st = check_device();
+  if (st) return st;
+  hipError_t e = nvfp4::launch_hessian(reinterpret_cast<const uint16_t*>(x), s, k, damp, h, workspace,
+                                       reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "hessian launch");
   return NVFP4_OK;
 }
 

@@ -27,7 +27,6 @@
 namespace nvfp4 {
 namespace {
 
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 
 constexpr int kTM = 128;        // dy rows per workgroup
 constexpr int kTK = 128;        // weight columns (outputs) per workgroup

@@ -29,7 +29,6 @@
 namespace nvfp4 {
 namespace {
 
-typedef __attribute__((ext_vector_type(16))) float f32x16_t;  // 32x32 MFMA accumulator
 
 constexpr int kBN = 128, kBM = 128, kBK = 64;
 // LDS fragment layout (each entry 16 bytes = 8 bf16):

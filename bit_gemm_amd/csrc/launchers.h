@@ -94,6 +94,12 @@ hipError_t launch_gptq(const float* w, int64_t n, int64_t k, const float* hinv_u
                        uint8_t* codes, uint8_t* scales, uint8_t* m4_mask, void* workspace,
                        int impl, hipStream_t stream);
 
+// GPTQ's damped Hessian H = 2 X^T X + damp * mean(diag) * I (bf16 X [s, k],
+// fp32 H [k, k]); workspace: X^T as bf16 [k, s rounded up to 32].
+size_t hessian_workspace_bytes(int64_t s, int64_t k);
+hipError_t launch_hessian(const uint16_t* x, int64_t s, int64_t k, float damp, float* h, void* workspace,
+                          hipStream_t stream);
+
 // Thread-local error text and status codes of the C ABI (api.cpp), for
 // entry points defined in other sources.
 void clear_error();

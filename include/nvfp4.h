@@ -169,6 +169,33 @@ NVFP4_API int nvfp4_quantize_fos_gptq(const float* w, int64_t n, int64_t k, cons
                                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * nvfp4_gptq_hessian - GPTQ's damped Hessian from calibration activations:
+ * H = 2 X^T X + damp * mean(diag(2 X^T X)) * I (the matrix whose inverse
+ * weighs the column errors of GPTQ, Frantar et al., 2022, run inside the
+ * FourOverSix scales: [Notes07] section 03 "How we integrated it").
+ *
+ * x          device bf16 [s, k] row-major: s calibration samples of the
+ *            layer's k inputs (the activations the layer sees).
+ * damp       the damping fraction (GPTQ uses 0.01); finite, >= 0.
+ * h          device fp32 [k, k] row-major, written whole (symmetric).
+ * workspace  device buffer of >= nvfp4_gptq_hessian_workspace_size(s, k)
+ *            bytes (X^T, bf16), 16-byte aligned; contents on entry do not
+ *            matter.
+ * s >= 0, 0 <= k <= 65536.  Products of bf16 values are exact in fp32 and
+ * summed in fp32 in a fixed order (bit-reproducible); the diagonal mean is
+ * summed in float64.  s == 0 gives H = 0; k == 0 does nothing.
+ * The factor nvfp4_quantize_fos_gptq takes, the upper Cholesky factor U of
+ * H^-1, is left to the caller: it is a standard dense factorization
+ * (Cholesky of H, its inverse, Cholesky again; O(k^3) once per layer) that
+ * any linear-algebra library provides and the method does not change.
+ * Launches: a transpose, the product (tiles on and above the diagonal,
+ * mirrored), the damping.
+ */
+NVFP4_API size_t nvfp4_gptq_hessian_workspace_size(int64_t s, int64_t k);
+NVFP4_API int nvfp4_gptq_hessian(const void* x, int64_t s, int64_t k, float damp, float* h, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * nvfp4_dequant - W_hat from the packed format ([Notes07] section 02:
  * "dequant" of a block with its scale).
  *

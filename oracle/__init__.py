@@ -55,6 +55,6 @@ from .codecs import (  # noqa: F401
 )
 from .fos import quantize_fos, quantize_fos_scalar, FosResult, block_sse  # noqa: F401
 from .gemm import dequant, dequant_f64, gemm_ref  # noqa: F401
-from .gptq import gptq_fos, gptq_fos_obs, hessian_factor  # noqa: F401
+from .gptq import gptq_fos, gptq_fos_obs, hessian, hessian_factor  # noqa: F401
 from .w4a4 import ActResult, act_blockscaled, quantize_act, w4a4_gemm_ref  # noqa: F401
 from .qat import qat_forward, qat_input_grad, qat_weight_grad  # noqa: F401

@@ -44,6 +44,15 @@ from .fos import FLT_MAX, FosResult, quantize_fos
 F32 = np.float32
 
 
+def hessian(x, damp: float = 0.01) -> np.ndarray:
+    """H = 2 X^T X + damp * mean(diag(2 X^T X)) * I in float64 (GPTQ's damped
+    Hessian; the damping keeps H positive definite), x [s, k]."""
+    x = np.asarray(x, dtype=np.float64)
+    h = 2.0 * (x.T @ x)
+    h[np.diag_indices_from(h)] += damp * float(np.mean(np.diag(h))) if h.size else 0.0
+    return h
+
+
 def hessian_factor(x, damp: float = 0.01) -> np.ndarray:
     """U (fp32, upper triangular) with H^-1 = U^T U, H = 2 X^T X + damp *
     mean(diag) * I, from calibration activations x [s, k], computed in float64
@@ -52,9 +61,7 @@ def hessian_factor(x, damp: float = 0.01) -> np.ndarray:
     route for a symmetric positive definite inverse."""
     from scipy.linalg import lapack
 
-    x = np.asarray(x, dtype=np.float64)
-    h = 2.0 * (x.T @ x)
-    h[np.diag_indices_from(h)] += damp * float(np.mean(np.diag(h)))
+    h = hessian(x, damp)
     c, info = lapack.dpotrf(h, lower=True)
     if info != 0:
         raise np.linalg.LinAlgError(f"H is not positive definite (potrf info {info})")

@@ -145,3 +145,74 @@ def test_gptq_many_panels_any_triangular_factor():
     r = oracle.gptq_fos(w, u)
     _assert_same(q, r, f"{n}x{k}")
     assert not np.array_equal(r.codes, oracle.quantize_fos(w).codes)
+
+
+# ---------------------------------------------------------------------------
+# nvfp4_gptq_hessian: H = 2 X^T X + damp * mean(diag) * I from bf16 X against
+# oracle.hessian (float64) on the same bf16 values.  Products of bf16 values
+# are exact in fp32, so the only error is fp32 summation over s samples:
+# |dH_ij| <= (s + 4) 2^-24 (2 sum_t |x_ti x_tj|) off the diagonal, plus the
+# rounding of the damping on it.
+# ---------------------------------------------------------------------------
+def _hessian_case(s, k, seed, damp=0.01):
+    x = torch.from_numpy(synth.calibration_activations(s, k, seed)).to(torch.bfloat16)
+    xv = x.float().numpy().astype(np.float64)
+    ref = oracle.hessian(xv, damp)
+    h = nv.gptq_hessian(x.cuda(), damp).cpu().numpy().astype(np.float64)
+    a = 2.0 * (np.abs(xv).T @ np.abs(xv))
+    u = 2.0 ** -24
+    bound = (s + 4) * u * a
+    bound[np.diag_indices(k)] += (s + 4) * u * damp * float(np.mean(np.diag(a))) + 2 * u * np.abs(np.diag(ref))
+    err = np.abs(h - ref)
+    assert np.all(err <= bound), (s, k, float(np.max(err / np.maximum(bound, 1e-300))))
+    rel = np.linalg.norm(h - ref) / max(np.linalg.norm(ref), 1e-300)
+    assert rel <= 1e-5, (s, k, rel)
+    assert np.array_equal(h, h.T), "H is symmetric bit for bit"
+    return x, h
+
+
+@pytest.mark.parametrize("s,k", [(1, 16), (37, 48), (300, 130), (512, 256), (1000, 1100), (64, 4096)])
+def test_hessian_matches_oracle(s, k):
+    print("hessian", s, k, flush=True)
+    _hessian_case(s, k, 1700 + s + k)
+
+
+def test_hessian_full_size_and_deterministic():
+    # the benchmark's calibration size for the 4096 x 4096 layer: s = 2k
+    print("hessian 8192 x 4096", flush=True)
+    x, h = _hessian_case(8192, 4096, 4242)
+    h2 = nv.gptq_hessian(x.cuda(), 0.01).cpu().numpy()
+    assert np.array_equal(h.astype(np.float32), h2)
+
+
+def test_hessian_empty_and_errors():
+    lib = nv.lib()
+    h = torch.full((16, 16), 7.0, dtype=torch.float32, device="cuda")
+    out = nv.gptq_hessian(torch.empty((0, 16), dtype=torch.bfloat16, device="cuda"), 0.01, out=h)
+    torch.cuda.synchronize()
+    assert bool((out == 0).all())  # s = 0: H = 0
+    assert lib.nvfp4_gptq_hessian(None, 4, 0, 0.01, None, None, 0, None) == nv.NVFP4_OK  # k = 0: nothing
+    x = torch.zeros((4, 16), dtype=torch.bfloat16, device="cuda")
+    assert lib.nvfp4_gptq_hessian(x.data_ptr(), 4, 16, -1.0, h.data_ptr(), None, 0, None) == 1
+    assert "damp" in lib.nvfp4_last_error().decode()
+    assert lib.nvfp4_gptq_hessian(x.data_ptr(), 4, 16, 0.01, h.data_ptr(), None, 0, None) == 4  # no workspace
+    assert lib.nvfp4_gptq_hessian(x.data_ptr(), 4, 65537, 0.01, h.data_ptr(), None, 0, None) == 2
+
+
+def test_gptq_from_library_hessian():
+    """The library's H feeds GPTQ: U from it (float64 Cholesky route on the
+    host, as oracle.hessian_factor does), then the GPU quantizer and the
+    oracle on the same U agree bit for bit."""
+    from scipy.linalg import lapack
+
+    n, k, s = 96, 256, 512
+    w = synth.student_t_weights(n, k, 1800)
+    x = torch.from_numpy(synth.calibration_activations(s, k, 1801)).to(torch.bfloat16)
+    h = nv.gptq_hessian(x.cuda(), 0.01).cpu().numpy().astype(np.float64)
+    c, info = lapack.dpotrf(h, lower=True)
+    assert info == 0
+    hinv, info = lapack.dpotri(c, lower=True)
+    assert info == 0
+    hinv = np.tril(hinv) + np.tril(hinv, -1).T
+    u = np.ascontiguousarray(np.linalg.cholesky(hinv).T).astype(np.float32)
+    _assert_same(_run(w, u), oracle.gptq_fos(w, u), "library Hessian")

@@ -363,3 +363,17 @@ def test_binding_rejects_wrong_output_shapes():
         nv.quantize_act(x, out=act)
     with pytest.raises(ValueError, match="out must have at least 1"):
         nv.tensor_amax(w, out=torch.zeros(0, dtype=torch.float32))
+
+
+def test_hessian_host_validation(L):
+    """nvfp4_gptq_hessian rejects bad arguments before any GPU call."""
+    assert L.nvfp4_gptq_hessian_workspace_size(8192, 4096) == 4096 * 8192 * 2
+    assert L.nvfp4_gptq_hessian_workspace_size(37, 48) == 48 * 64 * 2  # samples rounded up to 32
+    assert L.nvfp4_gptq_hessian_workspace_size(-1, 48) == 0
+    assert L.nvfp4_gptq_hessian(None, 4, 0, 0.01, None, None, 0, None) == nv.NVFP4_OK  # k = 0: nothing
+    assert L.nvfp4_gptq_hessian(16, 4, 16, -1.0, 64, None, 0, None) == 1
+    assert L.nvfp4_gptq_hessian(16, 4, 16, float("nan"), 64, None, 0, None) == 1
+    assert L.nvfp4_gptq_hessian(16, 4, 16, 0.01, 64, None, 0, None) == 4  # workspace too small
+    assert L.nvfp4_gptq_hessian(16, 4, 65537, 0.01, 64, None, 0, None) == 2
+    assert L.nvfp4_gptq_hessian(17, 4, 16, 0.01, 64, 1024, 1 << 20, None) == 3  # x not 2-byte aligned
+    assert L.nvfp4_gptq_hessian(None, 4, 16, 0.01, 64, 1024, 1 << 20, None) == 1  # x required for s > 0

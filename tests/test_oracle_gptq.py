@@ -217,3 +217,17 @@ def test_exact_evaluation_sees_a_fused_update():
                 row[l] = _rnd32(row[l] - e * Q(float(u[j, l])))
         differs |= any(np.float32(float(a)).view(np.uint32) != b.view(np.uint32) for a, b in zip(row, upd[i]))
     assert differs
+
+
+def test_hessian_is_the_damped_gram_matrix_exactly():
+    """oracle.hessian against its definition written out in exact rationals
+    on small integers and halves (every float64 operation exact here):
+    H_ij = 2 sum_s x_si x_sj, plus damp * mean_i(H_ii) on the diagonal."""
+    x = np.array([[1, -2, 0.5], [3, 0, -1], [0.5, 1.5, 2], [-1, 1, 1], [2, -0.5, 0]], dtype=np.float64)
+    damp = 0.25
+    s, k = x.shape
+    g = [[2 * sum(Q(float(x[t, i])) * Q(float(x[t, j])) for t in range(s)) for j in range(k)] for i in range(k)]
+    lam = Q(1, 4) * sum(g[i][i] for i in range(k)) / k
+    want = np.array([[float(g[i][j] + (lam if i == j else 0)) for j in range(k)] for i in range(k)])
+    assert np.array_equal(oracle.hessian(x, damp), want)
+    assert np.array_equal(oracle.hessian(x, 0.0), np.array([[float(g[i][j]) for j in range(k)] for i in range(k)]))
