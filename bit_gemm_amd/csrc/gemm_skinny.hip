@@ -41,6 +41,8 @@
 #include "launchers.h"
 #include "nvfp4_device.h"
 
+#include <type_traits>
+
 namespace nvfp4 {
 namespace {
 
@@ -575,19 +577,31 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
       }
     }
   };
-  auto consume = [&](PkTile<ROUNDS>& T, int i) __attribute__((always_inline)) {
+  auto consume = [&](PkTile<ROUNDS>& T, int i, auto after) __attribute__((always_inline)) {
+    constexpr int kAfter = decltype(after)::value;  // loads issued after this tile's
     if constexpr (kDot) {
       float acc[MR];
 #pragma unroll
       for (int m = 0; m < MR; ++m) acc[m] = 0.0f;
-      pk_dot<0, 0, MR, IMPL, ROUNDS, kPkAhead * kPkLoadsPerSlice * ROUNDS>(T, xw, g, acc);
+      pk_dot<0, 0, MR, IMPL, ROUNDS, kAfter>(T, xw, g, acc);
       finish(i, acc);
     } else {
       f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      pk_mfma<0, 0, MR, IMPL, ROUNDS, kPkAhead * kPkLoadsPerSlice * ROUNDS>(T, xw, g, min(r16, MR - 1), acc);
+      pk_mfma<0, 0, MR, IMPL, ROUNDS, kAfter>(T, xw, g, min(r16, MR - 1), acc);
       finish(i, acc);
     }
   };
+  using Ahead = std::integral_constant<int, kPkAhead * kPkLoadsPerSlice * ROUNDS>;
+  // One tile per workgroup (no more tiles than CUs): no look-ahead loads
+  // (they would only fill the memory queue), the tile's steps waited for one
+  // by one.  (The branch comes before the tile's loads: a register whose load
+  // is in flight must not be live across it.)
+  if (cnt == 1) {
+    PkTile<ROUNDS> T;
+    issue(T, 0);
+    consume(T, 0, std::integral_constant<int, 0>{});
+    return;
+  }
   // three register sets: while tile i is consumed the loads of tiles i + 1
   // and i + 2 are in flight
   PkTile<ROUNDS> A, B, C;
@@ -595,13 +609,13 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
   issue(B, 1);
   for (int i = 0; i < cnt; i += 3) {
     issue(C, i + 2);
-    consume(A, i);
+    consume(A, i, Ahead{});
     if (i + 1 >= cnt) break;
     issue(A, i + 3);
-    consume(B, i + 1);
+    consume(B, i + 1, Ahead{});
     if (i + 2 >= cnt) break;
     issue(B, i + 4);
-    consume(C, i + 2);
+    consume(C, i + 2, Ahead{});
   }
   wait_vm_all();  // the last (unused) loads land before the wave ends
 }
