@@ -770,12 +770,31 @@ def decoder_model(args, stream, w_dev, ceilings):
             views.append(v)
             off += n * k
     torch.cuda.synchronize()
-    packed = [nv.NVFP4Weight(torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
-                             torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
-                             torch.empty(1, dtype=torch.float32, device=dev),
-                             torch.empty(1, dtype=torch.float32, device=dev),
-                             torch.empty((n, k // 16), dtype=torch.uint8, device=dev))
-              for _ in range(layers) for _, n, k in shapes]
+    # packed weights stacked per layer as the grouped GEMM reads them: q, k, v
+    # in one buffer, gate and up in one, o and down alone; every matrix is
+    # also a view of its rows (the per-matrix GEMM pass uses those)
+    def stacked(rows, k):
+        return nv.NVFP4Grouped(codes=torch.empty((sum(rows), k // 2), dtype=torch.uint8, device=dev),
+                               scales=torch.empty((sum(rows), k // 16), dtype=torch.uint8, device=dev),
+                               tensor_scales=torch.empty(len(rows), dtype=torch.float32, device=dev),
+                               amax=torch.empty(len(rows), dtype=torch.float32, device=dev),
+                               m4_mask=torch.empty((sum(rows), k // 16), dtype=torch.uint8, device=dev),
+                               group_rows=tuple(rows))
+
+    names = [nm for nm, _, _ in shapes]
+    dims = {nm: (n, k) for nm, n, k in shapes}
+    groups_of_layer = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+    layer_groups, packed = [], []
+    for _ in range(layers):
+        per = {}
+        gl = []
+        for grp in groups_of_layer:
+            st = stacked([dims[nm][0] for nm in grp], dims[grp[0]][1])
+            gl.append(st)
+            for i, nm in enumerate(grp):
+                per[nm] = st.group(i)
+        layer_groups.append(gl)
+        packed.extend(per[nm] for nm in names)
     torch.cuda.synchronize()
 
     def replay_time(fn, reps=3):
@@ -839,7 +858,27 @@ def decoder_model(args, stream, w_dev, ceilings):
                                   "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                                   "frac_read_ceiling_1GiB": round(gbs / ceilings[str(1 << 30)]["gbs"], 4),
                                   "us_per_layer": round(tg * 1e6 / layers, 2)}
-    del packed
+        # the same pass with the matrices that share an input in one call
+        # each (q/k/v, gate/up: nvfp4_w4a16_gemm_grouped): 4 calls per layer
+        yg = {sum(st.group_rows): torch.empty((m, sum(st.group_rows)), dtype=torch.bfloat16, device=dev)
+              for st in layer_groups[0]}
+        wsg = torch.empty(max(16, max(nv.workspace_size(m, sum(st.group_rows), st.codes.shape[1] * 2)
+                                      for st in layer_groups[0])), dtype=torch.uint8, device=dev)
+
+        def grouped_pass():
+            for gl in layer_groups:
+                for st in gl:
+                    k = st.codes.shape[1] * 2
+                    nv.w4a16_gemm_grouped(xs[k], st, out=yg[sum(st.group_rows)], workspace=wsg)
+
+        tgg = replay_time(grouped_pass)
+        gbs = out["packed_bytes"] / tgg / 1e9
+        out[f"gemm_pass_grouped_m{m}"] = {"us": round(tgg * 1e6, 1), "weight_gbs": round(gbs, 1),
+                                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                          "frac_read_ceiling_1GiB": round(gbs / ceilings[str(1 << 30)]["gbs"], 4),
+                                          "us_per_layer": round(tgg * 1e6 / layers, 2), "calls_per_layer": 4}
+        del yg, wsg
+    del packed, layer_groups
     torch.cuda.empty_cache()
     return out
 

@@ -54,6 +54,8 @@ SIGNATURES = {
                                          _c_size, _c_p]),
     "nvfp4_gptq_hessian_workspace_size": (_c_size, [_c_i64, _c_i64]),
     "nvfp4_gptq_hessian": (_c_int, [_c_p, _c_i64, _c_i64, ctypes.c_float, _c_p, _c_p, _c_size, _c_p]),
+    "nvfp4_w4a16_gemm_grouped": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_int, _c_p, _c_i64, _c_i64, _c_int, _c_p,
+                                          _c_size, _c_p]),
     "nvfp4_tensor_amax": (_c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p]),
     "nvfp4_dequant": (_c_int, [_c_p, _c_p, _c_p, _c_p, _c_i64, _c_i64, _c_int, _c_p]),
     "nvfp4_w4a16_gemm_workspace_size": (_c_size, [_c_i64, _c_i64, _c_i64]),
@@ -340,6 +342,91 @@ def w4a16_gemm(x: torch.Tensor, q: NVFP4Weight, out_dtype: torch.dtype = torch.b
     _check(lib().nvfp4_w4a16_gemm_ex(
         _ptr(x), _ptr(q.codes), _ptr(q.scales), _ptr(q.tensor_scale), _ptr(out), m, n, k, code,
         _ptr(workspace), ws_bytes, path, split_k, impl, _stream(dev)))
+    return out
+
+
+@dataclass
+class NVFP4Grouped:
+    """G packed NVFP4 matrices of the same k stacked row-wise (the layout
+    nvfp4_w4a16_gemm_grouped reads): group g owns rows
+    [sum(group_rows[:g]), sum(group_rows[:g + 1])) of codes, scales and the
+    mask, and element g of tensor_scales and amax."""
+
+    codes: torch.Tensor  # uint8 [n_total, k/2]
+    scales: torch.Tensor  # uint8 [n_total, k/16]
+    tensor_scales: torch.Tensor  # float32 [G]
+    amax: torch.Tensor  # float32 [G]
+    m4_mask: Optional[torch.Tensor]  # uint8 [n_total, k/16] or None
+    group_rows: tuple
+
+    def group(self, g: int) -> NVFP4Weight:
+        r0 = sum(self.group_rows[:g])
+        r1 = r0 + self.group_rows[g]
+        return NVFP4Weight(self.codes[r0:r1], self.scales[r0:r1], self.tensor_scales[g:g + 1], self.amax[g:g + 1],
+                           None if self.m4_mask is None else self.m4_mask[r0:r1])
+
+
+def quantize_fos_grouped(ws, with_mask: bool = True) -> NVFP4Grouped:
+    """FourOverSix quantization of G float32 GPU matrices [n_g, k] (each
+    n_g a multiple of 16), each with its own tensor scale, straight into
+    stacked buffers."""
+    ws = list(ws)
+    if not ws or len(ws) > 4:
+        raise ValueError("1 to 4 matrices")
+    for i, w in enumerate(ws):
+        if not isinstance(w, torch.Tensor) or w.dim() != 2:
+            raise ValueError(f"matrix {i} must be a 2-D tensor")
+        if w.shape[1] != ws[0].shape[1] or w.shape[0] % 16 != 0 or w.shape[0] == 0:
+            raise ValueError(f"matrix {i}: every matrix needs the same k and a positive multiple of 16 rows")
+    k = ws[0].shape[1]
+    rows = tuple(int(w.shape[0]) for w in ws)
+    n = sum(rows)
+    dev = ws[0].device
+    out = NVFP4Grouped(codes=torch.empty((n, k // 2), dtype=torch.uint8, device=dev),
+                       scales=torch.empty((n, k // 16), dtype=torch.uint8, device=dev),
+                       tensor_scales=torch.empty(len(ws), dtype=torch.float32, device=dev),
+                       amax=torch.empty(len(ws), dtype=torch.float32, device=dev),
+                       m4_mask=torch.empty((n, k // 16), dtype=torch.uint8, device=dev) if with_mask else None,
+                       group_rows=rows)
+    for g, w in enumerate(ws):
+        quantize_fos(w, out=out.group(g))
+    return out
+
+
+def w4a16_gemm_grouped(x: torch.Tensor, gq: NVFP4Grouped, out_dtype: torch.dtype = torch.bfloat16,
+                       out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[m, n_total] = x @ [W_hat_0; W_hat_1; ...]^T, group g's columns with
+    its own tensor scale, in one call (nvfp4_w4a16_gemm_grouped)."""
+    G = len(gq.group_rows)
+    n = sum(gq.group_rows)
+    if not isinstance(gq.codes, torch.Tensor) or gq.codes.dim() != 2 or gq.codes.shape[0] != n:
+        raise ValueError("codes must be [n_total, k/2]")
+    k = gq.codes.shape[1] * 2
+    _need(gq.codes, "codes", torch.uint8, (n, k // 2), gpu=False)
+    _need(gq.scales, "scales", torch.uint8, (n, k // 16), gpu=False)
+    _need(gq.tensor_scales, "tensor_scales", torch.float32, None, min_numel=G, gpu=False)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != k:
+        raise ValueError(f"x must be [m, {k}], got {tuple(getattr(x, 'shape', ()))}")
+    _need(x, "x", torch.bfloat16, gpu=False)
+    m = x.shape[0]
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out_dtype must be float32 or bfloat16, got {out_dtype}")
+    dev = gq.codes.device
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    _need(out, "out", out_dtype, (m, n), gpu=False)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, gpu=False)
+    _on_gpu(dev, (x, "x"), (gq.codes, "codes"), (gq.scales, "scales"), (gq.tensor_scales, "tensor_scales"),
+            (out, "out"), (workspace, "workspace"))
+    need = workspace_size(m, n, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    rows = (ctypes.c_int64 * G)(*gq.group_rows)
+    _check(lib().nvfp4_w4a16_gemm_grouped(
+        _ptr(x), _ptr(gq.codes), _ptr(gq.scales), _ptr(gq.tensor_scales), ctypes.cast(rows, ctypes.c_void_p), G,
+        _ptr(out), m, k, {torch.float32: F32, torch.bfloat16: BF16}[out_dtype], _ptr(workspace),
+        0 if workspace is None else workspace.numel(), _stream(dev)))
     return out
 
 

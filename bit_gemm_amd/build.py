@@ -46,20 +46,30 @@ COMMON = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+# The GEMM sources once more with one tensor scale per group of stacked
+# matrices (namespace nvfp4::grouped, for nvfp4_w4a16_gemm_grouped).
+VARIANTS = [("gemm_skinny.hip", "gemm_skinny_grouped.o", ["-DNVFP4_GROUPED=1"]),
+            ("gemm_tiled.hip", "gemm_tiled_grouped.o", ["-DNVFP4_GROUPED=1"])]
+
+
+def _compile(job) -> str:
+    src, obj_name, defs = job if isinstance(job, tuple) else (job, os.path.splitext(job)[0] + ".o", [])
+    obj = os.path.join(BUILD, obj_name)
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc(), *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *COMMON, *defs, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
+def build(jobs: int = 6, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    # the two slowest compiles (and their grouped variants) first
+    order = ["gemm_skinny.hip", VARIANTS[0], "gemm_tiled.hip", VARIANTS[1]] + \
+        [s for s in SOURCES if s not in ("gemm_skinny.hip", "gemm_tiled.hip")]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, order))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

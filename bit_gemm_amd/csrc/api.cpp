@@ -305,12 +305,12 @@ NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size(int64_t m, int64_t n, int64_t k
   return nvfp4_w4a16_gemm_workspace_size_ex(m, n, k, NVFP4_PATH_AUTO, 0);
 }
 
-NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uint8_t* scales,
-                                  const float* tensor_scale, void* y, int64_t m, int64_t n,
-                                  int64_t k, int out_dtype, void* workspace,
-                                  size_t workspace_bytes, int path, int split_k, int impl,
-                                  void* stream) {
-  g_last_error.clear();
+namespace {
+// The W4A16 GEMM with one tensor scale per output column group (see RowScale).
+int gemm_common(const void* x, const uint8_t* codes, const uint8_t* scales, nvfp4::RowScale rs, void* y,
+                int64_t m, int64_t n, int64_t k, int out_dtype, void* workspace, size_t workspace_bytes,
+                int path, int split_k, int impl, void* stream) {
+  const float* tensor_scale = rs.ts;
   int st = check_nk(n, k);
   if (st) return st;
   if (m < 0) return fail(NVFP4_ERR_INVALID_VALUE, "negative m=%lld", (long long)m);
@@ -354,14 +354,48 @@ NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uin
   if ((st = check_device())) return st;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
+  const bool grouped = rs.b1 != INT32_MAX;
+  const int f32 = out_dtype == NVFP4_F32;
   if (p == NVFP4_PATH_SKINNY)
-    e = nvfp4::launch_skinny(x, codes, scales, tensor_scale, y, m, n, k, out_dtype == NVFP4_F32, plan,
-                             workspace, ci, s);
+    e = grouped ? nvfp4::grouped::launch_skinny(x, codes, scales, rs, y, m, n, k, f32, plan, workspace, ci, s)
+                : nvfp4::launch_skinny(x, codes, scales, rs, y, m, n, k, f32, plan, workspace, ci, s);
   else
-    e = nvfp4::launch_tiled(x, codes, scales, tensor_scale, y, m, n, k, out_dtype == NVFP4_F32, tplan,
-                            workspace, ci, s);
+    e = grouped ? nvfp4::grouped::launch_tiled(x, codes, scales, rs, y, m, n, k, f32, tplan, workspace, ci, s)
+                : nvfp4::launch_tiled(x, codes, scales, rs, y, m, n, k, f32, tplan, workspace, ci, s);
   if (e != hipSuccess) return hip_fail(e, "gemm launch");
   return NVFP4_OK;
+}
+}  // namespace
+
+NVFP4_API int nvfp4_w4a16_gemm_ex(const void* x, const uint8_t* codes, const uint8_t* scales,
+                                  const float* tensor_scale, void* y, int64_t m, int64_t n,
+                                  int64_t k, int out_dtype, void* workspace,
+                                  size_t workspace_bytes, int path, int split_k, int impl,
+                                  void* stream) {
+  g_last_error.clear();
+  return gemm_common(x, codes, scales, nvfp4::RowScale::one(tensor_scale), y, m, n, k, out_dtype, workspace,
+                     workspace_bytes, path, split_k, impl, stream);
+}
+
+NVFP4_API int nvfp4_w4a16_gemm_grouped(const void* x, const uint8_t* codes, const uint8_t* scales,
+                                       const float* tensor_scales, const int64_t* group_rows, int groups,
+                                       void* y, int64_t m, int64_t k, int out_dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  g_last_error.clear();
+  if (groups < 1 || groups > 4) return fail(NVFP4_ERR_INVALID_VALUE, "groups=%d: 1 to 4", groups);
+  if (!group_rows) return fail(NVFP4_ERR_INVALID_VALUE, "group_rows is required");
+  int64_t n = 0;
+  int b[3] = {INT32_MAX, INT32_MAX, INT32_MAX};
+  for (int g = 0; g < groups; ++g) {
+    if (group_rows[g] <= 0 || group_rows[g] % 16 != 0)
+      return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "group %d has %lld rows: a positive multiple of 16", g,
+                  (long long)group_rows[g]);
+    if (g > 0) b[g - 1] = (int)n;
+    n += group_rows[g];
+    if (n >= ((int64_t)1 << 27)) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "too many rows (%lld)", (long long)n);
+  }
+  return gemm_common(x, codes, scales, nvfp4::RowScale{tensor_scales, b[0], b[1], b[2]}, y, m, n, k, out_dtype,
+                     workspace, workspace_bytes, NVFP4_PATH_AUTO, 0, NVFP4_IMPL_DEFAULT, stream);
 }
 
 NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,

@@ -213,7 +213,7 @@ hipError_t launch_gemm_dx(const uint16_t* dy, const uint8_t* codes, const uint8_
                      (int)m, (int)n, (int)k, p.steps_per, out_f32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  return launch_split_reduce(ws, tensor_scale, dx, m * k, p.splits, out_f32, stream);
+  return launch_split_reduce(ws, RowScale::one(tensor_scale), dx, m * k, k, p.splits, out_f32, stream);
 }
 
 }  // namespace nvfp4

@@ -44,6 +44,7 @@
 #include <type_traits>
 
 namespace nvfp4 {
+NVFP4_VARIANT_BEGIN
 namespace {
 
 constexpr int kWaves = 4;
@@ -193,7 +194,7 @@ template <int MR, int IMPL, bool K32, bool K128, bool ONE>
 __global__ __launch_bounds__(512) void k_skinny_fk(const uint16_t* __restrict__ x,
                                                    const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ scales,
-                                                   const float* __restrict__ tensor_scale,
+                                                   const KScale tensor_scale,
                                                    void* __restrict__ y, int M, int N, int K,
                                                    int rounds, int out_f32) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(512) void k_skinny_fk(const uint16_t* __restrict__ 
   red[wave * 64 + lane] = acc;
   __syncthreads();
   if (wave != 0) return;
-  const float s_t = tensor_scale[0];
+  const float s_t = first_scale(tensor_scale);
   f32x4_t t = red[lane];
   for (int w = 1; w < nwaves; ++w) {
     const f32x4_t u = red[w * 64 + lane];
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(512) void k_skinny_fk(const uint16_t* __restrict__ 
   const int nbase = blockIdx.x * 16 + 4 * g;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    if (nbase + i < N) store_out(y, (int64_t)r16 * N + nbase + i, t[i] * s_t, out_f32);
+    if (nbase + i < N) store_out(y, (int64_t)r16 * N + nbase + i, t[i] * col_scale(tensor_scale, nbase + i, s_t), out_f32);
 }
 
 // Full-K kernel for one or two tokens: VALU dot products instead of MFMAs
@@ -325,7 +326,7 @@ template <int MR, int IMPL, bool K32, bool K128, bool ONE>
 __global__ __launch_bounds__(512) void k_skinny_dot(const uint16_t* __restrict__ x,
                                                     const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ scales,
-                                                    const float* __restrict__ tensor_scale,
+                                                    const KScale tensor_scale,
                                                     void* __restrict__ y, int M, int N, int K,
                                                     int rounds, int out_f32) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -379,13 +380,13 @@ __global__ __launch_bounds__(512) void k_skinny_dot(const uint16_t* __restrict__
   }
   __syncthreads();
   if (wave != 0 || g != 0 || !row_ok) return;
-  const float s_t = tensor_scale[0];
+  const float s_t = first_scale(tensor_scale);
 #pragma unroll
   for (int m = 0; m < MR; ++m) {
     if (m >= M) continue;
     float t = red[m * 16 + r16];
     for (int w = 1; w < nwaves; ++w) t += red[(w * MR + m) * 16 + r16];
-    store_out(y, (int64_t)m * N + row, t * s_t, out_f32);
+    store_out(y, (int64_t)m * N + row, t * col_scale(tensor_scale, row, s_t), out_f32);
   }
 }
 
@@ -486,7 +487,7 @@ template <int MR, int IMPL, int ROUNDS>
 __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ x,
                                                    const uint8_t* __restrict__ codes,
                                                    const uint8_t* __restrict__ scales,
-                                                   const float* __restrict__ tensor_scale,
+                                                   const KScale tensor_scale,
                                                    void* __restrict__ y, int M, int N, int K, int out_f32) {
   constexpr bool kDot = pk_dot_path(MR, IMPL);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -496,7 +497,7 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
   const int g = lane >> 4, r16 = lane & 15;
   uint16_t* xw = reinterpret_cast<uint16_t*>(lds) + wave * (ROUNDS * MR * kPkRow);
   uint8_t* red = lds + (size_t)W * ROUNDS * MR * kPkRow * 2;  // [2][W] partial tiles
-  const float s_t = tensor_scale[0];
+  const float s_t = first_scale(tensor_scale);
 
   // activations of this wave's slices, once (LDS DMA: lane l -> bf16 8l .. 8l + 7)
 #pragma unroll
@@ -551,7 +552,7 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
         const int m = lane >> 4, row = 16 * t + (lane & 15);
         float v = rf[lane];
         for (int w = 1; w < W; ++w) v += rf[w * MR * 16 + lane];
-        if (m < M && row < N) store_out(y, (int64_t)m * N + row, v * s_t, out_f32);
+        if (m < M && row < N) store_out(y, (int64_t)m * N + row, v * col_scale(tensor_scale, row, s_t), out_f32);
       }
     } else {
       f32x4_t* rf = reinterpret_cast<f32x4_t*>(red) + (size_t)par * W * 64;
@@ -572,7 +573,7 @@ __global__ __launch_bounds__(512) void k_skinny_pk(const uint16_t* __restrict__ 
         if (r16 < M) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (nb + e < N) store_out(y, (int64_t)r16 * N + nb + e, v[e] * s_t, out_f32);
+            if (nb + e < N) store_out(y, (int64_t)r16 * N + nb + e, v[e] * col_scale(tensor_scale, nb + e, s_t), out_f32);
         }
       }
     }
@@ -723,7 +724,7 @@ template <int MT, int IMPL, int NSTEP, int T>
 __global__ __launch_bounds__(T == 1 ? 512 : 256) void k_skinny_fx(const uint16_t* __restrict__ x,
                                                                   const uint8_t* __restrict__ codes,
                                                                   const uint8_t* __restrict__ scales,
-                                                                  const float* __restrict__ tensor_scale,
+                                                                  const KScale tensor_scale,
                                                                   void* __restrict__ y, int M, int N, int K,
                                                                   int out_f32) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -733,7 +734,7 @@ __global__ __launch_bounds__(T == 1 ? 512 : 256) void k_skinny_fx(const uint16_t
   const int g = lane >> 4, c16 = lane & 15;
   uint8_t* xbuf = lds + (size_t)wave * 2 * 4096 * MT;            // [2][16 MT rows][256 bytes]
   f32x4_t* red = reinterpret_cast<f32x4_t*>(lds + (size_t)W * 2 * 4096 * MT);  // [W][T][MT][64]
-  const float s_t = tensor_scale[0];
+  const float s_t = first_scale(tensor_scale);
   const int n0 = blockIdx.x * 16 * T;
   const int k0 = wave * NSTEP * kStepK;
   const uint8_t* cp[T];
@@ -789,7 +790,7 @@ __global__ __launch_bounds__(T == 1 ? 512 : 256) void k_skinny_fx(const uint16_t
     if (m >= M) continue;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (nb + e < N) store_out(y, (int64_t)m * N + nb + e, v[e] * s_t, out_f32);
+      if (nb + e < N) store_out(y, (int64_t)m * N + nb + e, v[e] * col_scale(tensor_scale, nb + e, s_t), out_f32);
   }
 }
 
@@ -799,7 +800,7 @@ template <int MT, int IMPL, bool K32>
 __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
                                                 const uint8_t* __restrict__ codes,
                                                 const uint8_t* __restrict__ scales,
-                                                const float* __restrict__ tensor_scale,
+                                                const KScale tensor_scale,
                                                 void* __restrict__ y, float* __restrict__ ws,
                                                 int M, int N, int K, int kchunk, int splits,
                                                 int out_f32) {
@@ -925,7 +926,7 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
     }
   }
 
-  const float s_t = tensor_scale[0];
+  const float s_t = first_scale(tensor_scale);
   const int nbase = blockIdx.x * kRowsPerWg + wave * 16 + 4 * g;
   if (splits == 1) {
 #pragma unroll
@@ -934,7 +935,7 @@ __global__ __launch_bounds__(256) void k_skinny(const uint16_t* __restrict__ x,
       if (m >= M) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * s_t, out_f32);
+        if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * col_scale(tensor_scale, nbase + i, s_t), out_f32);
     }
     return;
   }
@@ -1022,7 +1023,7 @@ template <int MT, int IMPL, int NKS>
 __global__ __launch_bounds__(256) void k_skinny_pipe(const uint16_t* __restrict__ x,
                                                      const uint8_t* __restrict__ codes,
                                                      const uint8_t* __restrict__ scales,
-                                                     const float* __restrict__ tensor_scale,
+                                                     const KScale tensor_scale,
                                                      void* __restrict__ y, float* __restrict__ ws,
                                                      int M, int N, int K, int out_f32) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -1062,14 +1063,14 @@ __global__ __launch_bounds__(256) void k_skinny_pipe(const uint16_t* __restrict_
 
   const int nbase = blockIdx.x * kRowsPerWg + wave * 16 + 4 * g;
   if (gridDim.y == 1) {
-    const float s_t = tensor_scale[0];
+    const float s_t = first_scale(tensor_scale);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = mt * 16 + r16;
       if (m >= M) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * s_t, out_f32);
+        if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * col_scale(tensor_scale, nbase + i, s_t), out_f32);
     }
     return;
   }
@@ -1160,7 +1161,7 @@ template <int MT, int IMPL, int NST>
 __global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__ x,
                                                     const uint8_t* __restrict__ codes,
                                                     const uint8_t* __restrict__ scales,
-                                                    const float* __restrict__ tensor_scale,
+                                                    const KScale tensor_scale,
                                                     void* __restrict__ y, float* __restrict__ ws, int M,
                                                     int N, int K, int rows, int out_f32) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
@@ -1200,7 +1201,7 @@ __global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__
   wait_vm<2 * NST>(A.cw[0], A.sb[0]);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");  // no LDS read moves above the barrier
-  const float s_t = tensor_scale[0];
+  const float s_t = first_scale(tensor_scale);
   const int64_t mn = (int64_t)M * N;
   auto finish = [&](int t, const f32x4_t* acc) {
     const int nbase = rg0 + 16 * t + 4 * g;
@@ -1211,7 +1212,7 @@ __global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__
       if (gridDim.y == 1) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * s_t, out_f32);
+          if (nbase + i < N) store_out(y, (int64_t)m * N + nbase + i, acc[mt][i] * col_scale(tensor_scale, nbase + i, s_t), out_f32);
       } else {
         float* dst = ws + blockIdx.y * mn + (int64_t)m * N + nbase;
         if ((N & 3) == 0 && nbase + 3 < N) {
@@ -1259,7 +1260,7 @@ __global__ __launch_bounds__(256) void k_skinny_str(const uint16_t* __restrict__
 
 template <int MT, int IMPL, int NST>
 hipError_t launch_str(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
-                      const uint8_t* scales, const float* ts, void* y, float* ws, int M, int N, int K,
+                      const uint8_t* scales, KScale ts, void* y, float* ws, int M, int N, int K,
                       int out_f32) {
   const size_t lds = (size_t)NST * 4096 * MT;
   hipError_t e = set_lds_limit<k_skinny_str<MT, IMPL, NST>>(lds);
@@ -1269,7 +1270,7 @@ hipError_t launch_str(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x
                      M, N, K, p.str_rows, out_f32);
   e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  return launch_split_reduce(ws, ts, y, (int64_t)M * N, p.splits, out_f32, stream);
+  return split_reduce(ws, ts, y, (int64_t)M * N, N, p.splits, out_f32, stream);
 }
 
 // y = s_t * sum over K chunks (in chunk order) of the fp32 partial sums;
@@ -1278,11 +1279,10 @@ hipError_t launch_str(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x
 // added in plane order.
 constexpr int kRedBatch = 8;
 
-__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
-                                                const float* __restrict__ tensor_scale,
-                                                void* __restrict__ y, int64_t mn, int splits,
+__global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws, const KScale tensor_scale,
+                                                void* __restrict__ y, int64_t mn, int64_t n, int splits,
                                                 int out_f32) {
-  const float s_t = tensor_scale[0];
+  const float s_t = first_scale(tensor_scale);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   if ((mn & 3) == 0) {
     const int64_t mn4 = mn >> 2;
@@ -1304,10 +1304,10 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
           }
         }
       }
-      store_out(y, 4 * i, s.x * s_t, out_f32);
-      store_out(y, 4 * i + 1, s.y * s_t, out_f32);
-      store_out(y, 4 * i + 2, s.z * s_t, out_f32);
-      store_out(y, 4 * i + 3, s.w * s_t, out_f32);
+      store_out(y, 4 * i, s.x * col_scale(tensor_scale, (4 * i) % n, s_t), out_f32);
+      store_out(y, 4 * i + 1, s.y * col_scale(tensor_scale, (4 * i + 1) % n, s_t), out_f32);
+      store_out(y, 4 * i + 2, s.z * col_scale(tensor_scale, (4 * i + 2) % n, s_t), out_f32);
+      store_out(y, 4 * i + 3, s.w * col_scale(tensor_scale, (4 * i + 3) % n, s_t), out_f32);
     }
     return;
   }
@@ -1322,7 +1322,7 @@ __global__ __launch_bounds__(256) void k_reduce(const float* __restrict__ ws,
       for (int b = 0; b < kRedBatch; ++b)
         if (sp + b < splits) s += t[b];
     }
-    store_out(y, i, s * s_t, out_f32);
+    store_out(y, i, s * col_scale(tensor_scale, i % n, s_t), out_f32);
   }
 }
 
@@ -1335,7 +1335,7 @@ size_t pk_lds_bytes(int mr, int w, int rounds, bool dot) {
 
 template <int MR, int IMPL, int ROUNDS>
 hipError_t launch_pk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
-                     const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+                     const uint8_t* scales, KScale ts, void* y, int M, int N, int K, int out_f32) {
   const size_t lds = pk_lds_bytes(MR, p.waves, ROUNDS, pk_dot_path(MR, IMPL));
   hipError_t e = set_lds_limit<k_skinny_pk<MR, IMPL, ROUNDS>>(lds);
   if (e != hipSuccess) return e;
@@ -1365,7 +1365,7 @@ hipError_t launch_pk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
 
 template <int MR, int IMPL>
 hipError_t launch_pk_r(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
-                       const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+                       const uint8_t* scales, KScale ts, void* y, int M, int N, int K, int out_f32) {
   if (p.pk_rounds != 1) return hipErrorInvalidValue;  // the planner takes one slice per wave only
   return launch_pk<MR, IMPL, 1>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
 }
@@ -1374,7 +1374,7 @@ size_t fx_lds_bytes(int mt, int w, int t) { return (size_t)w * mt * (2 * 4096 + 
 
 template <int MT, int IMPL, int NSTEP, int T>
 hipError_t launch_fx(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
-                     const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+                     const uint8_t* scales, KScale ts, void* y, int M, int N, int K, int out_f32) {
   const size_t lds = fx_lds_bytes(MT, p.waves, T);
   hipError_t e = set_lds_limit<k_skinny_fx<MT, IMPL, NSTEP, T>>(lds);
   if (e != hipSuccess) return e;
@@ -1385,7 +1385,7 @@ hipError_t launch_fx(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
 
 template <int MT, int IMPL, int T>
 hipError_t launch_fx_s(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
-                       const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+                       const uint8_t* scales, KScale ts, void* y, int M, int N, int K, int out_f32) {
   switch (p.fx_steps) {
     case 4: return launch_fx<MT, IMPL, 4, T>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
     case 8: return launch_fx<MT, IMPL, 8, T>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
@@ -1395,7 +1395,7 @@ hipError_t launch_fx_s(const SkinnyPlan& p, hipStream_t stream, const uint16_t* 
 
 template <int MT, int IMPL>
 hipError_t launch_fx_n(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
-                       const uint8_t* scales, const float* ts, void* y, int M, int N, int K, int out_f32) {
+                       const uint8_t* scales, KScale ts, void* y, int M, int N, int K, int out_f32) {
   switch (p.fx_tiles) {
     case 1: return launch_fx_s<MT, IMPL, 1>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
     case 2: return launch_fx_s<MT, IMPL, 2>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
@@ -1408,7 +1408,7 @@ hipError_t launch_fx_n(const SkinnyPlan& p, hipStream_t stream, const uint16_t* 
 template <auto Kernel>
 hipError_t launch_fk_kernel(dim3 grid, int waves, size_t lds, hipStream_t stream,
                             const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
-                            const float* ts, void* y, int M, int N, int K, int rounds,
+                            KScale ts, void* y, int M, int N, int K, int rounds,
                             int out_f32) {
   hipError_t e = set_lds_limit<Kernel>(lds);
   if (e != hipSuccess) return e;
@@ -1419,7 +1419,7 @@ hipError_t launch_fk_kernel(dim3 grid, int waves, size_t lds, hipStream_t stream
 
 template <int MR, int IMPL, bool K32>
 hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
-                     const uint8_t* codes, const uint8_t* scales, const float* ts, void* y, int M,
+                     const uint8_t* codes, const uint8_t* scales, KScale ts, void* y, int M,
                      int N, int K, int out_f32) {
   const dim3 grid((unsigned)((N + 15) / 16));
   const size_t lds = (size_t)p.waves * (64 * sizeof(f32x4_t) + (size_t)MR * (kWaveK + 8) * 2);
@@ -1459,7 +1459,7 @@ hipError_t launch_fk(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
 
 template <int MT, int IMPL, int NKS>
 hipError_t launch_pipe(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
-                       const uint8_t* codes, const uint8_t* scales, const float* ts, void* y,
+                       const uint8_t* codes, const uint8_t* scales, KScale ts, void* y,
                        float* ws, int M, int N, int K, int out_f32) {
   const size_t lds = (size_t)NKS * 4 * MT * 1024;
   hipError_t e = set_lds_limit<k_skinny_pipe<MT, IMPL, NKS>>(lds);
@@ -1469,12 +1469,12 @@ hipError_t launch_pipe(const SkinnyPlan& p, hipStream_t stream, const uint16_t* 
                      scales, ts, y, ws, M, N, K, out_f32);
   e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  return launch_split_reduce(ws, ts, y, (int64_t)M * N, p.splits, out_f32, stream);
+  return split_reduce(ws, ts, y, (int64_t)M * N, N, p.splits, out_f32, stream);
 }
 
 template <int MT, int IMPL, bool K32>
 hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
-                     const uint8_t* codes, const uint8_t* scales, const float* ts, void* y,
+                     const uint8_t* codes, const uint8_t* scales, KScale ts, void* y,
                      float* ws, int M, int N, int K, int out_f32) {
   if constexpr (MT == 1) {
     if (p.splits == 0 && p.pk_rounds > 0) {  // persistent full-K kernel
@@ -1529,12 +1529,12 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
                      p.kchunk, p.splits, out_f32);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  return launch_split_reduce(ws, ts, y, (int64_t)M * N, p.splits, out_f32, stream);
+  return split_reduce(ws, ts, y, (int64_t)M * N, N, p.splits, out_f32, stream);
 }
 
 template <int IMPL, bool K32>
 hipError_t launch_impl(int mt, const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
-                       const uint8_t* codes, const uint8_t* scales, const float* ts, void* y,
+                       const uint8_t* codes, const uint8_t* scales, KScale ts, void* y,
                        float* ws, int M, int N, int K, int out_f32) {
   switch (mt) {
     case 1: return launch_mt<1, IMPL, K32>(p, stream, x, codes, scales, ts, y, ws, M, N, K, out_f32);
@@ -1553,13 +1553,18 @@ int max_steps(int mt) {
 
 }  // namespace
 
-hipError_t launch_split_reduce(const float* ws, const float* tensor_scale, void* y, int64_t mn,
+hipError_t launch_split_reduce(const float* ws, RowScale rs, void* y, int64_t mn, int64_t n,
                                int splits, int out_f32, hipStream_t stream) {
+  return split_reduce(ws, kscale(rs), y, mn, n, splits, out_f32, stream);
+}
+
+hipError_t split_reduce(const float* ws, KScale tensor_scale, void* y, int64_t mn, int64_t n, int splits,
+                        int out_f32, hipStream_t stream) {
   const int64_t work = (mn & 3) == 0 ? mn / 4 : mn;  // outputs per thread: 4 or 1
   int64_t blocks = (work + 255) / 256;
   if (blocks > 2048) blocks = 2048;
   hipLaunchKernelGGL(k_reduce, dim3((unsigned)blocks), dim3(256), 0, stream, ws, tensor_scale, y,
-                     mn, splits, out_f32);
+                     mn, n > 0 ? n : 1, splits, out_f32);
   return hipGetLastError();
 }
 
@@ -1752,9 +1757,10 @@ SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits) 
 }
 
 hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* scales,
-                         const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                         RowScale rs, void* y, int64_t m, int64_t n, int64_t k,
                          int out_f32, const SkinnyPlan& plan, void* workspace, int impl,
                          hipStream_t stream) {
+  const KScale tensor_scale = kscale(rs);
   const int mt = (int)((m + 15) / 16);
   const bool k32 = (k % 32) == 0;
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
@@ -1767,4 +1773,5 @@ hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* sca
              : launch_impl<kConvPortable, false>(mt, plan, stream, xp, codes, scales, tensor_scale, y, ws, M, N, K, out_f32);
 }
 
+NVFP4_VARIANT_END
 }  // namespace nvfp4

@@ -27,6 +27,7 @@
 #include "nvfp4_device.h"
 
 namespace nvfp4 {
+NVFP4_VARIANT_BEGIN
 namespace {
 
 
@@ -47,7 +48,7 @@ template <int IMPL, bool K32>
 __global__ __launch_bounds__(256) void k_tiled(const uint16_t* __restrict__ x,
                                                const uint8_t* __restrict__ codes,
                                                const uint8_t* __restrict__ scales,
-                                               const float* __restrict__ tensor_scale,
+                                               const KScale tensor_scale,
                                                void* __restrict__ y, int M, int N, int K,
                                                int out_f32) {
   __shared__ __attribute__((aligned(16))) uint8_t sA[kFragBytes];
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256) void k_tiled(const uint16_t* __restrict__ x,
   }
 
   // epilogue: acc[a][b] lane holds D[n = 16(4wn+a) + 4g + i][m = 16(4wm+b) + r16]
-  const float s_t = tensor_scale[0];
+  const float s_t0 = first_scale(tensor_scale);
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int m = m0 + 16 * (4 * wm + b) + r16;
@@ -161,6 +162,7 @@ __global__ __launch_bounds__(256) void k_tiled(const uint16_t* __restrict__ x,
       for (int i = 0; i < 4; ++i) {
         const int n = n0 + 16 * (4 * wn + a) + 4 * g + i;
         if (n >= N) continue;
+        const float s_t = col_scale(tensor_scale, n, s_t0);
         const int64_t idx = (int64_t)m * N + n;
         if (out_f32)
           reinterpret_cast<float*>(y)[idx] = acc[a][b][i] * s_t;
@@ -184,7 +186,7 @@ template <int BN, int BM, int WGN, int WGM, int IMPL>
 __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restrict__ x,
                                                        const uint8_t* __restrict__ codes,
                                                        const uint8_t* __restrict__ scales,
-                                                       const float* __restrict__ tensor_scale,
+                                                       const KScale tensor_scale,
                                                        void* __restrict__ y, float* __restrict__ ws,
                                                        int M, int N, int K, int steps_per,
                                                        int out_f32) {
@@ -312,7 +314,7 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
   // + v % 4, token l % 32.  With a K split: raw fp32 partials to plane z.
   const bool partial = gridDim.z > 1;
   float* plane = ws + (int64_t)blockIdx.z * M * N;
-  const float s_t = partial ? 1.0f : tensor_scale[0];
+  const float s_t0 = first_scale(tensor_scale);
 #pragma unroll
   for (int b = 0; b < WMT; ++b) {
     const int m = m0 + 32 * (WMT * wm + b) + r32;
@@ -322,6 +324,7 @@ __global__ __launch_bounds__(64 * WGN * WGM) void k_lm(const uint16_t* __restric
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + 32 * (WNT * wn + a) + 8 * q + 4 * h;
+        const float s_t = partial ? 1.0f : col_scale(tensor_scale, n, s_t0);  // n .. n + 3: one group
         const float v0 = acc[a][b][4 * q] * s_t, v1 = acc[a][b][4 * q + 1] * s_t;
         const float v2 = acc[a][b][4 * q + 2] * s_t, v3 = acc[a][b][4 * q + 3] * s_t;
         const int64_t idx = (int64_t)m * N + n;
@@ -386,7 +389,7 @@ template <int BM, int IMPL>
 __global__ __launch_bounds__(256, 2) void k_lmr(const uint16_t* __restrict__ x,
                                              const uint8_t* __restrict__ codes,
                                              const uint8_t* __restrict__ scales,
-                                             const float* __restrict__ tensor_scale,
+                                             const KScale tensor_scale,
                                              void* __restrict__ y, float* __restrict__ ws, int M,
                                              int N, int K, int steps_per, int out_f32) {
   constexpr int MTILES = BM / 32;  // 32-token MFMA B tiles
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(256, 2) void k_lmr(const uint16_t* __restrict__ x,
   // + v % 4, token l % 32.  With a K split: raw fp32 partials to plane z.
   const bool partial = gridDim.z > 1;
   float* plane = ws + (int64_t)blockIdx.z * M * N;
-  const float s_t = partial ? 1.0f : tensor_scale[0];
+  const float s_t0 = first_scale(tensor_scale);
 #pragma unroll
   for (int b = 0; b < MTILES; ++b) {
     const int m = m0 + 32 * b + r32;
@@ -505,6 +508,7 @@ __global__ __launch_bounds__(256, 2) void k_lmr(const uint16_t* __restrict__ x,
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int n = n0 + 64 * wave + 32 * a + 8 * q + 4 * h;
+        const float s_t = partial ? 1.0f : col_scale(tensor_scale, n, s_t0);  // n .. n + 3: one group
         const float v0 = acc[a][b][4 * q] * s_t, v1 = acc[a][b][4 * q + 1] * s_t;
         const float v2 = acc[a][b][4 * q + 2] * s_t, v3 = acc[a][b][4 * q + 3] * s_t;
         const int64_t idx = (int64_t)m * N + n;
@@ -544,7 +548,7 @@ __global__ __launch_bounds__(256, 2) void k_lmr(const uint16_t* __restrict__ x,
 
 template <int BM, int IMPL>
 hipError_t launch_lmr(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
-                      const float* ts, void* y, float* ws, int M, int N, int K, int splits,
+                      KScale ts, void* y, float* ws, int M, int N, int K, int splits,
                       int steps_per, int out_f32, hipStream_t stream) {
   constexpr size_t lds = 2 * (size_t)BM * 128;
   hipError_t e = set_lds_limit<k_lmr<BM, IMPL>>(lds);
@@ -554,12 +558,12 @@ hipError_t launch_lmr(const uint16_t* x, const uint8_t* codes, const uint8_t* sc
                      M, N, K, steps_per, out_f32);
   e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  return launch_split_reduce(ws, ts, y, (int64_t)M * N, splits, out_f32, stream);
+  return split_reduce(ws, ts, y, (int64_t)M * N, N, splits, out_f32, stream);
 }
 
 template <int BN, int BM, int WGN, int WGM, int IMPL>
 hipError_t launch_lm(const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
-                     const float* ts, void* y, float* ws, int M, int N, int K, int splits,
+                     KScale ts, void* y, float* ws, int M, int N, int K, int splits,
                      int steps_per, int out_f32, hipStream_t stream) {
   constexpr size_t lds = 2 * (4 * (BN / 32) * 1024 + 4 * (BM / 32) * 1024);
   hipError_t e = set_lds_limit<k_lm<BN, BM, WGN, WGM, IMPL>>(lds);
@@ -569,12 +573,12 @@ hipError_t launch_lm(const uint16_t* x, const uint8_t* codes, const uint8_t* sca
                      codes, scales, ts, y, ws, M, N, K, steps_per, out_f32);
   e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
-  return launch_split_reduce(ws, ts, y, (int64_t)M * N, splits, out_f32, stream);
+  return split_reduce(ws, ts, y, (int64_t)M * N, N, splits, out_f32, stream);
 }
 
 template <int IMPL>
 hipError_t launch_lm_plan(const TiledPlan& p, const uint16_t* x, const uint8_t* codes,
-                          const uint8_t* scales, const float* ts, void* y, float* ws, int M, int N,
+                          const uint8_t* scales, KScale ts, void* y, float* ws, int M, int N,
                           int K, int out_f32, hipStream_t stream) {
   switch (p.kernel) {
     case 3:
@@ -645,9 +649,10 @@ TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k, int forced_splits) {
 }
 
 hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scales,
-                        const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                        RowScale rs, void* y, int64_t m, int64_t n, int64_t k,
                         int out_f32, const TiledPlan& plan, void* workspace, int impl,
                         hipStream_t stream) {
+  const KScale tensor_scale = kscale(rs);
   const uint16_t* xp = reinterpret_cast<const uint16_t*>(x);
   float* ws = reinterpret_cast<float*>(workspace);
   const int M = (int)m, N = (int)n, K = (int)k;
@@ -668,4 +673,5 @@ hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scal
   return hipGetLastError();
 }
 
+NVFP4_VARIANT_END
 }  // namespace nvfp4

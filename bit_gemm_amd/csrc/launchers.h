@@ -8,6 +8,52 @@
 
 namespace nvfp4 {
 
+// The fp32 tensor scale of every output column (weight row) of a GEMM: one
+// scale, or one per group of stacked weight matrices (rows [0, b1), [b1, b2),
+// [b2, b3), [b3, n); a boundary of INT32_MAX is absent).  Boundaries are
+// multiples of 16.  The GEMM sources are compiled twice: once for one scale
+// per call (the kernels read ts[0] as always), once with NVFP4_GROUPED set
+// into namespace nvfp4::grouped, whose epilogues read each column's scale.
+struct RowScale {
+  const float* ts;
+  int b1, b2, b3;
+  __host__ __device__ static RowScale one(const float* t) { return RowScale{t, INT32_MAX, INT32_MAX, INT32_MAX}; }
+};
+
+#ifndef NVFP4_GROUPED
+#define NVFP4_GROUPED 0
+#endif
+#if NVFP4_GROUPED
+#define NVFP4_VARIANT_BEGIN namespace grouped {
+#define NVFP4_VARIANT_END }
+#else
+#define NVFP4_VARIANT_BEGIN
+#define NVFP4_VARIANT_END
+#endif
+
+NVFP4_VARIANT_BEGIN
+// What the kernels take: the plain build the tensor scale pointer (exactly
+// as before groups existed), the grouped build the whole RowScale.
+#if NVFP4_GROUPED
+typedef RowScale KScale;
+inline KScale kscale(const RowScale& r) { return r; }
+__device__ __forceinline__ float first_scale(const RowScale& r) { return r.ts[0]; }
+// The scale of output column col.
+__device__ __forceinline__ float col_scale(const RowScale& rs, int64_t col, float) {
+  return rs.ts[(col >= rs.b1) + (col >= rs.b2) + (col >= rs.b3)];
+}
+#else
+typedef const float* __restrict__ KScale;
+inline const float* kscale(const RowScale& r) { return r.ts; }
+__device__ __forceinline__ float first_scale(const float* t) { return t[0]; }
+__device__ __forceinline__ float col_scale(const float*, int64_t, float s0) { return s0; }
+#endif
+// The split-K reduction as the GEMM launchers call it (launch_split_reduce
+// for callers outside them).
+hipError_t split_reduce(const float* ws, KScale ts, void* y, int64_t mn, int64_t n, int splits, int out_f32,
+                        hipStream_t stream);
+NVFP4_VARIANT_END
+
 // Conversion implementations (see NVFP4_IMPL_* in nvfp4.h).
 enum ConvImpl { kConvPortable = 1, kConvHw = 2 };
 
@@ -39,13 +85,13 @@ struct SkinnyPlan {
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits);
 hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* scales,
-                         const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                         RowScale tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
                          int out_f32, const SkinnyPlan& plan, void* workspace, int impl,
                          hipStream_t stream);
 
 // y = s_t * (sum of `splits` fp32 planes [splits, mn] in plane order),
-// rounded to the output type.
-hipError_t launch_split_reduce(const float* ws, const float* tensor_scale, void* y, int64_t mn,
+// rounded to the output type; n = columns of y (for per-column scales).
+hipError_t launch_split_reduce(const float* ws, RowScale tensor_scale, void* y, int64_t mn, int64_t n,
                                int splits, int out_f32, hipStream_t stream);
 
 // Tiled bf16-MFMA path (any m).  kernel: 0 = 128 x 128 single-stage kernel
@@ -62,9 +108,22 @@ struct TiledPlan {
 };
 TiledPlan plan_tiled(int64_t m, int64_t n, int64_t k, int forced_splits);
 hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scales,
-                        const float* tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
+                        RowScale tensor_scale, void* y, int64_t m, int64_t n, int64_t k,
                         int out_f32, const TiledPlan& plan, void* workspace, int impl,
                         hipStream_t stream);
+
+// The same three entry points for stacked matrices with one scale per group
+// (the sources compiled with NVFP4_GROUPED).
+namespace grouped {
+hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* scales, RowScale tensor_scale, void* y,
+                         int64_t m, int64_t n, int64_t k, int out_f32, const SkinnyPlan& plan, void* workspace,
+                         int impl, hipStream_t stream);
+hipError_t launch_split_reduce(const float* ws, RowScale tensor_scale, void* y, int64_t mn, int64_t n, int splits,
+                               int out_f32, hipStream_t stream);
+hipError_t launch_tiled(const void* x, const uint8_t* codes, const uint8_t* scales, RowScale tensor_scale, void* y,
+                        int64_t m, int64_t n, int64_t k, int out_f32, const TiledPlan& plan, void* workspace,
+                        int impl, hipStream_t stream);
+}  // namespace grouped
 
 // dx[m, k] = s_t * sum_n dy[m, n] * (val * sigma)[n, k] (bf16 dy, packed W):
 // 128 x 128 output tiles, the reduction split over `splits` workgroups of

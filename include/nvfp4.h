@@ -268,6 +268,30 @@ NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_
                                int out_dtype, void* workspace, size_t workspace_bytes,
                                void* stream);
 
+/*
+ * nvfp4_w4a16_gemm_grouped - the W4A16 GEMMs of G weight matrices that read
+ * the same activations (a decoder layer's q, k and v projections, or gate
+ * and up: [Recap] section 1's W4A16 kernel, decode being bound by reading
+ * every weight once per token, [Notes08] section 01), in one call.
+ *
+ * The G packed matrices are stacked row-wise: codes [n_total, k/2] and
+ * scales [n_total, k/16] hold group 0's rows, then group 1's, ... (each
+ * quantized on its own: nvfp4_quantize_fos can write straight into a row
+ * block of the stacked buffers); tensor_scales is a device fp32 [G] array,
+ * group g's s_t; group_rows a host int64 [G] array of row counts, each a
+ * positive multiple of 16, n_total their sum (< 2^27).  y [m, n_total] of
+ * out_dtype: columns of group g hold x . W_hat_g^T with s_t[g] (the fused
+ * output of the stacked projections; group g's result is the column block
+ * starting at the sum of the earlier groups' rows).  G in 1 .. 4.
+ * Everything else as nvfp4_w4a16_gemm on (m, n_total, k), including the
+ * dispatch and the workspace: nvfp4_w4a16_gemm_workspace_size(m, n_total,
+ * k) bytes.  One launch (or two with a K split) instead of G.
+ */
+NVFP4_API int nvfp4_w4a16_gemm_grouped(const void* x, const uint8_t* codes, const uint8_t* scales,
+                                       const float* tensor_scales, const int64_t* group_rows, int groups,
+                                       void* y, int64_t m, int64_t k, int out_dtype, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
 /* Same, with an explicit path (NVFP4_PATH_*), a split-K factor
  * (0 = automatic; skinny path: >= 1 = the split-K kernel with that many K
  * chunks, clamped to [1, 64], more when a chunk would not fit in registers

@@ -28,8 +28,37 @@ def test_checker_flags_early_reads():
     assert check_kernel(lines) == []
 
 
-@pytest.mark.skipif(not os.path.exists("/opt/rocm/bin/hipcc") and not os.environ.get("HIPCC"),
-                    reason="hipcc not available")
+_HAVE_HIPCC = os.path.exists("/opt/rocm/bin/hipcc") or bool(os.environ.get("HIPCC"))
+# (source, extra defines): the GEMM sources are also built with one tensor
+# scale per group of stacked matrices (NVFP4_GROUPED), whose epilogues read
+# each column's scale; both builds are checked
+_BUILDS = [("gemm_skinny.hip", ()), ("gemm_skinny.hip", ("-DNVFP4_GROUPED=1",)),
+           ("gemm_tiled.hip", ()), ("gemm_tiled.hip", ("-DNVFP4_GROUPED=1",))]
+_ASM = {}
+
+
+@pytest.fixture(scope="module")
+def device_asm(tmp_path_factory):
+    """Device assembly of every build above, compiled once and in parallel."""
+    if not _ASM:
+        d = tmp_path_factory.mktemp("asm")
+        flags = [f for f in build.COMMON if f != "-fPIC"]
+        procs = []
+        for i, (source, defs) in enumerate(_BUILDS):
+            out = d / f"{i}.s"
+            cmd = [build.hipcc(), *flags, *defs, "-x", "hip", "--offload-device-only", "-S",
+                   os.path.join(build.CSRC, source), "-o", str(out)]
+            procs.append(((source, defs), out, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE,
+                                                                 text=True)))
+        for key, out, pr in procs:
+            _, err = pr.communicate()
+            assert pr.returncode == 0, err[-2000:]
+            _ASM[key] = out.read_text()
+    return _ASM
+
+
+@pytest.mark.skipif(not _HAVE_HIPCC, reason="hipcc not available")
+@pytest.mark.parametrize("grouped", [False, True], ids=["one_scale", "grouped"])
 @pytest.mark.parametrize("source,pattern,minimum", [
     ("gemm_skinny.hip", r"k_skinny_pipe", 20),  # MT 1..4 x chunk lengths x 2 conversion implementations
     ("gemm_skinny.hip", r"k_skinny_str", 16),    # streaming kernel: MT 1..4 x chunk lengths x 2 conversion implementations
@@ -37,13 +66,8 @@ def test_checker_flags_early_reads():
     ("gemm_skinny.hip", r"k_skinny_fx", 48),     # single-launch full-K kernel: MT 2..4 x 4 or 8 steps x 1..4 tiles x 2 implementations
     ("gemm_tiled.hip", r"k_lmr", 2),             # weights-in-registers large-M kernel, 2 implementations
 ])
-def test_counted_waits_cover_every_use(tmp_path, source, pattern, minimum):
-    src = os.path.join(build.CSRC, source)
-    out = tmp_path / (source + ".s")
-    flags = [f for f in build.COMMON if f != "-fPIC"]
-    cmd = [build.hipcc(), *flags, "-x", "hip", "--offload-device-only", "-S", src, "-o", str(out)]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    assert r.returncode == 0, r.stderr[-2000:]
-    found, bad = check_assembly(out.read_text(), pattern)
+def test_counted_waits_cover_every_use(device_asm, source, pattern, minimum, grouped):
+    text = device_asm[(source, ("-DNVFP4_GROUPED=1",) if grouped else ())]
+    found, bad = check_assembly(text, pattern)
     assert found >= minimum, found
     assert bad == [], bad[:10]

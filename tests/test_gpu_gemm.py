@@ -326,3 +326,70 @@ def test_workspace_reuse_across_shapes():
         torch.cuda.synchronize()
         ref = oracle.gemm_ref(x, r.codes, r.scales, r.tensor_scale)
         assert _rel(y, ref) <= 1e-5, (m, n, k, split)
+
+
+# ---------------------------------------------------------------------------
+# nvfp4_w4a16_gemm_grouped: G matrices stacked row-wise, one tensor scale per
+# group, one call.  Each group's column block of y against the oracle of that
+# matrix alone (its own quantization and tensor scale), through every route
+# the stacked shape dispatches to (full-K, persistent, single-launch with
+# 1-4 tiles per workgroup, streaming split-K + reduction, tiled).
+# ---------------------------------------------------------------------------
+GROUPED_CASES = [
+    # (group rows, k, token counts)
+    ((48, 1024, 16), 512, (1, 5, 17, 40, 100)),
+    ((4096, 4096, 4096), 4096, (1, 8, 17, 48)),  # q, k, v of the decoder layer
+    ((14336, 14336), 4096, (1, 48)),             # gate, up
+    ((256, 512), 1040, (3, 24, 200)),            # k % 512 != 0: split-K skinny and single-stage tiled
+]
+
+
+@pytest.mark.parametrize("rows,k,ms", GROUPED_CASES, ids=lambda v: str(v))
+def test_grouped_gemm(rows, k, ms):
+    ws = [synth.student_t_weights(n, k, 2000 + 7 * i + n % 97) for i, n in enumerate(rows)]
+    gq = nv.quantize_fos_grouped([torch.from_numpy(w).cuda() for w in ws])
+    refs = [oracle.quantize_fos(w) for w in ws]
+    torch.cuda.synchronize()
+    off = 0
+    for g, (r, n) in enumerate(zip(refs, rows)):
+        q = gq.group(g)
+        assert np.array_equal(q.codes.cpu().numpy(), r.codes) and np.array_equal(q.scales.cpu().numpy(), r.scales)
+        assert q.tensor_scale.cpu().numpy()[0].view(np.uint32) == np.float32(r.tensor_scale).view(np.uint32)
+    w_hats = [oracle.dequant_f64(r.codes, r.scales, r.tensor_scale) for r in refs]
+    for m in ms:
+        print("grouped", rows, k, "m", m, flush=True)
+        x = synth.activations(m, k, 2100 + m)
+        xd = x.cuda()
+        xv = np.asarray(x.float().numpy(), dtype=np.float64)
+        for dt in (torch.bfloat16, torch.float32):
+            y = nv.w4a16_gemm_grouped(xd, gq, out_dtype=dt)
+            torch.cuda.synchronize()
+            yd = y.double().cpu().numpy()
+            off = 0
+            for g, n in enumerate(rows):
+                ref = xv @ w_hats[g].T
+                blk = yd[:, off:off + n]
+                e = _rel(blk, ref)
+                assert e <= _tol(dt, ref), (rows, k, m, g, dt, e)
+                assert_gemm_elementwise(blk, x, w_hats[g], ref, dt, f"grouped {rows} g={g} m={m} {dt}")
+                off += n
+
+
+def test_grouped_gemm_errors():
+    lib = nv.lib()
+    x = torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda")
+    codes = torch.zeros((48, 32), dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((48, 4), dtype=torch.uint8, device="cuda")
+    ts = torch.ones(3, dtype=torch.float32, device="cuda")
+    y = torch.zeros((4, 48), dtype=torch.bfloat16, device="cuda")
+    import ctypes
+
+    def call(rows, groups):
+        arr = (ctypes.c_int64 * max(1, len(rows)))(*rows)
+        return lib.nvfp4_w4a16_gemm_grouped(x.data_ptr(), codes.data_ptr(), scales.data_ptr(), ts.data_ptr(),
+                                            ctypes.cast(arr, ctypes.c_void_p), groups, y.data_ptr(), 4, 64, nv.BF16,
+                                            None, 0, None)
+    assert call([16, 16, 16], 3) == nv.NVFP4_OK
+    assert call([16, 16, 16, 16, 16], 5) == 1
+    assert call([16, 24, 8], 3) == 2  # not multiples of 16
+    assert call([], 0) == 1

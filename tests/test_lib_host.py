@@ -377,3 +377,16 @@ def test_hessian_host_validation(L):
     assert L.nvfp4_gptq_hessian(16, 4, 65537, 0.01, 64, None, 0, None) == 2
     assert L.nvfp4_gptq_hessian(17, 4, 16, 0.01, 64, 1024, 1 << 20, None) == 3  # x not 2-byte aligned
     assert L.nvfp4_gptq_hessian(None, 4, 16, 0.01, 64, 1024, 1 << 20, None) == 1  # x required for s > 0
+
+
+def test_grouped_gemm_host_validation(L):
+    import ctypes
+
+    def call(rows, groups):
+        arr = (ctypes.c_int64 * max(1, len(rows)))(*rows)
+        return L.nvfp4_w4a16_gemm_grouped(16, 16, 16, 16, ctypes.cast(arr, ctypes.c_void_p), groups, 16, 4, 64,
+                                          nv.BF16, None, 0, None)
+    assert call([16, 16], 0) == 1 and call([16] * 5, 5) == 1
+    assert call([16, 24], 2) == 2 and call([0, 16], 2) == 2 and call([-16], 1) == 2
+    assert call([1 << 26, 1 << 26], 2) == 2  # 2^27 rows
+    assert L.nvfp4_w4a16_gemm_grouped(16, 16, 16, 16, None, 1, 16, 4, 64, nv.BF16, None, 0, None) == 1
