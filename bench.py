@@ -74,9 +74,9 @@ def parse_args(argv=None):
     ap.add_argument("--no-cpu-configs", action="store_true",
                     help="skip the oracle on the MLP set and the large-M shapes (per-matrix M=4 share, "
                          "GPU == oracle)")
-    ap.add_argument("--cpu-full", action="store_true",
-                    help="also run the oracle on layers 0 and 31 of the 32-layer decoder in full (adds "
-                         "about a minute of host work)")
+    ap.add_argument("--no-cpu-full", action="store_true",
+                    help="skip the oracle on layers 0 and 31 of the 32-layer decoder in full (about 20 s "
+                         "of host work)")
     ap.add_argument("--eager", action="store_true",
                     help="launch the steps directly instead of from HIP graphs (for counter "
                          "collection); prints the step time only")
@@ -919,7 +919,7 @@ def cpu_baseline(args, w_host, xs_dev, q_dev):
     Also the quantizer, the MLP set (whole matrices: quantization time and
     the M=4 share, GPU == oracle bit for bit), the large-M shapes on a row
     sample, and the 32-layer decoder extrapolated from those rates (or run
-    on layers 0 and 31 with --cpu-full).  The oracle is a reported baseline,
+    on layers 0 and 31 of the decoder in full).  The oracle is a reported baseline,
     not the optimisation target."""
     from concurrent.futures import ThreadPoolExecutor
 
@@ -1000,6 +1000,7 @@ def cpu_baseline(args, w_host, xs_dev, q_dev):
         rates = {"gemm_gbs": {}, "quant_wps": []}
         if not args.no_cpu_configs:
             configs = cpu_configs(args, ex, quant_all, gemm_all, rates, q_dev.codes.device)
+        layers_measured = cpu_decoder_layers(args, quant_all, gemm_all, q_dev.codes.device) if not args.no_cpu_full else None
     torch.set_num_threads(torch_threads)
 
     gemm_rate_all = len(xs) * wbytes * repsA / dtA / 1e9
@@ -1017,8 +1018,8 @@ def cpu_baseline(args, w_host, xs_dev, q_dev):
         g = rates["gemm_gbs"].get(m)
         if g:
             model[f"gemm_pass_m{m}_s_extrapolated"] = round(packed_bytes / (g * 1e9), 2)
-    if args.cpu_full:
-        model["layers_0_31_measured"] = cpu_decoder_layers(args, quant_all, q_dev.codes.device)
+    if layers_measured is not None:
+        model["layers_0_31_measured"] = layers_measured
 
     cpu = {"value": round(gemm_rate_all, 4), "unit": "GB/s", "cores": ncores, "kind": "oracle",
            "sample": f"{repsA} passes of the five float64 reference GEMMs (M = 1, 8, 16, 32, 48) on the "
@@ -1111,10 +1112,14 @@ def cpu_configs(args, ex, quant_all, gemm_all, rates, dev):
     return out
 
 
-def cpu_decoder_layers(args, quant_all, dev):
+def cpu_decoder_layers(args, quant_all, gemm_all, dev):
     """Layers 0 and 31 of the 32-layer decoder in full: each matrix drawn at
     its seed, quantized by the oracle on all cores and by the GPU, compared
-    bit for bit, with its M=4 share."""
+    bit for bit, with its M=4 share; then the oracle's float64 GEMM of the
+    whole matrix at M = 1 and 48 (dequantization on row chunks in the thread
+    pool, BLAS on all cores).  The 32-layer figures
+    are these two layers' times x 16 (every layer has the same shapes and
+    draws from the same distribution)."""
     import numpy as np
     import torch
 
@@ -1122,21 +1127,36 @@ def cpu_decoder_layers(args, quant_all, dev):
     import synth
 
     res = {}
-    t_all = 0.0
+    t_q = 0.0
+    t_g = {1: 0.0, 48: 0.0}
+    xs = {}
     for layer in (0, 31):
         for j, (name, n, k) in enumerate(synth.decoder_layer_shapes()):
             w = synth.student_t_weights(n, k, synth.decoder_weight_seed(layer, j))
             t0 = time.perf_counter()
-            codes, scales, mask, _ = quant_all(w)
+            codes, scales, mask, s_t = quant_all(w)
             dt = time.perf_counter() - t0
-            t_all += dt
+            t_q += dt
             g = nv.quantize_fos(torch.from_numpy(w).to(dev))
             same = bool(np.array_equal(g.codes.cpu().numpy(), codes) and np.array_equal(g.scales.cpu().numpy(), scales)
                         and np.array_equal(g.m4_mask.cpu().numpy(), mask))
-            res[f"layer{layer}_{name}"] = {"quantize_s": round(dt, 2), "m4_share": round(float(mask.mean()), 4),
-                                           "gpu_equals_oracle": same}
+            entry = {"quantize_s": round(dt, 2), "m4_share": round(float(mask.mean()), 4), "gpu_equals_oracle": same}
             del w, g
-    res["quantize_s_total"] = round(t_all, 2)
+            for m in (1, 48):
+                if (m, k) not in xs:
+                    xs[(m, k)] = synth.activations(m, k, synth.activation_seed(m))
+                t0 = time.perf_counter()
+                gemm_all(xs[(m, k)], codes, scales, s_t)
+                dg = time.perf_counter() - t0
+                t_g[m] += dg
+                entry[f"gemm_m{m}_s"] = round(dg, 3)
+            res[f"layer{layer}_{name}"] = entry
+    res["quantize_s_two_layers"] = round(t_q, 2)
+    res["quantize_s_32_layers_extrapolated"] = round(16 * t_q, 1)
+    for m in (1, 48):
+        res[f"gemm_pass_m{m}_s_two_layers"] = round(t_g[m], 2)
+        res[f"gemm_pass_m{m}_s_32_layers_extrapolated"] = round(16 * t_g[m], 1)
+    res["extrapolation"] = "32 layers = 16 x (layers 0 and 31): same shapes and weight distribution in every layer"
     return res
 
 
