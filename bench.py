@@ -666,8 +666,10 @@ def profile_large_m(w_dev):
     """A short, eager run of the large-M configurations for counter
     collection (rocprofv3 --kernel-trace / --pmc): for each shape in
     LARGE_SHAPES and M in PROFILE_M, one warm-up and three launches of the
-    automatic-path GEMM on the current stream, in this fixed order (so
-    dispatches map to configurations by their order)."""
+    automatic-path GEMM on the current stream, then the same for the QAT
+    input gradient and for torch's dense bf16 GEMM (for comparison) at the
+    largest M, in this fixed order (so dispatches map to configurations by
+    their order)."""
     import torch
 
     import bit_gemm_amd as nv
@@ -689,6 +691,26 @@ def profile_large_m(w_dev):
             runs.append({"shape": f"{name}_n{n}_k{k}", "m": m, "launches": 4, "flops": 2 * m * n * k,
                          "path": "skinny" if nv.gemm_path(m, n, k) == nv.PATH_SKINNY else "tiled",
                          "workspace_bytes": nv.workspace_size(m, n, k)})
+        # the QAT input gradient dx = dy @ W_hat on the same packed weights, M = 4096
+        m = PROFILE_M[-1]
+        dy = synth.activations(m, n, synth.activation_seed(m) + 1).to(dev)
+        dx = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(16, nv.gemm_dx_workspace_size(m, n, k)), dtype=torch.uint8, device=dev)
+        for _ in range(4):
+            nv.w4a16_gemm_dx(dy, q, out=dx, workspace=ws)
+        torch.cuda.synchronize()
+        runs.append({"shape": f"{name}_n{n}_k{k}", "m": m, "launches": 4, "flops": 2 * m * n * k, "path": "dx",
+                     "workspace_bytes": nv.gemm_dx_workspace_size(m, n, k)})
+        # context, not part of the library: torch's dense bf16 GEMM (hipBLASLt)
+        # of the same shape, no dequantization - the matrix-core rate a plain
+        # bf16 product reaches on this GPU
+        a = synth.activations(m, k, synth.activation_seed(m)).to(dev)
+        b = torch.randn((k, n), dtype=torch.bfloat16, device=dev)
+        for _ in range(4):
+            torch.matmul(a, b)
+        torch.cuda.synchronize()
+        runs.append({"shape": f"{name}_n{n}_k{k}", "m": m, "launches": 4, "flops": 2 * m * n * k, "path": "blas",
+                     "workspace_bytes": 0})
     return runs
 
 

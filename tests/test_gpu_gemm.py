@@ -293,10 +293,13 @@ def test_large_m_kernel_configs(impl):
 
 
 @pytest.mark.parametrize("split", [0, 1, 2, 3, 7, 16])
-def test_tiled_split_k(split):
+@pytest.mark.parametrize("k", [1024, 960])
+def test_tiled_split_k(split, k):
     """K split over workgroups on the tiled path (fp32 partials + in-order
-    reduction); 0 = the automatic plan."""
-    m, n, k = 200, 520, 1024
+    reduction); 0 = the automatic plan.  k = 1024 runs the large-M kernel
+    with 128 k per barrier (splits rounded to whole 128-k steps: 3 -> 6 + 6
+    + 4 steps of 64, 7 -> 4 splits of 4), k = 960 the one with 64 k."""
+    m, n = 200, 520
     w = synth.student_t_weights(n, k, seed=1000)
     q, r = _quant(w)
     x = synth.activations(m, k, seed=1001)
@@ -304,7 +307,7 @@ def test_tiled_split_k(split):
     for dt in (torch.bfloat16, torch.float32):
         y = nv.w4a16_gemm(x.cuda(), q, out_dtype=dt, path=nv.PATH_TILED, split_k=split)
         torch.cuda.synchronize()
-        assert _rel(y, ref) <= TOL[dt], (split, dt)
+        assert _rel(y, ref) <= TOL[dt], (split, k, dt)
 
 
 def test_workspace_reuse_across_shapes():

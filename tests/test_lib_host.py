@@ -240,6 +240,10 @@ def test_dispatch_and_workspace_plan(L):
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(64, 4096, 4112, T, 0) == 0
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(256, 4096, 4096, T, 3) == 3 * 4 * 256 * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 5) == 2 * 4 * 100 * 256
+    # k % 128 == 0 (128 k per barrier): splits in whole 128-k steps, 16 steps
+    # of 64 in 7 -> 4 splits of 4; k % 128 == 64 keeps 64-k steps: 15 in 7 -> 5 of 3
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(200, 520, 1024, T, 7) == 4 * 4 * 200 * 520
+    assert L.nvfp4_w4a16_gemm_workspace_size_ex(200, 520, 960, T, 7) == 5 * 4 * 200 * 520
     assert L.nvfp4_w4a16_gemm_workspace_size_ex(100, 256, 128, T, 1) == 0
     for m in (1, 8, 16):  # the full-K skinny kernels need no workspace
         for (n, k) in ((4096, 4096), (14336, 4096), (4096, 14336), (17, 48)):
