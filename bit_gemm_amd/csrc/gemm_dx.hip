@@ -19,6 +19,8 @@
 // and issue step s + 2's global loads, one barrier per step.  When the tiles
 // are few the reduction over n is split over workgroups (fp32 partials, then
 // the split reduction).  fp32 accumulation; s_t applied once.
+// Where n % 64 == 0 and k % 128 == 0, k_gemm_dx_tr replaces the transposed
+// stores with transposing LDS reads and brings dy in by LDS DMA (below).
 #include "launchers.h"
 #include "nvfp4_device.h"
 
@@ -40,6 +42,39 @@ struct DxLoads {
   uint2 code[2];     // 16 codes of weight rows 2p and 2p+1, one block
   uint32_t sc[2];    // their scale bytes
 };
+
+// Epilogue: a wave's 2 x 2 tiles of 32 x 32, rows mw .. +64, columns kw .. +64.
+// D of a 32 x 32 tile: lane l, value v -> dy row 8 (v / 4) + 4 (l / 32) + v % 4,
+// weight column l % 32.  With a split reduction: raw fp32 partials to plane
+// z of the workspace (the reduction kernel applies s_t).
+__device__ __forceinline__ void store_dx(const f32x16_t (&acc)[2][2], const float* tensor_scale, void* dx, float* ws,
+                                         int M, int K, int mw, int kw, int out_f32) {
+  const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
+  const bool partial = gridDim.z > 1;
+  float* plane = ws + (int64_t)blockIdx.z * M * K;
+  const float s_t = partial ? 1.0f : tensor_scale[0];
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int k = kw + 32 * b + r32;
+      if (k >= K) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = mw + 32 * a + 8 * (v / 4) + 4 * h + (v % 4);
+        if (m >= M) continue;
+        const float o = acc[a][b][v] * s_t;
+        const int64_t idx = (int64_t)m * K + k;
+        if (partial)
+          plane[idx] = o;
+        else if (out_f32)
+          reinterpret_cast<float*>(dx)[idx] = o;
+        else
+          reinterpret_cast<uint16_t*>(dx)[idx] = (uint16_t)bf16_rne_bits(o);
+      }
+    }
+  }
+}
 
 __global__ __launch_bounds__(256) void k_gemm_dx(const uint16_t* __restrict__ dy,
                                                  const uint8_t* __restrict__ codes,
@@ -158,33 +193,148 @@ __global__ __launch_bounds__(256) void k_gemm_dx(const uint16_t* __restrict__ dy
     __syncthreads();
   }
 
-  // D of a 32 x 32 tile: lane l, value v -> dy row 8 (v / 4) + 4 (l / 32) + v % 4,
-  // weight column l % 32.  With a split reduction: raw fp32 partials to
-  // plane z of the workspace (the reduction kernel applies s_t).
-  const bool partial = gridDim.z > 1;
-  float* plane = ws + (int64_t)blockIdx.z * M * K;
-  const float s_t = partial ? 1.0f : tensor_scale[0];
+  store_dx(acc, tensor_scale, dx, ws, M, K, m0 + wm, k0 + wk, out_f32);
+}
+
+// ---------------------------------------------------------------------------
+// k_gemm_dx_tr (n % 64 == 0, k % 128 == 0): the same tiles, waves, MFMA order
+// and split as k_gemm_dx, but the weights are stored in LDS in their own
+// row-major order and transposed by the reads.  Per 64-row step:
+//  * thread t dequantizes 32 consecutive columns of weight row t / 4
+//    (16 bytes of codes, 2 scale bytes) and stores them as four 16-byte
+//    pieces of an LDS row of 128 bf16 (+ 32 bytes of padding);
+//  * the dy tile (128 rows x 64 n) arrives by LDS DMA in whole cache lines,
+//    16-byte pieces XOR-swizzled by row as in the large-M forward kernel;
+//  * a B fragment (8 consecutive n of one weight column per lane) is two
+//    ds_read_b64_tr_b16: within each 16-lane group, lane i of the result
+//    holds element i % 4 of the 4-element reads of lanes i / 4 + 4 j,
+//    j = 0..3, so a lane that reads 4 columns of row 8h + j' gives its
+//    neighbours the column values of 4 consecutive rows.
+// Against k_gemm_dx: no VGPR round trip for dy, four 16-byte LDS stores
+// per thread for the weights instead of sixteen 4-byte ones, and no
+// repacking of column pairs.  Loads: dy one step ahead (two stages), weights
+// two steps ahead in two register sets, inline asm with counted waits.
+constexpr int kWRow = kTK + 16;                 // LDS row of 128 bf16 + 32 bytes
+constexpr int kDyStage = kTM * kTN * 2;         // 16 KiB
+constexpr int kWStage = kTN * kWRow * 2;        // 18 KiB
+constexpr int kTrStage = kDyStage + kWStage;
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(256, 2) void k_gemm_dx_tr(const uint16_t* __restrict__ dy,
+                                                    const uint8_t* __restrict__ codes,
+                                                    const uint8_t* __restrict__ scales,
+                                                    const float* __restrict__ tensor_scale,
+                                                    void* __restrict__ dx, float* __restrict__ ws,
+                                                    int M, int N, int K, int steps_per, int out_f32) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k0 = blockIdx.x * kTK, m0 = blockIdx.y * kTM;
+  const int s_begin = blockIdx.z * steps_per;
+  const int nst = min(N / kTN - s_begin, steps_per);  // >= 1: the plan has no empty split
+  // dy copies: instruction c of wave w takes dy rows 8 (w + 4 c) .. +8 (rows
+  // past M read row M - 1, not stored), lane l the 16-byte piece
+  // (l % 8) ^ ((row / 2) % 8) of row 8 (w + 4 c) + l / 8
+  const uint16_t* dp[4];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int k = k0 + wk + 32 * b + r32;
-      if (k >= K) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm + 32 * a + 8 * (v / 4) + 4 * h + (v % 4);
-        if (m >= M) continue;
-        const float o = acc[a][b][v] * s_t;
-        const int64_t idx = (int64_t)m * K + k;
-        if (partial)
-          plane[idx] = o;
-        else if (out_f32)
-          reinterpret_cast<float*>(dx)[idx] = o;
-        else
-          reinterpret_cast<uint16_t*>(dx)[idx] = (uint16_t)bf16_rne_bits(o);
-      }
-    }
+  for (int c = 0; c < 4; ++c) {
+    const int rho = 8 * (wave + 4 * c) + (lane >> 3);
+    dp[c] = dy + (int64_t)min(m0 + rho, M - 1) * N + (int64_t)s_begin * kTN + 8 * ((lane & 7) ^ ((rho >> 1) & 7));
   }
+  // weights: thread -> row wr of the step, columns 32 wq .. +32 of the tile
+  const int wr = tid >> 2, wq = tid & 3;
+  const uint8_t* cp = codes + (int64_t)(s_begin * kTN + wr) * (K / 2) + k0 / 2 + 16 * wq;
+  const uint8_t* sp = scales + (int64_t)(s_begin * kTN + wr) * (K / 16) + k0 / 16 + 2 * wq;
+  struct WRegs {
+    u32x4_t c;   // 32 codes
+    uint32_t s;  // 2 scale bytes
+  };
+  auto issue_w = [&](WRegs& R, int s) {
+    s = min(s, nst - 1);  // past the last step: the last step again (not used)
+    load_b128_async<0>(R.c, cp + (int64_t)s * kTN * (K / 2));
+    load_u16_async<0>(R.s, sp + (int64_t)s * kTN * (K / 16));
+  };
+  auto issue_dy = [&](int s) {
+    const int st = s & 1;
+    s = min(s, nst - 1);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) copy16_to_lds(dp[c] + (int64_t)s * kTN, lds + st * kTrStage + 1024 * (wave + 4 * c));
+    asm volatile("" ::: "memory");
+  };
+  auto store_w = [&](const WRegs& R, int st) {
+    uint16_t* wl = reinterpret_cast<uint16_t*>(lds + st * kTrStage + kDyStage);
+    const float sg0 = scale_at<kConvHw, 0>(R.s), sg1 = scale_at<kConvHw, 1>(R.s);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(wl + wr * kWRow + 32 * wq + 8 * i) = dequant8_bf16<kConvHw>(R.c[i], i < 2 ? sg0 : sg1);
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.f;
+
+  // wave tile: dy rows 64 (wave / 2) .. +64, weight columns 64 (wave % 2) .. +64
+  const int wm = 64 * (wave >> 1), wk = 64 * (wave & 1);
+  const int r32 = lane & 31, h = lane >> 5;
+  // transposing reads: lane i of group g (h = g / 2, column half g % 2) reads
+  // 4 columns of row 8 h + i / 4 (+ 16 ks, + 4 for the second read)
+  const int sl = lane & 15, grp = lane >> 4;
+  const int trow = 8 * (grp >> 1) + (sl >> 2);
+  const int tcol = wk + 16 * (grp & 1) + 4 * (sl & 3);
+
+  // One step: wait until its weights (set R) and dy copies have landed (only
+  // the next step's weights may be in flight), store the weights, barrier
+  // (every wave's stores and copies are in LDS, every wave is done with the
+  // other stage), issue step s + 1's copies and step s + 2's weights (into
+  // R), multiply.
+  auto step = [&](int s, WRegs& R) {
+    asm volatile("s_waitcnt vmcnt(2)" : "+v"(R.c), "+v"(R.s) : : "memory");
+    const int st = s & 1;
+    store_w(R, st);
+    __syncthreads();
+    issue_dy(s + 1);
+    issue_w(R, s + 2);
+    const uint8_t* dyl = lds + st * kTrStage;
+    const uint16_t* wl = reinterpret_cast<const uint16_t*>(lds + st * kTrStage + kDyStage);
+#pragma unroll
+    for (int ks = 0; ks < kTN / 16; ++ks) {
+      bf16x8_t af[2], bf[2];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) {
+        const int rho = wm + 32 * a + r32;
+        af[a] = *reinterpret_cast<const bf16x8_t*>(dyl + 128 * rho + 16 * ((2 * ks + h) ^ ((rho >> 1) & 7)));
+      }
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const uint16_t* p = wl + (16 * ks + trow) * kWRow + tcol + 32 * b;
+        const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+        const v4i16_t hi =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)(p + 4 * kWRow));
+        bf[b] = __builtin_bit_cast(bf16x8_t, v8i16_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+  };
+
+  WRegs R0, R1;
+  issue_dy(0);
+  issue_w(R0, 0);
+  issue_w(R1, 1);
+  for (int s = 0; s < nst; s += 2) {
+    step(s, R0);
+    if (s + 1 < nst) step(s + 1, R1);
+  }
+  wait_vm_all();  // the tail's clamped loads land before the workgroup's LDS is released
+  store_dx(acc, tensor_scale, dx, ws, M, K, m0 + wm, k0 + wk, out_f32);
 }
 
 }  // namespace
@@ -209,8 +359,16 @@ hipError_t launch_gemm_dx(const uint16_t* dy, const uint8_t* codes, const uint8_
                           int out_f32, const DxPlan& p, void* workspace, hipStream_t stream) {
   const dim3 grid((unsigned)((k + kTK - 1) / kTK), (unsigned)((m + kTM - 1) / kTM), (unsigned)p.splits);
   float* ws = reinterpret_cast<float*>(workspace);
-  hipLaunchKernelGGL(k_gemm_dx, grid, dim3(256), 0, stream, dy, codes, scales, tensor_scale, dx, ws,
-                     (int)m, (int)n, (int)k, p.steps_per, out_f32);
+  if (n % kTN == 0 && k % kTK == 0) {
+    constexpr size_t lds = 2 * (size_t)kTrStage;
+    hipError_t e = set_lds_limit<k_gemm_dx_tr>(lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_gemm_dx_tr, grid, dim3(256), lds, stream, dy, codes, scales, tensor_scale, dx, ws, (int)m,
+                       (int)n, (int)k, p.steps_per, out_f32);
+  } else {
+    hipLaunchKernelGGL(k_gemm_dx, grid, dim3(256), 0, stream, dy, codes, scales, tensor_scale, dx, ws,
+                       (int)m, (int)n, (int)k, p.steps_per, out_f32);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
   return launch_split_reduce(ws, RowScale::one(tensor_scale), dx, m * k, k, p.splits, out_f32, stream);

@@ -33,7 +33,7 @@ _HAVE_HIPCC = os.path.exists("/opt/rocm/bin/hipcc") or bool(os.environ.get("HIPC
 # scale per group of stacked matrices (NVFP4_GROUPED), whose epilogues read
 # each column's scale; both builds are checked
 _BUILDS = [("gemm_skinny.hip", ()), ("gemm_skinny.hip", ("-DNVFP4_GROUPED=1",)),
-           ("gemm_tiled.hip", ()), ("gemm_tiled.hip", ("-DNVFP4_GROUPED=1",))]
+           ("gemm_tiled.hip", ()), ("gemm_tiled.hip", ("-DNVFP4_GROUPED=1",)), ("gemm_dx.hip", ())]
 _ASM = {}
 
 
@@ -70,4 +70,13 @@ def test_counted_waits_cover_every_use(device_asm, source, pattern, minimum, gro
     text = device_asm[(source, ("-DNVFP4_GROUPED=1",) if grouped else ())]
     found, bad = check_assembly(text, pattern)
     assert found >= minimum, found
+    assert bad == [], bad[:10]
+
+
+@pytest.mark.skipif(not _HAVE_HIPCC, reason="hipcc not available")
+def test_counted_waits_input_gradient(device_asm):
+    """The input-gradient kernel with transposing LDS reads loads the weights
+    two steps ahead with inline asm and counted waits, like the kernels above."""
+    found, bad = check_assembly(device_asm[("gemm_dx.hip", ())], r"k_gemm_dx_tr")
+    assert found >= 1, found
     assert bad == [], bad[:10]

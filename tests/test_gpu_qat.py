@@ -20,9 +20,13 @@ def _rel(y, ref):
 
 
 # (m, n, k): one tile, ragged tiles everywhere, n not a multiple of 8 (the
-# unaligned dy rows), k not a multiple of 128, a long reduction
+# unaligned dy rows), k not a multiple of 128, a long reduction.  n % 64 == 0
+# and k % 128 == 0 take the kernel with transposing LDS reads ((1, 64, 128),
+# (128, 256, 256), (64, 4096, 4096) split 16 ways, (257, 14336, 512), (200,
+# 1024, 384) split 4 ways), the others the kernel with transposed stores
+# ((64, 4100, 512): its reduction split 13 ways).
 SHAPES = [(1, 64, 128), (17, 100, 48), (128, 256, 256), (300, 1001, 1040), (64, 4096, 4096),
-          (257, 14336, 512)]
+          (257, 14336, 512), (200, 1024, 384), (64, 4100, 512)]
 
 
 @pytest.mark.parametrize("m,n,k", SHAPES)
