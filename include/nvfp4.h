@@ -258,9 +258,9 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  * The tiled kernel (bf16 MFMA): when k % 64 == 0, one 64-token tile x 256
  * (or, for k >= 8192, 128) weight rows for m <= 64, 128 x 128 tiles for
  * m <= 128, else 256 weight rows x 128 tokens with the weights dequantized
- * in registers; K is split over workgroups (fp32 partials in the
- * workspace, one reduction kernel) when there are few tiles.  Other k:
- * 128 x 128 single-stage tiles.
+ * in registers (128 k per barrier when k % 128 == 0); K is split over
+ * workgroups (fp32 partials in the workspace, one reduction kernel) when
+ * there are few tiles.  Other k: 128 x 128 single-stage tiles.
  */
 NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size(int64_t m, int64_t n, int64_t k);
 NVFP4_API int nvfp4_w4a16_gemm(const void* x, const uint8_t* codes, const uint8_t* scales,
@@ -296,8 +296,8 @@ NVFP4_API int nvfp4_w4a16_gemm_grouped(const void* x, const uint8_t* codes, cons
  * (0 = automatic; skinny path: >= 1 = the split-K kernel with that many K
  * chunks, clamped to [1, 64], more when a chunk would not fit in registers
  * and LDS; tiled path with k % 64 == 0: that many K splits of whole 64-wide
- * steps, at most k / 64, fewer when the steps do not divide evenly; other k
- * ignore it) and a dequantization implementation (NVFP4_IMPL_*).  The
+ * steps (128-wide when m > 128 and k % 128 == 0), at most k / 64, fewer when
+ * the steps do not divide evenly; other k ignore it) and a dequantization implementation (NVFP4_IMPL_*).  The
  * skinny path requires m <= 64.  The workspace size for these choices is
  * nvfp4_w4a16_gemm_workspace_size_ex(m, n, k, path, split_k). */
 NVFP4_API size_t nvfp4_w4a16_gemm_workspace_size_ex(int64_t m, int64_t n, int64_t k, int path,
