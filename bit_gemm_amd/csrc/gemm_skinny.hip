@@ -1687,6 +1687,12 @@ SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits) 
     int64_t waves = (k + kWaveK - 1) / kWaveK;
     if (waves < 1) waves = 1;
     if (waves > 8) waves = 8;
+    // one or two tokens on more than 1024 row tiles (e.g. gate and up
+    // stacked, 28672 x 4096): four waves of two rounds, the second round's
+    // loads in flight while the first is multiplied - 32 back-to-back calls
+    // at m = 1 / 2: 519 / 568 against 549 / 592 us; on 768 tiles (q, k, v
+    // stacked) it was even or slower (296 / 334 against 294 / 319 us)
+    if (m <= 2 && (n + 15) / 16 > 1024 && k <= 4096 && waves > 4) waves = 4;
     p.splits = 0;
     p.waves = (int)waves;
     p.steps_per_wave = kSpw;

@@ -148,6 +148,8 @@ FULL_K_CASES = [
     (32, 4096, 3072), (49, 64, 2048),
     # two to four row tiles per workgroup (more than 256 tiles), ragged n
     (17, 8192, 4096), (48, 12000, 4096), (33, 14336, 2048), (25, 7777, 2048),
+    # one or two tokens on more than 1024 row tiles: four waves of two rounds
+    (1, 16400, 4096), (2, 16416, 4096), (1, 20000, 3584),
 ]
 
 
