@@ -232,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_dx_tr(const uint16_t* __restric
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int k0 = blockIdx.x * kTK, m0 = blockIdx.y * kTM;
   const int s_begin = blockIdx.z * steps_per;
-  const int nst = min(N / kTN - s_begin, steps_per);  // >= 1: the plan has no empty split
+  const int nst = min(N / kTN - s_begin, steps_per);  // >= 1: n > 0 and the plan has no empty split
   // dy copies: instruction c of wave w takes dy rows 8 (w + 4 c) .. +8 (rows
   // past M read row M - 1, not stored), lane l the 16-byte piece
   // (l % 8) ^ ((row / 2) % 8) of row 8 (w + 4 c) + l / 8
@@ -359,7 +359,7 @@ hipError_t launch_gemm_dx(const uint16_t* dy, const uint8_t* codes, const uint8_
                           int out_f32, const DxPlan& p, void* workspace, hipStream_t stream) {
   const dim3 grid((unsigned)((k + kTK - 1) / kTK), (unsigned)((m + kTM - 1) / kTM), (unsigned)p.splits);
   float* ws = reinterpret_cast<float*>(workspace);
-  if (n % kTN == 0 && k % kTK == 0) {
+  if (n > 0 && n % kTN == 0 && k % kTK == 0) {  // n == 0 (zeros) stays with k_gemm_dx, which loads nothing then
     constexpr size_t lds = 2 * (size_t)kTrStage;
     hipError_t e = set_lds_limit<k_gemm_dx_tr>(lds);
     if (e != hipSuccess) return e;

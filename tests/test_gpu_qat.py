@@ -85,8 +85,10 @@ def test_full_size_sampled_rows_and_empty():
     rows = np.unique(np.concatenate([[0, 127, 128, 4095], np.random.default_rng(4).choice(m, 12, replace=False)]))
     ref = oracle.qat_input_grad(dy[torch.from_numpy(rows)], r.codes, r.scales, r.tensor_scale)
     assert _rel(dx[rows], ref) <= 1e-5
-    # no weight rows: the product is zero
-    q0 = nv.quantize_fos(torch.zeros((0, 64), dtype=torch.float32, device="cuda"))
-    z = nv.w4a16_gemm_dx(torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda"), q0, out_dtype=torch.float32)
-    torch.cuda.synchronize()
-    assert z.shape == (5, 64) and float(z.abs().sum()) == 0.0
+    # no weight rows: the product is zero (k = 128 would otherwise select the
+    # kernel with transposing reads, which needs at least one 64-row step)
+    for k0 in (64, 128):
+        q0 = nv.quantize_fos(torch.zeros((0, k0), dtype=torch.float32, device="cuda"))
+        z = nv.w4a16_gemm_dx(torch.zeros((5, 0), dtype=torch.bfloat16, device="cuda"), q0, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert z.shape == (5, k0) and float(z.abs().sum()) == 0.0
