@@ -149,7 +149,12 @@ FULL_K_CASES = [
     # two to four row tiles per workgroup (more than 256 tiles), ragged n
     (17, 8192, 4096), (48, 12000, 4096), (33, 14336, 2048), (25, 7777, 2048),
     # one or two tokens on more than 1024 row tiles: four waves of two rounds
+    # (one token with k = 2048 c: the row-per-wave kernel with the hardware
+    # decode; 3584 is not such a k)
     (1, 16400, 4096), (2, 16416, 4096), (1, 20000, 3584),
+    # one token, row-per-wave kernel: more than 256 row tiles (ragged n, one
+    # 2048-wide chunk), or k > 4096 (3 and 8 chunks)
+    (1, 4100, 2048), (1, 4096, 6144), (1, 2000, 16384),
 ]
 
 
