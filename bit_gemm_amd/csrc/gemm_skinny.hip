@@ -390,22 +390,25 @@ __global__ __launch_bounds__(512) void k_skinny_dot(const uint16_t* __restrict__
   }
 }
 
-// Row-per-wave dot-product kernel for one token on tall or long matrices
-// (k = 2048 NCH, NCH <= 8): each wave owns two whole weight rows and its 64
-// lanes run along K, so a code load instruction reads 1 KiB of one row
-// (lane l: bytes 1024 c + 16 l of chunk c, codes k = 2048 c + 32 l .. +32)
-// and a scale load 128 contiguous bytes; every row of the workgroup's 16
-// reads the token's activations from LDS, staged once per workgroup (the
+// Row-per-wave dot-product kernel for one token (k = 2048 NCH, NCH <= 8):
+// each wave owns two whole weight rows and its 64 lanes run along K, so a
+// code load instruction reads 1 KiB of one row (lane l: bytes 1024 c + 16 l
+// of chunk c, codes k = 2048 c + 32 l .. +32) and a scale load 128
+// contiguous bytes; every row of the workgroup's 8 (4 waves) reads the
+// token's activations from LDS, staged once per workgroup (the
 // copies are issued before the weight loads, so they land first and the
 // multiplies of chunk 0 can start while the later chunks stream in).  Per
 // chunk and row a lane forms the two 16-code block sums with v_dot2 on the
 // unit-scale decode, scales each by its sigma, and the 64 lane sums of a
 // row are added with xor shuffles in a fixed order.  Against the full-K dot
 // kernel (rows across lanes, K slices across waves, a cross-wave sum in
-// LDS), measured at m = 1: 12288 x 4096 7.6 against 8.8 us, 28672 x 4096
-// 14.2 against 16.2 us, 4096 x 14336 9.9 against 10.9 us; 4096 x 4096 even
-// (4.5 us), so 256 row tiles with k <= 4096 keep the full-K kernel.
-constexpr int kRdWaves = 8, kRdRows = 2;  // waves per workgroup, rows per wave
+// LDS), measured at m = 1 (per call, 32 back-to-back calls on rotating
+// copies): 4096 x 4096 4.25 against 4.52 us, 14336 x 4096 7.9 against 8.6,
+// 12288 x 4096 7.2 against 8.8, 28672 x 4096 13.1-14.1 against 16.2, 4096 x
+// 14336 9.3 against 10.9 us.  Eight rows per workgroup measured best over
+// 4 / 8 / 16 waves of 1, 2 or 4 rows (16 rows: 4096 x 14336 10.2 us, 4096 x
+// 4096 4.5 us).
+constexpr int kRdWaves = 4, kRdRows = 2;  // waves per workgroup, rows per wave
 template <int NCH>
 __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* __restrict__ x,
                                                              const uint8_t* __restrict__ codes,
@@ -1750,11 +1753,9 @@ SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits);
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   int w = 0, r = 0, t = 0;
-  // one token on more than 256 row tiles or k > 4096, k = 2048 x (1 .. 8):
-  // the row-per-wave dot-product kernel (the portable decode takes the
-  // full-K kernel with the same plan's waves)
-  if (forced_splits <= 0 && m == 1 && k % 2048 == 0 && k / 2048 >= 1 && k / 2048 <= 8 &&
-      ((n + 15) / 16 > 256 || k > 4096)) {
+  // one token, k = 2048 x (1 .. 8): the row-per-wave dot-product kernel
+  // (the portable decode takes the full-K kernel with the same plan's waves)
+  if (forced_splits <= 0 && m == 1 && k % 2048 == 0 && k / 2048 >= 1 && k / 2048 <= 8) {
     SkinnyPlan p = plan_skinny_base(m, n, k, forced_splits);
     if (p.splits == 0) {
       p.rdot_chunks = (int)(k / 2048);

@@ -152,9 +152,10 @@ FULL_K_CASES = [
     # (one token with k = 2048 c: the row-per-wave kernel with the hardware
     # decode; 3584 is not such a k)
     (1, 16400, 4096), (2, 16416, 4096), (1, 20000, 3584),
-    # one token, row-per-wave kernel: more than 256 row tiles (ragged n, one
-    # 2048-wide chunk), or k > 4096 (3 and 8 chunks)
-    (1, 4100, 2048), (1, 4096, 6144), (1, 2000, 16384),
+    # one token, row-per-wave kernel (k = 2048 c): ragged n with one
+    # 2048-wide chunk, 3 and 8 chunks, n not a multiple of the 8 rows of a
+    # workgroup
+    (1, 4100, 2048), (1, 4096, 6144), (1, 2000, 16384), (1, 1003, 4096),
 ]
 
 
