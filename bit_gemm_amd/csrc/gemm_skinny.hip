@@ -416,35 +416,38 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* _
                                                              const KScale tensor_scale,
                                                              void* __restrict__ y, int N, int out_f32) {
   constexpr int K = 2048 * NCH;
-  constexpr int XP = K / 8;                                            // 16-byte pieces of x
-  constexpr int XPT = (XP + 64 * kRdWaves - 1) / (64 * kRdWaves);      // per thread
+  constexpr int XPT = K / 8 / (64 * kRdWaves);  // 16-byte pieces of x per thread
+  static_assert(XPT * 8 * 64 * kRdWaves == K, "every thread copies the same number of x pieces");
   __shared__ __attribute__((aligned(16))) uint16_t xs[K];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row0 = (blockIdx.x * kRdWaves + wave) * kRdRows;
+  // Every piece is in range, so no load is conditional: a guarded load would
+  // make the compiler wait for the activations before issuing any weight load.
   u32x4_t xv[XPT];
 #pragma unroll
-  for (int t = 0; t < XPT; ++t) {
-    const int i = threadIdx.x + 64 * kRdWaves * t;
-    if (i < XP) xv[t] = *reinterpret_cast<const u32x4_t*>(x + 8 * i);
-  }
-  u32x4_t cw[kRdRows][NCH];
-  uint32_t sw[kRdRows][NCH];
+  for (int t = 0; t < XPT; ++t) xv[t] = *reinterpret_cast<const u32x4_t*>(x + 8 * (threadIdx.x + 64 * kRdWaves * t));
+  const uint8_t* crow[kRdRows];
+  const uint8_t* srow[kRdRows];
 #pragma unroll
   for (int j = 0; j < kRdRows; ++j) {
     const int row = min(row0 + j, N - 1);  // rows past N read row N - 1, not stored
-    const uint8_t* crow = codes + (int64_t)row * (K / 2);
-    const uint8_t* srow = scales + (int64_t)row * (K / 16);
+    crow[j] = codes + (int64_t)row * (K / 2);
+    srow[j] = scales + (int64_t)row * (K / 16);
+  }
+  // chunk-major: chunk c of every row lands before chunk c + 1, so the dot
+  // products below start while later chunks are still in flight
+  u32x4_t cw[kRdRows][NCH];
+  uint32_t sw[kRdRows][NCH];
 #pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      cw[j][c] = *reinterpret_cast<const u32x4_t*>(crow + 1024 * c + 16 * lane);
-      sw[j][c] = *reinterpret_cast<const uint16_t*>(srow + 128 * c + 2 * lane);
+  for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+    for (int j = 0; j < kRdRows; ++j) {
+      cw[j][c] = *reinterpret_cast<const u32x4_t*>(crow[j] + 1024 * c + 16 * lane);
+      sw[j][c] = *reinterpret_cast<const uint16_t*>(srow[j] + 128 * c + 2 * lane);
     }
   }
 #pragma unroll
-  for (int t = 0; t < XPT; ++t) {
-    const int i = threadIdx.x + 64 * kRdWaves * t;
-    if (i < XP) *reinterpret_cast<u32x4_t*>(xs + 8 * i) = xv[t];
-  }
+  for (int t = 0; t < XPT; ++t) *reinterpret_cast<u32x4_t*>(xs + 8 * (threadIdx.x + 64 * kRdWaves * t)) = xv[t];
   __syncthreads();
   float acc[kRdRows] = {};
 #pragma unroll
