@@ -476,11 +476,84 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* _
   }
 }
 
+// The same dot products for long rows (NCH >= 3): one row per wave (16 rows
+// per workgroup halve the x copies per weight byte but leave too few waves
+// to overlap the chunks' sums with the loads) and the activations copied
+// into LDS by the LDS DMA, issued before the weight loads.  The weight loads
+// are inline asm in chunk order, so one counted wait (only the weight loads
+// may stay outstanding) and a bare barrier make every wave's copies
+// visible, and chunk c waits only for its own loads (the compiler's own
+// wait for the copies would be vmcnt(0), i.e. for every weight load too).
+// Measured at m = 1 against the two-row kernel above (per call, 32 calls on
+// rotating copies): 4096 x 8192 5.66 against 5.89 us, 4096 x 12288 7.45
+// against 7.87, 4096 x 14336 8.45 against 8.70, 4096 x 16384 9.08 against
+// 9.98, 11008 x 6144 8.92 against 9.26; 4096 x 6144 even (4.89 / 4.88); at
+// NCH <= 2 it is slower (14336 x 4096 8.89 against 7.61 us), so those keep
+// the two-row kernel.
+template <int NCH, int C>
+__device__ __forceinline__ void rdot_dma_chunk(u32x4_t (&cw)[NCH], uint32_t (&sw)[NCH], const uint16_t* xs, int lane,
+                                               float& acc) {
+  wait_vm<2 * (NCH - 1 - C)>(cw[C], sw[C]);
+  u32x4_t xq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xq[q] = *reinterpret_cast<const u32x4_t*>(xs + 2048 * C + 32 * lane + 8 * q);
+  const uint32_t s2 = sw[C];
+  const float sg0 = scale_at<kConvHw, 0>(s2), sg1 = scale_at<kConvHw, 1>(s2);
+  const float b0 = dot8<kConvHw>(cw[C][1], xq[1], dot8<kConvHw>(cw[C][0], xq[0], 0.0f));
+  const float b1 = dot8<kConvHw>(cw[C][3], xq[3], dot8<kConvHw>(cw[C][2], xq[2], 0.0f));
+  acc += sg0 * b0;
+  acc += sg1 * b1;
+  if constexpr (C + 1 < NCH) rdot_dma_chunk<NCH, C + 1>(cw, sw, xs, lane, acc);
+}
+
+template <int NCH>
+__global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot_dma(const uint16_t* __restrict__ x,
+                                                                 const uint8_t* __restrict__ codes,
+                                                                 const uint8_t* __restrict__ scales,
+                                                                 const KScale tensor_scale,
+                                                                 void* __restrict__ y, int N, int out_f32) {
+  constexpr int K = 2048 * NCH;
+  constexpr int XPT = K / 8 / (64 * kRdWaves);  // 16-byte pieces of x per lane
+  static_assert(XPT * 8 * 64 * kRdWaves == K, "every lane copies the same number of x pieces");
+  __shared__ __attribute__((aligned(16))) uint16_t xs[K];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < XPT; ++t)  // piece i = threadIdx.x + 256 t lands at byte 16 i of xs
+    copy16_to_lds(x + 8 * ((int)threadIdx.x + 64 * kRdWaves * t),
+                  reinterpret_cast<uint8_t*>(xs) + 16 * (64 * kRdWaves * t + 64 * wave));
+  const int row = blockIdx.x * kRdWaves + wave;
+  const int rr = min(row, N - 1);  // a row past N reads row N - 1, not stored
+  const uint8_t* crow = codes + (int64_t)rr * (K / 2) + 16 * lane;
+  const uint8_t* srow = scales + (int64_t)rr * (K / 16) + 2 * lane;
+  u32x4_t cw[NCH];
+  uint32_t sw[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    load_b128_async<0>(cw[c], crow + 1024 * c);
+    load_u16_async<0>(sw[c], srow + 128 * c);
+  }
+  wait_vm_count<2 * NCH>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");  // no LDS read moves above the barrier
+  float acc = 0.0f;
+  rdot_dma_chunk<NCH, 0>(cw, sw, xs, lane, acc);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0 && row < N) store_out(y, row, acc * col_scale(tensor_scale, row, first_scale(tensor_scale)), out_f32);
+}
+
 template <int NCH>
 hipError_t launch_rdot_n(hipStream_t stream, const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                          KScale ts, void* y, int N, int out_f32) {
-  const dim3 grid((unsigned)((N + kRdWaves * kRdRows - 1) / (kRdWaves * kRdRows)));
-  hipLaunchKernelGGL((k_skinny_rdot<NCH>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N, out_f32);
+  if constexpr (NCH >= 3) {
+    const dim3 grid((unsigned)((N + kRdWaves - 1) / kRdWaves));
+    hipLaunchKernelGGL((k_skinny_rdot_dma<NCH>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N,
+                       out_f32);
+  } else {
+    const dim3 grid((unsigned)((N + kRdWaves * kRdRows - 1) / (kRdWaves * kRdRows)));
+    hipLaunchKernelGGL((k_skinny_rdot<NCH>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N,
+                       out_f32);
+  }
   return hipGetLastError();
 }
 

@@ -239,6 +239,16 @@ __device__ __forceinline__ void bind_loaded(u32x4_t& c, uint32_t& s) {
 #endif
 }
 
+// Wait until at most V vector-memory operations of this wave are
+// outstanding, binding no register: for LDS DMA copies issued before V
+// loads (their data is read from LDS after a barrier, not from registers).
+template <int V>
+__device__ __forceinline__ void wait_vm_count() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(V > 63 ? 63 : V) : "memory");
+#endif
+}
+
 // Wait until every vector-memory operation of this wave has completed.
 __device__ __forceinline__ void wait_vm_all() {
 #if defined(__HIP_DEVICE_COMPILE__)

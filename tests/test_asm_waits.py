@@ -1,5 +1,5 @@
-"""The pipelined split-K and persistent full-K skinny kernels and the large-M kernel with the
-weights in registers issue their weight loads as inline asm and wait for
+"""The pipelined split-K, persistent full-K and one-token row-per-wave skinny kernels and the
+large-M kernel with the weights in registers issue their weight loads as inline asm and wait for
 them with counted vmcnt waits.  Compile them for gfx950 (device assembly,
 the library's own flags) and check that no instruction touches a load's
 destination register before the wait that covers it."""
@@ -64,6 +64,7 @@ def device_asm(tmp_path_factory):
     ("gemm_skinny.hip", r"k_skinny_str", 16),    # streaming kernel: MT 1..4 x chunk lengths x 2 conversion implementations
     ("gemm_skinny.hip", r"k_skinny_pk", 4),      # persistent full-K kernel: 8 or 16 token rows x 2 implementations
     ("gemm_skinny.hip", r"k_skinny_fx", 48),     # single-launch full-K kernel: MT 2..4 x 4 or 8 steps x 1..4 tiles x 2 implementations
+    ("gemm_skinny.hip", r"k_skinny_rdot_dma", 6),  # one-token row-per-wave kernel with LDS DMA activations: 3..8 chunks of 2048
     ("gemm_tiled.hip", r"k_lmr", 4),             # weights-in-registers large-M kernels (64 or 128 k per barrier), 2 implementations each
 ])
 def test_counted_waits_cover_every_use(device_asm, source, pattern, minimum, grouped):

@@ -156,6 +156,10 @@ FULL_K_CASES = [
     # 2048-wide chunk, 3 and 8 chunks, n not a multiple of the 8 rows of a
     # workgroup
     (1, 4100, 2048), (1, 4096, 6144), (1, 2000, 16384), (1, 1003, 4096),
+    # from 3 chunks one row per wave with the activations copied by LDS DMA:
+    # every chunk count 4 .. 7, n not a multiple of the 4 rows of a
+    # workgroup, a single row
+    (1, 4097, 8192), (1, 1003, 10240), (1, 1, 12288), (1, 4101, 14336),
 ]
 
 
