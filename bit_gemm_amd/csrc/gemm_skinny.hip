@@ -390,7 +390,8 @@ __global__ __launch_bounds__(512) void k_skinny_dot(const uint16_t* __restrict__
   }
 }
 
-// Row-per-wave dot-product kernel for one token (k = 2048 NCH, NCH <= 8):
+// Row-per-wave dot-product kernel for one token, k = 2048 NCH (it takes NCH
+// <= 2; longer rows and partial chunks take the LDS DMA form below):
 // each wave owns two whole weight rows and its 64 lanes run along K, so a
 // code load instruction reads 1 KiB of one row (lane l: bytes 1024 c + 16 l
 // of chunk c, codes k = 2048 c + 32 l .. +32) and a scale load 128
@@ -476,98 +477,140 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* _
   }
 }
 
-// The same dot products for long rows (NCH >= 3): one row per wave (16 rows
-// per workgroup halve the x copies per weight byte but leave too few waves
-// to overlap the chunks' sums with the loads) and the activations copied
-// into LDS by the LDS DMA, issued before the weight loads.  The weight loads
-// are inline asm in chunk order, so one counted wait (only the weight loads
-// may stay outstanding) and a bare barrier make every wave's copies
-// visible, and chunk c waits only for its own loads (the compiler's own
-// wait for the copies would be vmcnt(0), i.e. for every weight load too).
-// Measured at m = 1 against the two-row kernel above (per call, 32 calls on
-// rotating copies): 4096 x 8192 5.66 against 5.89 us, 4096 x 12288 7.45
-// against 7.87, 4096 x 14336 8.45 against 8.70, 4096 x 16384 9.08 against
-// 9.98, 11008 x 6144 8.92 against 9.26; 4096 x 6144 even (4.89 / 4.88); at
-// NCH <= 2 it is slower (14336 x 4096 8.89 against 7.61 us), so those keep
-// the two-row kernel.
-template <int NCH, int C>
-__device__ __forceinline__ void rdot_dma_chunk(u32x4_t (&cw)[NCH], uint32_t (&sw)[NCH], const uint16_t* xs, int lane,
-                                               float& acc) {
-  wait_vm<2 * (NCH - 1 - C)>(cw[C], sw[C]);
+// The same dot products with the activations copied into LDS by the LDS
+// DMA, issued before the weight loads, and k = 2048 (NCH - 1) + kl for any
+// 0 < kl <= 2048 with kl % 256 == 0: in a partial last chunk only lanes
+// < kl / 32 hold codes; the others load piece 0 of that chunk (a valid
+// address) and their sums are discarded by a select (the activations they
+// read from LDS past k are never written).  The weight loads are inline asm
+// in chunk order, so one counted wait (only the weight loads may stay
+// outstanding) and a bare barrier make every wave's copies visible, and
+// chunk c waits only for its own loads (the compiler's own wait for the
+// copies would be vmcnt(0), i.e. for every weight load too).  RW rows per
+// wave: one for long rows (16 rows per workgroup halve the x copies per
+// weight byte but leave too few waves to overlap the chunks' sums with the
+// loads), two for one or two chunks on tall matrices.  Measured at m = 1
+// (per call, 32 calls on rotating copies), whole chunks against the two-row
+// kernel above: 4096 x 8192 5.66 against 5.89 us, 4096 x 12288 7.45 against
+// 7.87, 4096 x 14336 8.45 against 8.70, 4096 x 16384 9.08 against 9.98,
+// 11008 x 6144 8.92 against 9.26; 4096 x 6144 even (4.89 / 4.88); at
+// NCH <= 2 slower (14336 x 4096 8.89 against 7.61 us), so whole chunks
+// there keep the two-row kernel.  k not a multiple of 2048, against the
+// full-K dot kernel that took them before: 5120 x 13824 9.2 against 16.0 us,
+// 13824 x 5120 9.3 against 14.5, 4096 x 11008 7.1 against 9.1, 18944 x 3584
+// 8.9 (two rows per wave; one row 9.5) against 11.1, 1003 x 2816 2.6
+// against 3.4, 3584 x 3584 3.84 against 3.90 us.
+template <int NCH, int RW, int C>
+__device__ __forceinline__ void rdot_dma_chunk(u32x4_t (&cw)[RW][NCH], uint32_t (&sw)[RW][NCH], const uint16_t* xs,
+                                               int lane, bool on_last, float (&acc)[RW]) {
+#pragma unroll
+  for (int j = 0; j < RW; ++j) wait_vm<2 * RW * (NCH - 1 - C)>(cw[j][C], sw[j][C]);
   u32x4_t xq[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) xq[q] = *reinterpret_cast<const u32x4_t*>(xs + 2048 * C + 32 * lane + 8 * q);
-  const uint32_t s2 = sw[C];
-  const float sg0 = scale_at<kConvHw, 0>(s2), sg1 = scale_at<kConvHw, 1>(s2);
-  const float b0 = dot8<kConvHw>(cw[C][1], xq[1], dot8<kConvHw>(cw[C][0], xq[0], 0.0f));
-  const float b1 = dot8<kConvHw>(cw[C][3], xq[3], dot8<kConvHw>(cw[C][2], xq[2], 0.0f));
-  acc += sg0 * b0;
-  acc += sg1 * b1;
-  if constexpr (C + 1 < NCH) rdot_dma_chunk<NCH, C + 1>(cw, sw, xs, lane, acc);
+#pragma unroll
+  for (int j = 0; j < RW; ++j) {
+    const uint32_t s2 = sw[j][C];
+    const float sg0 = scale_at<kConvHw, 0>(s2), sg1 = scale_at<kConvHw, 1>(s2);
+    const float b0 = dot8<kConvHw>(cw[j][C][1], xq[1], dot8<kConvHw>(cw[j][C][0], xq[0], 0.0f));
+    const float b1 = dot8<kConvHw>(cw[j][C][3], xq[3], dot8<kConvHw>(cw[j][C][2], xq[2], 0.0f));
+    if constexpr (C == NCH - 1) {
+      acc[j] += on_last ? sg0 * b0 : 0.0f;
+      acc[j] += on_last ? sg1 * b1 : 0.0f;
+    } else {
+      acc[j] += sg0 * b0;
+      acc[j] += sg1 * b1;
+    }
+  }
+  if constexpr (C + 1 < NCH) rdot_dma_chunk<NCH, RW, C + 1>(cw, sw, xs, lane, on_last, acc);
 }
 
-template <int NCH>
+template <int NCH, int RW>
 __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot_dma(const uint16_t* __restrict__ x,
                                                                  const uint8_t* __restrict__ codes,
                                                                  const uint8_t* __restrict__ scales,
                                                                  const KScale tensor_scale,
-                                                                 void* __restrict__ y, int N, int out_f32) {
-  constexpr int K = 2048 * NCH;
-  constexpr int XPT = K / 8 / (64 * kRdWaves);  // 16-byte pieces of x per lane
-  static_assert(XPT * 8 * 64 * kRdWaves == K, "every lane copies the same number of x pieces");
-  __shared__ __attribute__((aligned(16))) uint16_t xs[K];
+                                                                 void* __restrict__ y, int N, int K, int out_f32) {
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2048 * NCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int xp = K / 8;  // 16-byte pieces of x (a multiple of 32)
 #pragma unroll
-  for (int t = 0; t < XPT; ++t)  // piece i = threadIdx.x + 256 t lands at byte 16 i of xs
-    copy16_to_lds(x + 8 * ((int)threadIdx.x + 64 * kRdWaves * t),
-                  reinterpret_cast<uint8_t*>(xs) + 16 * (64 * kRdWaves * t + 64 * wave));
-  const int row = blockIdx.x * kRdWaves + wave;
-  const int rr = min(row, N - 1);  // a row past N reads row N - 1, not stored
-  const uint8_t* crow = codes + (int64_t)rr * (K / 2) + 16 * lane;
-  const uint8_t* srow = scales + (int64_t)rr * (K / 16) + 2 * lane;
-  u32x4_t cw[NCH];
-  uint32_t sw[NCH];
+  for (int t = 0; t < NCH; ++t) {  // piece i = threadIdx.x + 256 t lands at byte 16 i of xs
+    const int i = (int)threadIdx.x + 64 * kRdWaves * t;
+    if (i < xp) copy16_to_lds(x + 8 * i, reinterpret_cast<uint8_t*>(xs) + 16 * (64 * kRdWaves * t + 64 * wave));
+  }
+  const bool on_last = lane < (K - 2048 * (NCH - 1)) / 32;  // this lane holds codes in the last chunk
+  const int lane_last = on_last ? lane : 0;
+  const int row0 = (blockIdx.x * kRdWaves + wave) * RW;
+  const uint8_t* crow[RW];
+  const uint8_t* srow[RW];
+#pragma unroll
+  for (int j = 0; j < RW; ++j) {
+    const int rr = min(row0 + j, N - 1);  // a row past N reads row N - 1, not stored
+    crow[j] = codes + (int64_t)rr * (K / 2);
+    srow[j] = scales + (int64_t)rr * (K / 16);
+  }
+  u32x4_t cw[RW][NCH];
+  uint32_t sw[RW][NCH];
 #pragma unroll
   for (int c = 0; c < NCH; ++c) {
-    load_b128_async<0>(cw[c], crow + 1024 * c);
-    load_u16_async<0>(sw[c], srow + 128 * c);
+    const int l = c == NCH - 1 ? lane_last : lane;
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+      load_b128_async<0>(cw[j][c], crow[j] + 1024 * c + 16 * l);
+      load_u16_async<0>(sw[j][c], srow[j] + 128 * c + 2 * l);
+    }
   }
-  wait_vm_count<2 * NCH>();
+  wait_vm_count<2 * RW * NCH>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");  // no LDS read moves above the barrier
-  float acc = 0.0f;
-  rdot_dma_chunk<NCH, 0>(cw, sw, xs, lane, acc);
+  float acc[RW] = {};
+  rdot_dma_chunk<NCH, RW, 0>(cw, sw, xs, lane, on_last, acc);
+  const float s_t = first_scale(tensor_scale);
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0 && row < N) store_out(y, row, acc * col_scale(tensor_scale, row, first_scale(tensor_scale)), out_f32);
+  for (int j = 0; j < RW; ++j) {
+    float v = acc[j];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int row = row0 + j;
+    if (lane == 0 && row < N) store_out(y, row, v * col_scale(tensor_scale, row, s_t), out_f32);
+  }
 }
 
 template <int NCH>
 hipError_t launch_rdot_n(hipStream_t stream, const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
-                         KScale ts, void* y, int N, int out_f32) {
-  if constexpr (NCH >= 3) {
-    const dim3 grid((unsigned)((N + kRdWaves - 1) / kRdWaves));
-    hipLaunchKernelGGL((k_skinny_rdot_dma<NCH>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N,
-                       out_f32);
-  } else {
-    const dim3 grid((unsigned)((N + kRdWaves * kRdRows - 1) / (kRdWaves * kRdRows)));
-    hipLaunchKernelGGL((k_skinny_rdot<NCH>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N,
-                       out_f32);
+                         KScale ts, void* y, int N, int K, int out_f32) {
+  if constexpr (NCH <= 2) {
+    if (K == 2048 * NCH) {  // whole chunks: the two-row kernel staging x through registers
+      const dim3 grid((unsigned)((N + kRdWaves * kRdRows - 1) / (kRdWaves * kRdRows)));
+      hipLaunchKernelGGL((k_skinny_rdot<NCH>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N,
+                         out_f32);
+      return hipGetLastError();
+    }
+    if (N > 8192) {  // a partial chunk on a tall matrix: two rows per wave
+      const dim3 grid((unsigned)((N + 2 * kRdWaves - 1) / (2 * kRdWaves)));
+      hipLaunchKernelGGL((k_skinny_rdot_dma<NCH, 2>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y,
+                         N, K, out_f32);
+      return hipGetLastError();
+    }
   }
+  const dim3 grid((unsigned)((N + kRdWaves - 1) / kRdWaves));
+  hipLaunchKernelGGL((k_skinny_rdot_dma<NCH, 1>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N, K,
+                     out_f32);
   return hipGetLastError();
 }
 
 hipError_t launch_rdot(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
-                       const uint8_t* scales, KScale ts, void* y, int N, int out_f32) {
+                       const uint8_t* scales, KScale ts, void* y, int N, int K, int out_f32) {
   switch (p.rdot_chunks) {
-    case 1: return launch_rdot_n<1>(stream, x, codes, scales, ts, y, N, out_f32);
-    case 2: return launch_rdot_n<2>(stream, x, codes, scales, ts, y, N, out_f32);
-    case 3: return launch_rdot_n<3>(stream, x, codes, scales, ts, y, N, out_f32);
-    case 4: return launch_rdot_n<4>(stream, x, codes, scales, ts, y, N, out_f32);
-    case 5: return launch_rdot_n<5>(stream, x, codes, scales, ts, y, N, out_f32);
-    case 6: return launch_rdot_n<6>(stream, x, codes, scales, ts, y, N, out_f32);
-    case 7: return launch_rdot_n<7>(stream, x, codes, scales, ts, y, N, out_f32);
-    case 8: return launch_rdot_n<8>(stream, x, codes, scales, ts, y, N, out_f32);
+    case 1: return launch_rdot_n<1>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 2: return launch_rdot_n<2>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 3: return launch_rdot_n<3>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 4: return launch_rdot_n<4>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 5: return launch_rdot_n<5>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 6: return launch_rdot_n<6>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 7: return launch_rdot_n<7>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 8: return launch_rdot_n<8>(stream, x, codes, scales, ts, y, N, K, out_f32);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1660,7 +1703,7 @@ hipError_t launch_mt(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x,
                      float* ws, int M, int N, int K, int out_f32) {
   if constexpr (MT == 1) {
     if (p.splits == 0 && p.rdot_chunks > 0 && IMPL == kConvHw)  // row-per-wave dot products (m == 1)
-      return launch_rdot(p, stream, x, codes, scales, ts, y, N, out_f32);
+      return launch_rdot(p, stream, x, codes, scales, ts, y, N, K, out_f32);
     if (p.splits == 0 && p.pk_rounds > 0) {  // persistent full-K kernel
       if constexpr (K32) {  // the planner takes it for 4 < m <= 16
         if (M <= 8) return launch_pk_r<8, IMPL>(p, stream, x, codes, scales, ts, y, M, N, K, out_f32);
@@ -1829,12 +1872,13 @@ SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits);
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   int w = 0, r = 0, t = 0;
-  // one token, k = 2048 x (1 .. 8): the row-per-wave dot-product kernel
-  // (the portable decode takes the full-K kernel with the same plan's waves)
-  if (forced_splits <= 0 && m == 1 && k % 2048 == 0 && k / 2048 >= 1 && k / 2048 <= 8) {
+  // one token, 0 < k <= 16384 with k % 256 == 0: the row-per-wave
+  // dot-product kernel over ceil(k / 2048) chunks of 2048 (the portable
+  // decode takes the full-K kernel with the same plan's waves)
+  if (forced_splits <= 0 && m == 1 && k > 0 && k % 256 == 0 && k <= 16384) {
     SkinnyPlan p = plan_skinny_base(m, n, k, forced_splits);
     if (p.splits == 0) {
-      p.rdot_chunks = (int)(k / 2048);
+      p.rdot_chunks = (int)((k + 2047) / 2048);
       return p;
     }
   }

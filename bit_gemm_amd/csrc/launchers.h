@@ -82,7 +82,7 @@ struct SkinnyPlan {
   int pk_rounds;  // > 0 (with splits == 0): persistent full-K kernel, `waves` waves x pk_rounds K slices of 512
   int fx_steps;   // > 0: single-launch full-K kernel, `waves` waves x fx_steps K steps of 128 (16 < m <= 64)
   int fx_tiles;   // with fx_steps: 16-row weight tiles per workgroup (1 .. 4)
-  int rdot_chunks;  // > 0 (with splits == 0, m == 1): row-per-wave dot-product kernel, k = 2048 rdot_chunks
+  int rdot_chunks;  // > 0 (with splits == 0, m == 1): row-per-wave dot-product kernel over rdot_chunks chunks of 2048 k (the last may be partial)
 };
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits);
 hipError_t launch_skinny(const void* x, const uint8_t* codes, const uint8_t* scales,

@@ -149,8 +149,7 @@ FULL_K_CASES = [
     # two to four row tiles per workgroup (more than 256 tiles), ragged n
     (17, 8192, 4096), (48, 12000, 4096), (33, 14336, 2048), (25, 7777, 2048),
     # one or two tokens on more than 1024 row tiles: four waves of two rounds
-    # (one token with k = 2048 c: the row-per-wave kernel with the hardware
-    # decode; 3584 is not such a k)
+    # (one token: the row-per-wave kernel with the hardware decode)
     (1, 16400, 4096), (2, 16416, 4096), (1, 20000, 3584),
     # one token, row-per-wave kernel (k = 2048 c): ragged n with one
     # 2048-wide chunk, 3 and 8 chunks, n not a multiple of the 8 rows of a
@@ -160,6 +159,11 @@ FULL_K_CASES = [
     # every chunk count 4 .. 7, n not a multiple of the 4 rows of a
     # workgroup, a single row
     (1, 4097, 8192), (1, 1003, 10240), (1, 1, 12288), (1, 4101, 14336),
+    # k % 2048 != 0 (k % 256 == 0): a partial last chunk (lanes past k / 32
+    # of it hold no codes); one row per wave, and two rows per wave with one
+    # or two chunks on more than 8192 rows; k from 256 to 14592
+    (1, 3584, 3584), (1, 4101, 11008), (1, 1003, 2816), (1, 13, 1280), (1, 64, 256), (1, 600, 14592),
+    (1, 8200, 3840), (1, 9000, 768),
 ]
 
 
