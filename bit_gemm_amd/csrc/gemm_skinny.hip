@@ -611,6 +611,14 @@ hipError_t launch_rdot(const SkinnyPlan& p, hipStream_t stream, const uint16_t* 
     case 6: return launch_rdot_n<6>(stream, x, codes, scales, ts, y, N, K, out_f32);
     case 7: return launch_rdot_n<7>(stream, x, codes, scales, ts, y, N, K, out_f32);
     case 8: return launch_rdot_n<8>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 9: return launch_rdot_n<9>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 10: return launch_rdot_n<10>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 11: return launch_rdot_n<11>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 12: return launch_rdot_n<12>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 13: return launch_rdot_n<13>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 14: return launch_rdot_n<14>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 15: return launch_rdot_n<15>(stream, x, codes, scales, ts, y, N, K, out_f32);
+    case 16: return launch_rdot_n<16>(stream, x, codes, scales, ts, y, N, K, out_f32);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1872,10 +1880,10 @@ SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits);
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   int w = 0, r = 0, t = 0;
-  // one token, 0 < k <= 16384 with k % 256 == 0: the row-per-wave
+  // one token, 0 < k <= 32768 with k % 256 == 0: the row-per-wave
   // dot-product kernel over ceil(k / 2048) chunks of 2048 (the portable
   // decode takes the full-K kernel with the same plan's waves)
-  if (forced_splits <= 0 && m == 1 && k > 0 && k % 256 == 0 && k <= 16384) {
+  if (forced_splits <= 0 && m == 1 && k > 0 && k % 256 == 0 && k <= 32768) {
     SkinnyPlan p = plan_skinny_base(m, n, k, forced_splits);
     if (p.splits == 0) {
       p.rdot_chunks = (int)((k + 2047) / 2048);

@@ -164,6 +164,8 @@ FULL_K_CASES = [
     # or two chunks on more than 8192 rows; k from 256 to 14592
     (1, 3584, 3584), (1, 4101, 11008), (1, 1003, 2816), (1, 13, 1280), (1, 64, 256), (1, 600, 14592),
     (1, 8200, 3840), (1, 9000, 768),
+    # rows of 9 to 16 chunks (k up to 32768), whole and partial
+    (1, 77, 18944), (1, 129, 22016), (1, 1030, 28672), (1, 300, 32768),
 ]
 
 
