@@ -479,7 +479,7 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* _
 
 // The same dot products with the activations copied into LDS by the LDS
 // DMA, issued before the weight loads, and k = 2048 (NCH - 1) + kl for any
-// 0 < kl <= 2048 with kl % 256 == 0: in a partial last chunk only lanes
+// 0 < kl <= 2048 with kl % 256 == 0 and NCH <= 16 (64 KiB of activations): in a partial last chunk only lanes
 // < kl / 32 hold codes; the others load piece 0 of that chunk (a valid
 // address) and their sums are discarded by a select (the activations they
 // read from LDS past k are never written).  The weight loads are inline asm
@@ -499,7 +499,9 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* _
 // full-K dot kernel that took them before: 5120 x 13824 9.2 against 16.0 us,
 // 13824 x 5120 9.3 against 14.5, 4096 x 11008 7.1 against 9.1, 18944 x 3584
 // 8.9 (two rows per wave; one row 9.5) against 11.1, 1003 x 2816 2.6
-// against 3.4, 3584 x 3584 3.84 against 3.90 us.
+// against 3.4, 3584 x 3584 3.84 against 3.90 us; rows of 9-16 chunks:
+// 8192 x 28672 28.1 against 30.7 us, 4096 x 22016 12.2 against 16.3,
+// 1024 x 32768 6.8 against 15.2 us.
 template <int NCH, int RW, int C>
 __device__ __forceinline__ void rdot_dma_chunk(u32x4_t (&cw)[RW][NCH], uint32_t (&sw)[RW][NCH], const uint16_t* xs,
                                                int lane, bool on_last, float (&acc)[RW]) {
