@@ -479,7 +479,7 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* _
 
 // The same dot products with the activations copied into LDS by the LDS
 // DMA, issued before the weight loads, and k = 2048 (NCH - 1) + kl for any
-// 0 < kl <= 2048 with kl % 256 == 0 and NCH <= 16 (64 KiB of activations): in a partial last chunk only lanes
+// 0 < kl <= 2048 with kl % 32 == 0 and NCH <= 16 (64 KiB of activations): in a partial last chunk only lanes
 // < kl / 32 hold codes; the others load piece 0 of that chunk (a valid
 // address) and their sums are discarded by a select (the activations they
 // read from LDS past k are never written).  The weight loads are inline asm
@@ -535,7 +535,7 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot_dma(const uint16_
                                                                  void* __restrict__ y, int N, int K, int out_f32) {
   __shared__ __attribute__((aligned(16))) uint16_t xs[2048 * NCH];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int xp = K / 8;  // 16-byte pieces of x (a multiple of 32)
+  const int xp = K / 8;  // 16-byte pieces of x (a multiple of 4)
 #pragma unroll
   for (int t = 0; t < NCH; ++t) {  // piece i = threadIdx.x + 256 t lands at byte 16 i of xs
     const int i = (int)threadIdx.x + 64 * kRdWaves * t;
@@ -1882,10 +1882,10 @@ SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits);
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   int w = 0, r = 0, t = 0;
-  // one token, 0 < k <= 32768 with k % 256 == 0: the row-per-wave
+  // one token, 0 < k <= 32768 with k % 32 == 0: the row-per-wave
   // dot-product kernel over ceil(k / 2048) chunks of 2048 (the portable
   // decode takes the full-K kernel with the same plan's waves)
-  if (forced_splits <= 0 && m == 1 && k > 0 && k % 256 == 0 && k <= 32768) {
+  if (forced_splits <= 0 && m == 1 && k > 0 && k % 32 == 0 && k <= 32768) {
     SkinnyPlan p = plan_skinny_base(m, n, k, forced_splits);
     if (p.splits == 0) {
       p.rdot_chunks = (int)((k + 2047) / 2048);

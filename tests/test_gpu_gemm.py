@@ -166,6 +166,8 @@ FULL_K_CASES = [
     (1, 8200, 3840), (1, 9000, 768),
     # rows of 9 to 16 chunks (k up to 32768), whole and partial
     (1, 77, 18944), (1, 129, 22016), (1, 1030, 28672), (1, 300, 32768),
+    # k % 256 != 0 (k % 32 == 0): 14, 1, 33 and 1 lanes with codes in the last chunk
+    (1, 333, 4544), (1, 100, 2080), (1, 8500, 1056), (1, 70, 32),
 ]
 
 
