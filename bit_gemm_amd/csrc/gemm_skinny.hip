@@ -403,12 +403,13 @@ __global__ __launch_bounds__(512) void k_skinny_dot(const uint16_t* __restrict__
 // unit-scale decode, scales each by its sigma, and the 64 lane sums of a
 // row are added with xor shuffles in a fixed order.  Against the full-K dot
 // kernel (rows across lanes, K slices across waves, a cross-wave sum in
-// LDS), measured at m = 1 (per call, 32 back-to-back calls on rotating
-// copies): 4096 x 4096 4.25 against 4.52 us, 14336 x 4096 7.9 against 8.6,
-// 12288 x 4096 7.2 against 8.8, 28672 x 4096 13.1-14.1 against 16.2, 4096 x
-// 14336 9.3 against 10.9 us.  Eight rows per workgroup measured best over
-// 4 / 8 / 16 waves of 1, 2 or 4 rows (16 rows: 4096 x 14336 10.2 us, 4096 x
-// 4096 4.5 us).
+// LDS), measured at m = 1 with the first version of this kernel, which then
+// served every k = 2048 c up to 16384 (per call, 32 back-to-back calls on
+// rotating copies): 4096 x 4096 4.25 against 4.52 us, 14336 x 4096 7.9
+// against 8.6, 12288 x 4096 7.2 against 8.8, 28672 x 4096 13.1-14.1
+// against 16.2, 4096 x 14336 9.3 against 10.9 us.  Eight rows per
+// workgroup measured best over 4 / 8 / 16 waves of 1, 2 or 4 rows (16 rows:
+// 4096 x 14336 10.2 us, 4096 x 4096 4.5 us).
 constexpr int kRdWaves = 4, kRdRows = 2;  // waves per workgroup, rows per wave
 template <int NCH>
 __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* __restrict__ x,
