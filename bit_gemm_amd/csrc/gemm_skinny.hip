@@ -1941,6 +1941,17 @@ SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits) 
     // at m = 1 / 2: 519 / 568 against 549 / 592 us; on 768 tiles (q, k, v
     // stacked) it was even or slower (296 / 334 against 294 / 319 us)
     if (m <= 2 && (n + 15) / 16 > 1024 && k <= 4096 && waves > 4) waves = 4;
+    // at most one workgroup per CU (n <= 4096): as few waves as keep the
+    // number of rounds, so none idles in the last one (4096 x 14336 at m =
+    // 2 / 3: 7 waves 12.06 / 13.26 against 8 waves 12.45 / 13.82 us; 4096 x
+    // 6144 at m = 2 / 4: 6 waves 7.60 / 7.99 against 7.95 / 8.44 us); with
+    // more workgroups than CUs it measured even or slower (13824 x 5120 at
+    // m = 2: 17.61 against 17.45 us)
+    if ((n + 15) / 16 <= 256) {
+      const int64_t slices = (k + kWaveK - 1) / kWaveK;
+      const int64_t rounds = (slices + waves - 1) / waves;
+      waves = (slices + rounds - 1) / rounds;
+    }
     p.splits = 0;
     p.waves = (int)waves;
     p.steps_per_wave = kSpw;
