@@ -168,6 +168,8 @@ FULL_K_CASES = [
     (1, 77, 18944), (1, 129, 22016), (1, 1030, 28672), (1, 300, 32768),
     # k % 256 != 0 (k % 32 == 0): 14, 1, 33 and 1 lanes with codes in the last chunk
     (1, 333, 4544), (1, 100, 2080), (1, 8500, 1056), (1, 70, 32),
+    # one token past the row-per-wave kernel's range (k > 32768, k % 32 != 0): the full-K kernel
+    (1, 64, 32800), (1, 64, 48),
     # full-K kernel with its waves trimmed to the rounds (at most 256 row
     # tiles): 7 waves x 4 rounds, 6 x 2, 5 x 2, 7 x 3
     (2, 1000, 13824), (3, 4096, 6144), (4, 300, 5120), (2, 4000, 9728),
