@@ -490,7 +490,7 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot(const uint16_t* _
 // copies would be vmcnt(0), i.e. for every weight load too).  RW rows per
 // wave: one for long rows (16 rows per workgroup halve the x copies per
 // weight byte but leave too few waves to overlap the chunks' sums with the
-// loads), two for one or two chunks on tall matrices.  Measured at m = 1
+// loads), two for a partial second chunk on tall matrices.  Measured at m = 1
 // (per call, 32 calls on rotating copies), whole chunks against the two-row
 // kernel above: 4096 x 8192 5.66 against 5.89 us, 4096 x 12288 7.45 against
 // 7.87, 4096 x 14336 8.45 against 8.70, 4096 x 16384 9.08 against 9.98,
@@ -583,24 +583,30 @@ __global__ __launch_bounds__(64 * kRdWaves) void k_skinny_rdot_dma(const uint16_
 template <int NCH>
 hipError_t launch_rdot_n(hipStream_t stream, const uint16_t* x, const uint8_t* codes, const uint8_t* scales,
                          KScale ts, void* y, int N, int K, int out_f32) {
-  if constexpr (NCH <= 2) {
-    if (K == 2048 * NCH) {  // whole chunks: the two-row kernel staging x through registers
-      const dim3 grid((unsigned)((N + kRdWaves * kRdRows - 1) / (kRdWaves * kRdRows)));
-      hipLaunchKernelGGL((k_skinny_rdot<NCH>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N,
-                         out_f32);
-      return hipGetLastError();
+  if constexpr (NCH == 1) {  // k = 2048 (the planner takes k >= 2048)
+    const dim3 grid((unsigned)((N + kRdWaves * kRdRows - 1) / (kRdWaves * kRdRows)));
+    hipLaunchKernelGGL((k_skinny_rdot<1>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N, out_f32);
+    return hipGetLastError();
+  } else {
+    if constexpr (NCH == 2) {
+      if (K == 2048 * NCH) {  // whole chunks: the two-row kernel staging x through registers
+        const dim3 grid((unsigned)((N + kRdWaves * kRdRows - 1) / (kRdWaves * kRdRows)));
+        hipLaunchKernelGGL((k_skinny_rdot<NCH>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N,
+                           out_f32);
+        return hipGetLastError();
+      }
+      if (N > 8192) {  // a partial second chunk on a tall matrix: two rows per wave
+        const dim3 grid((unsigned)((N + 2 * kRdWaves - 1) / (2 * kRdWaves)));
+        hipLaunchKernelGGL((k_skinny_rdot_dma<NCH, 2>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts,
+                           y, N, K, out_f32);
+        return hipGetLastError();
+      }
     }
-    if (N > 8192) {  // a partial chunk on a tall matrix: two rows per wave
-      const dim3 grid((unsigned)((N + 2 * kRdWaves - 1) / (2 * kRdWaves)));
-      hipLaunchKernelGGL((k_skinny_rdot_dma<NCH, 2>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y,
-                         N, K, out_f32);
-      return hipGetLastError();
-    }
+    const dim3 grid((unsigned)((N + kRdWaves - 1) / kRdWaves));
+    hipLaunchKernelGGL((k_skinny_rdot_dma<NCH, 1>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N,
+                       K, out_f32);
+    return hipGetLastError();
   }
-  const dim3 grid((unsigned)((N + kRdWaves - 1) / kRdWaves));
-  hipLaunchKernelGGL((k_skinny_rdot_dma<NCH, 1>), grid, dim3(64 * kRdWaves), 0, stream, x, codes, scales, ts, y, N, K,
-                     out_f32);
-  return hipGetLastError();
 }
 
 hipError_t launch_rdot(const SkinnyPlan& p, hipStream_t stream, const uint16_t* x, const uint8_t* codes,
@@ -1883,10 +1889,13 @@ SkinnyPlan plan_skinny_base(int64_t m, int64_t n, int64_t k, int forced_splits);
 
 SkinnyPlan plan_skinny(int64_t m, int64_t n, int64_t k, int forced_splits) {
   int w = 0, r = 0, t = 0;
-  // one token, 0 < k <= 32768 with k % 32 == 0: the row-per-wave
+  // one token, 2048 <= k <= 32768 with k % 32 == 0: the row-per-wave
   // dot-product kernel over ceil(k / 2048) chunks of 2048 (the portable
-  // decode takes the full-K kernel with the same plan's waves)
-  if (forced_splits <= 0 && m == 1 && k > 0 && k % 32 == 0 && k <= 32768) {
+  // decode takes the full-K kernel with the same plan's waves).  Below one
+  // whole chunk most lanes would hold no codes, and the full-K kernel is
+  // faster (8192 x 512 2.99 against 3.64 us, 32768 x 768 5.31 against 7.64,
+  // 16384 x 1024 4.62 against 4.95 us)
+  if (forced_splits <= 0 && m == 1 && k >= 2048 && k % 32 == 0 && k <= 32768) {
     SkinnyPlan p = plan_skinny_base(m, n, k, forced_splits);
     if (p.splits == 0) {
       p.rdot_chunks = (int)((k + 2047) / 2048);

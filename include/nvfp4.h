@@ -236,11 +236,11 @@ NVFP4_API int nvfp4_dequant(const uint8_t* codes, const uint8_t* scales, const f
  * Dispatch (the lower-latency kernel for the shape, [Recap] section 1, as
  * measured on MI355X; nvfp4_w4a16_gemm_path tells which):
  *   m <= 16 -> memory-bound skinny kernel, one launch, no workspace: for
- *     m == 1 with k a multiple of 32 up to 32768 a kernel in which each
- *     wave streams whole weight rows (lanes along K, the activations staged
- *     once per workgroup: 8 rows for k = 2048 or 4096, else 4 rows, or 8
- *     for k < 4096 on more than 8192 rows, with the activations copied by
- *     LDS DMA); for
+ *     m == 1 with k a multiple of 32 from 2048 to 32768 a kernel in which
+ *     each wave streams whole weight rows (lanes along K, the activations
+ *     staged once per workgroup: 8 rows for k = 2048 or 4096, else 4 rows,
+ *     or 8 for k < 4096 on more than 8192 rows, with the activations copied
+ *     by LDS DMA); for
  *     4 < m <= 16 with k % 512 == 0 and k <= 4096 a persistent kernel (a
  *     workgroup per CU walks 16-row tiles with the activations in LDS
  *     once); otherwise a workgroup per 16 weight rows over the whole K

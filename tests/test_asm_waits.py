@@ -64,7 +64,7 @@ def device_asm(tmp_path_factory):
     ("gemm_skinny.hip", r"k_skinny_str", 16),    # streaming kernel: MT 1..4 x chunk lengths x 2 conversion implementations
     ("gemm_skinny.hip", r"k_skinny_pk", 4),      # persistent full-K kernel: 8 or 16 token rows x 2 implementations
     ("gemm_skinny.hip", r"k_skinny_fx", 48),     # single-launch full-K kernel: MT 2..4 x 4 or 8 steps x 1..4 tiles x 2 implementations
-    ("gemm_skinny.hip", r"k_skinny_rdot_dma", 18),  # one-token row-per-wave kernel with LDS DMA activations: 1..16 chunks of 2048, two rows per wave at 1..2
+    ("gemm_skinny.hip", r"k_skinny_rdot_dma", 16),  # one-token row-per-wave kernel with LDS DMA activations: 2..16 chunks of 2048, two rows per wave at 2
     ("gemm_tiled.hip", r"k_lmr", 4),             # weights-in-registers large-M kernels (64 or 128 k per barrier), 2 implementations each
 ])
 def test_counted_waits_cover_every_use(device_asm, source, pattern, minimum, grouped):

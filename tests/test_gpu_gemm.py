@@ -160,14 +160,16 @@ FULL_K_CASES = [
     # workgroup, a single row
     (1, 4097, 8192), (1, 1003, 10240), (1, 1, 12288), (1, 4101, 14336),
     # k % 2048 != 0 (k % 256 == 0): a partial last chunk (lanes past k / 32
-    # of it hold no codes); one row per wave, and two rows per wave with one
-    # or two chunks on more than 8192 rows; k from 256 to 14592
+    # of it hold no codes); one row per wave, and two rows per wave with two
+    # chunks on more than 8192 rows; k from 2816 to 14592 (below 2048 the
+    # full-K kernel: 1280, 256, 768)
     (1, 3584, 3584), (1, 4101, 11008), (1, 1003, 2816), (1, 13, 1280), (1, 64, 256), (1, 600, 14592),
     (1, 8200, 3840), (1, 9000, 768),
     # rows of 9 to 16 chunks (k up to 32768), whole and partial
     (1, 77, 18944), (1, 129, 22016), (1, 1030, 28672), (1, 300, 32768),
-    # k % 256 != 0 (k % 32 == 0): 14, 1, 33 and 1 lanes with codes in the last chunk
-    (1, 333, 4544), (1, 100, 2080), (1, 8500, 1056), (1, 70, 32),
+    # k % 256 != 0 (k % 32 == 0): 14 and 1 lanes with codes in the last chunk
+    # (k = 1056 and 32: the full-K kernel)
+    (1, 333, 4544), (1, 100, 2080), (1, 8500, 1056), (1, 70, 32), (1, 9000, 2080),
     # one token past the row-per-wave kernel's range (k > 32768, k % 32 != 0): the full-K kernel
     (1, 64, 32800), (1, 64, 48),
     # full-K kernel with its waves trimmed to the rounds (at most 256 row

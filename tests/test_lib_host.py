@@ -212,7 +212,7 @@ def test_dispatch_and_workspace_plan(L):
         assert P(m, 4096, 14336) == S
         assert L.nvfp4_w4a16_gemm_workspace_size(m, 4096, 14336) == 14 * 4 * m * 4096
     assert L.nvfp4_w4a16_gemm_workspace_size(4, 4096, 14336) == 0
-    # one token: the row-per-wave kernel for every k % 32 == 0 up to 32768
+    # one token: the row-per-wave kernel for every k % 32 == 0 from 2048 to 32768
     # (whole or partial chunks of 2048) and the full-K kernel for other k;
     # all skinny, one launch, no workspace
     for n, k in ((4096, 4096), (3584, 3584), (4101, 11008), (70, 32), (333, 4544), (8192, 28672),
